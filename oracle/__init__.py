@@ -1,0 +1,187 @@
+"""Python face of the fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module.  The product path
+(the HIP library and its binding) never loads it, and it never loads them.
+
+Every function takes and returns raw storage bits as numpy arrays:
+``uint16`` for binary16 / bfloat16 tensors, ``float32`` for binary32 tables,
+``uint8`` for E4M3FN codes.  Row-major 2-D arrays; ``n`` columns of each row
+are used (a row may be wider than ``n``, which models a row stride).
+
+The definitions followed are those of the page "TileLang tutorial, ch. 13:
+elementwise, normalisation and RoPE operators": RMSNorm and LayerNorm from
+its reference implementations (s3.2.1), the two RoPE pairings (s3.3.1,
+s3.3.2), the per-token FP8 cast (s3.1.5) and the fused norm/rotate/quantise
+operator (s3.3.4).  The C source states each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f16": 1, "bf16": 2, "f32": 3}
+_STORAGE = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_SO):
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+               "-o", _SO + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        build(force=True)
+    L = ctypes.CDLL(_SO)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+    L.oracle_decode_f16.restype = ctypes.c_double
+    L.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    L.oracle_decode_bf16.restype = ctypes.c_double
+    L.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    L.oracle_decode_e4m3.restype = ctypes.c_double
+    L.oracle_encode_f16.argtypes = [ctypes.c_double]
+    L.oracle_encode_f16.restype = ctypes.c_uint16
+    L.oracle_encode_bf16.argtypes = [ctypes.c_double]
+    L.oracle_encode_bf16.restype = ctypes.c_uint16
+    L.oracle_encode_e4m3.argtypes = [ctypes.c_double]
+    L.oracle_encode_e4m3.restype = ctypes.c_uint8
+    L.oracle_rmsnorm.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, f32]
+    L.oracle_rmsnorm.restype = None
+    L.oracle_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32]
+    L.oracle_layernorm.restype = None
+    L.oracle_rope.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32]
+    L.oracle_rope.restype = None
+    L.oracle_rmsnorm_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                          i64, i64, i32, i32, i32, f32, vp]
+    L.oracle_rmsnorm_rope_fp8.restype = None
+    _lib = L
+    return L
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(a, dtype, name):
+    if a is None:
+        return None
+    want = _STORAGE[dtype]
+    if a.dtype != want:
+        raise TypeError(f"{name}: expected {np.dtype(want)} storage for {dtype}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError(f"{name} must be C-contiguous")
+    return a
+
+
+# ---------------------------------------------------------------- scalars
+def decode_f16(bits: int) -> float:
+    return _load().oracle_decode_f16(int(bits))
+
+
+def decode_bf16(bits: int) -> float:
+    return _load().oracle_decode_bf16(int(bits))
+
+
+def decode_e4m3(code: int) -> float:
+    return _load().oracle_decode_e4m3(int(code))
+
+
+def encode_f16(v: float) -> int:
+    return _load().oracle_encode_f16(float(v))
+
+
+def encode_bf16(v: float) -> int:
+    return _load().oracle_encode_bf16(float(v))
+
+
+def encode_e4m3(v: float) -> int:
+    return _load().oracle_encode_e4m3(float(v))
+
+
+# ---------------------------------------------------------------- operators
+def rmsnorm(x, w, dtype: str, eps: float, n: int | None = None, y_stride: int | None = None,
+            fill: int = 0):
+    """y[r, :n] = RMSNorm(x[r, :n]) * w, rounded once to ``dtype``."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    w = _check(w, dtype, "w")
+    rows, xs = x.shape
+    n = xs if n is None else n
+    ys = n if y_stride is None else y_stride
+    y = np.full((rows, ys), fill, dtype=_STORAGE[dtype])
+    L.oracle_rmsnorm(_ptr(x), _ptr(w), _ptr(y), rows, n, xs, ys, DTYPE_CODE[dtype], eps)
+    return y
+
+
+def layernorm(x, gamma, beta, dtype: str, eps: float, n: int | None = None,
+              y_stride: int | None = None, fill: int = 0):
+    """y[r, :n] = LayerNorm(x[r, :n]; gamma, beta), biased variance, one rounding."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    gamma = _check(gamma, dtype, "gamma")
+    beta = _check(beta, dtype, "beta")
+    rows, xs = x.shape
+    n = xs if n is None else n
+    ys = n if y_stride is None else y_stride
+    y = np.full((rows, ys), fill, dtype=_STORAGE[dtype])
+    L.oracle_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, n, xs, ys,
+                       DTYPE_CODE[dtype], eps)
+    return y
+
+
+def rope(x, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str, cs_dtype: str,
+         neox: bool, y_stride: int | None = None, fill: int = 0):
+    """RoPE on each head's tail span.  x: [tokens, >= heads*head_dim];
+    cos/sin: [tokens, rope_dim/2]."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    cos = _check(cos, cs_dtype, "cos")
+    sin = _check(sin, cs_dtype, "sin")
+    tokens, xs = x.shape
+    n = heads * head_dim
+    assert cos.shape == (tokens, rope_dim // 2) and sin.shape == cos.shape
+    ys = n if y_stride is None else y_stride
+    y = np.full((tokens, ys), fill, dtype=_STORAGE[dtype])
+    L.oracle_rope(_ptr(x), _ptr(cos), _ptr(sin), _ptr(y), tokens, heads, head_dim, rope_dim,
+                  xs, ys, DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)))
+    return y
+
+
+def rmsnorm_rope_fp8(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str,
+                     cs_dtype: str, neox: bool, eps: float, q_stride: int | None = None,
+                     want_z: bool = False, fill: int = 0):
+    """Fused RMSNorm -> RoPE -> per-token E4M3FN.  Returns (codes, scales[, z])."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    w = _check(w, dtype, "w")
+    cos = _check(cos, cs_dtype, "cos")
+    sin = _check(sin, cs_dtype, "sin")
+    tokens, xs = x.shape
+    n = heads * head_dim
+    assert cos.shape == (tokens, rope_dim // 2) and sin.shape == cos.shape
+    qs = n if q_stride is None else q_stride
+    q = np.full((tokens, qs), fill, dtype=np.uint8)
+    scales = np.zeros(tokens, dtype=np.float32)
+    z = np.zeros((tokens, n), dtype=np.float64) if want_z else None
+    L.oracle_rmsnorm_rope_fp8(_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(q), _ptr(scales),
+                              tokens, heads, head_dim, rope_dim, xs, qs, DTYPE_CODE[dtype],
+                              DTYPE_CODE[cs_dtype], int(bool(neox)), eps, _ptr(z))
+    return (q, scales, z) if want_z else (q, scales)

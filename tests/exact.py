@@ -1,0 +1,206 @@
+"""Exact-arithmetic checkers used to pin the CPU oracle.
+
+Nothing here calls the oracle or the HIP library.  Values are carried as
+``decimal.Decimal`` at 400 significant digits (every binary16/bfloat16/binary32
+input and every product of two of them is exact at that precision), and each
+result is rounded to a storage format by searching the format's sorted value
+table for the nearest representable value, ties to the even code.  The value
+tables come from independent decoders: numpy's float16, the bfloat16 layout
+(top half of a binary32) read through numpy's float32, and torch's
+``float8_e4m3fn``.
+"""
+from __future__ import annotations
+
+import bisect
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+getcontext().prec = 400
+
+
+class CodeTable:
+    """Non-negative finite values of a sign-magnitude format, indexed by code."""
+
+    def __init__(self, mags: np.ndarray, sign_bit: int, overflow_code: int):
+        # mags[c] = value of code c for c = 0 .. max finite magnitude code
+        assert np.all(np.diff(mags) > 0), "values must increase with the code"
+        self.vals = [Decimal(float(v)) for v in mags]
+        self.sign_bit = sign_bit
+        self.overflow_code = overflow_code
+
+    def nearest(self, v: Decimal) -> int:
+        neg = v.is_signed()
+        m = abs(v)
+        vals = self.vals
+        top = vals[-1]
+        if m > top:
+            # beyond the largest finite value: RNE keeps it only below the
+            # midpoint to the next (non-representable) step
+            step = top - vals[-2]
+            mid = top + step / 2
+            top_even = (len(vals) - 1) % 2 == 0
+            if m < mid or (m == mid and top_even):
+                c = len(vals) - 1
+            else:
+                c = self.overflow_code
+        else:
+            i = bisect.bisect_right(vals, m) - 1  # vals[i] <= m
+            if i == len(vals) - 1 or vals[i] == m:
+                c = i
+            else:
+                lo, hi = vals[i], vals[i + 1]
+                dl, dh = m - lo, hi - m
+                if dl < dh:
+                    c = i
+                elif dh < dl:
+                    c = i + 1
+                else:
+                    c = i if i % 2 == 0 else i + 1
+        return (self.sign_bit | c) if neg else c
+
+
+def _f16_table():
+    codes = np.arange(0, 0x7C00, dtype=np.uint16)
+    return CodeTable(codes.view(np.float16).astype(np.float64), 0x8000, 0x7C00)
+
+
+def _bf16_table():
+    codes = np.arange(0, 0x7F80, dtype=np.uint32)
+    return CodeTable((codes << 16).view(np.float32).astype(np.float64), 0x8000, 0x7F80)
+
+
+def _e4m3_table():
+    import torch
+
+    codes = torch.arange(0, 0x7F, dtype=torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return CodeTable(vals, 0x80, 0x7F)
+
+
+_TABLES = {}
+
+
+def table(fmt: str) -> CodeTable:
+    if fmt not in _TABLES:
+        _TABLES[fmt] = {"f16": _f16_table, "bf16": _bf16_table, "e4m3": _e4m3_table}[fmt]()
+    return _TABLES[fmt]
+
+
+def dec(bits: int, fmt: str) -> Decimal:
+    """Exact value of one stored element."""
+    if fmt == "f16":
+        return Decimal(float(np.array([bits], dtype=np.uint16).view(np.float16)[0]))
+    if fmt == "bf16":
+        return Decimal(float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0]))
+    if fmt == "f32":
+        return Decimal(float(np.float32(bits)))
+    if fmt == "e4m3":
+        import torch
+
+        return Decimal(float(torch.tensor([bits], dtype=torch.uint8)
+                             .view(torch.float8_e4m3fn).to(torch.float64)[0]))
+    raise ValueError(fmt)
+
+
+def round_to(v: Decimal, fmt: str) -> int:
+    return table(fmt).nearest(v)
+
+
+def round_f32(v: Decimal) -> float:
+    """Nearest binary32 to ``v`` (ties to even), by checking the neighbours."""
+    f = np.float32(float(v))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = None
+    for c in cands:
+        d = abs(Decimal(float(c)) - v)
+        even = (int(np.array([c], dtype=np.float32).view(np.uint32)[0]) & 1) == 0
+        key = (d, 0 if even else 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return float(best[1])
+
+
+def sqrt(v: Decimal) -> Decimal:
+    return v.sqrt()
+
+
+# ----------------------------------------------------------------- references
+def rmsnorm_ref(xrow, wrow, fmt, eps32):
+    """Exact RMSNorm of one row; returns output codes."""
+    xs = [dec(b, fmt) for b in xrow]
+    ws = [dec(b, fmt) for b in wrow] if wrow is not None else [Decimal(1)] * len(xs)
+    n = len(xs)
+    ms = sum(x * x for x in xs) / n
+    r = 1 / sqrt(ms + Decimal(float(np.float32(eps32))))
+    return [round_to(x * r * w, fmt) for x, w in zip(xs, ws)]
+
+
+def layernorm_ref(xrow, grow, brow, fmt, eps32):
+    xs = [dec(b, fmt) for b in xrow]
+    n = len(xs)
+    gs = [dec(b, fmt) for b in grow] if grow is not None else [Decimal(1)] * n
+    bs = [dec(b, fmt) for b in brow] if brow is not None else [Decimal(0)] * n
+    mu = sum(xs) / n
+    var = sum((x - mu) * (x - mu) for x in xs) / n
+    r = 1 / sqrt(var + Decimal(float(np.float32(eps32))))
+    return [round_to((x - mu) * r * g + b, fmt) for x, g, b in zip(xs, gs, bs)]
+
+
+def rope_pairs(rope_dim, neox):
+    half = rope_dim // 2
+    if neox:
+        return [(p, p, p + half) for p in range(half)]
+    return [(p, 2 * p, 2 * p + 1) for p in range(half)]
+
+
+def rope_values(vals, cos_row, sin_row, heads, head_dim, rope_dim, neox):
+    """Rotate exact values (list of Decimal, one token) on each head's tail span."""
+    out = list(vals)
+    start = head_dim - rope_dim
+    for h in range(heads):
+        base = h * head_dim + start
+        for p, a, b in rope_pairs(rope_dim, neox):
+            c, s = cos_row[p], sin_row[p]
+            xa, xb = vals[base + a], vals[base + b]
+            out[base + a] = xa * c - xb * s
+            out[base + b] = xa * s + xb * c
+    return out
+
+
+def rope_ref(xrow, crow, srow, heads, head_dim, rope_dim, fmt, cs_fmt, neox):
+    xs = [dec(b, fmt) for b in xrow]
+    cs = [dec(b, cs_fmt) for b in crow]
+    ss = [dec(b, cs_fmt) for b in srow]
+    z = rope_values(xs, cs, ss, heads, head_dim, rope_dim, neox)
+    start = head_dim - rope_dim
+    out = []
+    for j, v in enumerate(z):
+        if (j % head_dim) < start:
+            out.append(int(xrow[j]))  # pass-through channel: the same bits
+        else:
+            out.append(round_to(v, fmt))
+    return out
+
+
+def fused_ref(xrow, wrow, crow, srow, heads, head_dim, rope_dim, fmt, cs_fmt, neox, eps32):
+    """Exact fused op of one token; returns (codes, scale, z values)."""
+    xs = [dec(b, fmt) for b in xrow]
+    n = len(xs)
+    ws = [dec(b, fmt) for b in wrow] if wrow is not None else [Decimal(1)] * n
+    ms = sum(x * x for x in xs) / n
+    r = 1 / sqrt(ms + Decimal(float(np.float32(eps32))))
+    normed = [x * r * w for x, w in zip(xs, ws)]
+    cs = [dec(b, cs_fmt) for b in crow]
+    ss = [dec(b, cs_fmt) for b in srow]
+    z = rope_values(normed, cs, ss, heads, head_dim, rope_dim, neox)
+    amax = max(abs(v) for v in z)
+    floor = Decimal(float(np.float32(1e-4)))
+    scale = round_f32(max(amax, floor) / 448)
+    S = Decimal(scale)
+    codes = []
+    for v in z:
+        q = v / S
+        q = min(max(q, Decimal(-448)), Decimal(448))
+        codes.append(round_to(q, "e4m3"))
+    return codes, scale, z

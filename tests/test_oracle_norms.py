@@ -1,0 +1,147 @@
+"""Pins of the oracle's RMSNorm and LayerNorm ("TileLang tutorial, ch. 13",
+s3.2.1 reference definitions; s5.4 on ragged rows) against exact brute force,
+closed forms, invariants and torch's float64 implementations."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quant_row_workgroup_amd import synth
+from tests import exact
+
+FMTS = ["f16", "bf16"]
+
+
+def _rand(seed, shape, mean, std, fmt):
+    return synth.normal(seed, shape, mean, std, fmt)
+
+
+def _f64(bits, fmt):
+    return synth.storage_to_f64(bits, fmt)
+
+
+def _ulp(v, fmt):
+    """Spacing of the format at |v| (for tolerance checks against float64 references)."""
+    mbits, emin = (10, -14) if fmt == "f16" else (7, -126)
+    a = np.maximum(np.abs(v), 2.0 ** emin)
+    e = np.floor(np.log2(a))
+    return 2.0 ** (e - mbits)
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("with_w", [True, False])
+def test_rmsnorm_brute_force_4x8(fmt, with_w):
+    for seed in range(6):
+        x = _rand(100 + seed, (4, 8), 0.0, 1.5, fmt)
+        w = _rand(200 + seed, (8,), 1.0, 0.3, fmt) if with_w else None
+        eps = [1e-6, 1e-5, 0.25][seed % 3]
+        y = oracle.rmsnorm(x, w, fmt, eps)
+        for r in range(4):
+            want = exact.rmsnorm_ref(x[r], w, fmt, eps)
+            assert [int(v) for v in y[r]] == want, (seed, r)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rmsnorm_constant_row_returns_weight(fmt):
+    # c / sqrt(c^2 + eps) = 1 - O(eps / c^2), far inside half an ulp, so y == w bit-exactly
+    w = _rand(7, (96,), 1.0, 0.1, fmt)
+    for c in [1.0, 3.0, 0.75, -2.0]:
+        x = synth.to_storage(np.full((3, 96), c), fmt)
+        y = oracle.rmsnorm(x, w, fmt, 1e-6)
+        want = w if c > 0 else (w ^ np.uint16(0x8000))
+        assert np.array_equal(y, np.broadcast_to(want, y.shape)), c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rmsnorm_power_of_two_scale_invariance(fmt):
+    # with eps = 0, scaling x by 2^k scales the mean square by 4^k and the root by 2^k exactly
+    x = _rand(8, (5, 64), 0.0, 1.0, fmt)
+    w = _rand(9, (64,), 1.0, 0.1, fmt)
+    y0 = oracle.rmsnorm(x, w, fmt, 0.0)
+    for k in [-1, 2, 5]:
+        xs = synth.to_storage(_f64(x, fmt) * 2.0 ** k, fmt)
+        assert np.array_equal(_f64(xs, fmt), _f64(x, fmt) * 2.0 ** k)  # the scaling is exact
+        assert np.array_equal(oracle.rmsnorm(xs, w, fmt, 0.0), y0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rmsnorm_matches_torch_float64(fmt):
+    x = _rand(10, (64, 1000), 0.0, 1.0, fmt)
+    w = _rand(11, (1000,), 1.0, 0.1, fmt)
+    y = _f64(oracle.rmsnorm(x, w, fmt, 1e-6), fmt)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(_f64(x, fmt)), (1000,),
+                                       torch.from_numpy(_f64(w, fmt)), eps=1e-6).numpy()
+    # a once-rounded result is within half an ulp of the exact value
+    assert np.all(np.abs(y - ref) <= 0.5 * _ulp(ref, fmt) * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rmsnorm_reads_only_n_columns_and_divides_by_n(fmt):
+    # a row stored wider than n (a row stride): the pad never enters the sum
+    n = 1000
+    x = _rand(12, (6, n), 0.0, 1.0, fmt)
+    w = _rand(13, (n,), 1.0, 0.1, fmt)
+    wide = synth.to_storage(np.full((6, 1024), 7.0), fmt)
+    wide[:, :n] = x
+    y_tight = oracle.rmsnorm(x, w, fmt, 1e-6)
+    y_wide = oracle.rmsnorm(wide, w, fmt, 1e-6, n=n, y_stride=1016, fill=0x1234)
+    assert np.array_equal(y_wide[:, :n], y_tight)
+    assert np.all(y_wide[:, n:] == 0x1234)
+    # and the divisor is n: against exact brute force on a short ragged row
+    xr = _rand(14, (2, 24), 0.0, 1.0, fmt)
+    yr = oracle.rmsnorm(xr, None, fmt, 1e-6)
+    for r in range(2):
+        assert [int(v) for v in yr[r]] == exact.rmsnorm_ref(xr[r], None, fmt, 1e-6)
+
+
+def test_rmsnorm_zero_row_is_zero():
+    x = np.zeros((2, 16), dtype=np.uint16)
+    y = oracle.rmsnorm(x, None, "bf16", 1e-6)
+    assert np.all(y == 0)
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("affine", [True, False])
+def test_layernorm_brute_force_4x8(fmt, affine):
+    for seed in range(6):
+        x = _rand(300 + seed, (4, 8), 0.5, 2.0, fmt)
+        g = _rand(400 + seed, (8,), 1.0, 0.1, fmt) if affine else None
+        b = _rand(500 + seed, (8,), 0.0, 0.1, fmt) if affine else None
+        eps = [1e-5, 1e-3, 0.5][seed % 3]
+        y = oracle.layernorm(x, g, b, fmt, eps)
+        for r in range(4):
+            assert [int(v) for v in y[r]] == exact.layernorm_ref(x[r], g, b, fmt, eps), (seed, r)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_layernorm_constant_row_returns_beta(fmt):
+    g = _rand(15, (80,), 1.0, 0.1, fmt)
+    b = _rand(16, (80,), 0.0, 0.1, fmt)
+    for c in [0.0, 1.0, -3.5]:
+        x = synth.to_storage(np.full((2, 80), c), fmt)
+        y = oracle.layernorm(x, g, b, fmt, 1e-5)
+        assert np.array_equal(y, np.broadcast_to(b, y.shape)), c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_layernorm_matches_torch_float64(fmt):
+    x = _rand(17, (64, 1000), 0.5, 2.0, fmt)
+    g = _rand(18, (1000,), 1.0, 0.1, fmt)
+    b = _rand(19, (1000,), 0.0, 0.1, fmt)
+    y = _f64(oracle.layernorm(x, g, b, fmt, 1e-5), fmt)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(_f64(x, fmt)), (1000,),
+                                         torch.from_numpy(_f64(g, fmt)),
+                                         torch.from_numpy(_f64(b, fmt)), eps=1e-5).numpy()
+    assert np.all(np.abs(y - ref) <= 0.5 * _ulp(ref, fmt) * (1 + 1e-6) + 1e-300)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_layernorm_standardises(fmt):
+    # without affine and with eps = 0 the output has mean 0 and variance 1, up to rounding
+    x = _rand(20, (8, 4096), 0.5, 2.0, fmt)
+    y = _f64(oracle.layernorm(x, None, None, fmt, 0.0), fmt)
+    tol = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -11
+    assert np.all(np.abs(y.mean(axis=1)) < tol)
+    assert np.all(np.abs(y.var(axis=1) - 1.0) < 4 * tol)
