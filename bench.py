@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM bandwidth of the fused RMSNorm -> RoPE -> per-token
+FP8 row operator on one MI355X (4096 tokens x 4096 channels = 32 heads x 128,
+bf16 in, NeoX rotation over every head with bf16 cos/sin [4096, 64],
+E4M3FN codes + binary32 per-token scales out).
+
+One step = one launch of the operator over one 4096 x 4096 batch.  The batch
+rotates over --sets independent input/output buffer sets (default 8 x 51.4 MB,
+more than the 256 MB last-level cache), so every launch reads inputs that sit
+in HBM rather than in cache.  The K timed steps are captured once into a HIP
+graph and replayed, bracketed by HIP events on the launch stream; the events
+give the average launch duration, and
+
+    achieved GB/s = counted bytes per launch / average launch duration
+
+where counted bytes are the byte-ledger minimum of one launch (every input
+read once, every output written once): 51,404,800 B for this workload.
+
+`traffic` reports HBM bytes per launch measured with rocprofv3 counters
+(FETCH_SIZE, WRITE_SIZE, scaled by the same counters on a plain copy of known
+size) as stored in profiles/traffic.json, and only while the kernel sources
+are the ones those counters were taken on; otherwise null.
+
+`cpu_baseline` times the CPU checker (single-threaded C, float64) on a bounded
+sample of the same workload on this host.
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (% of MI355X peak), fused RMSNorm+RoPE+FP8 4096x4096"
+DEFAULT_WORKLOAD = "rmsnorm_rope_fp8_4096x4096_bf16"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "quant_row_workgroup_amd", "csrc", "*")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, src_hash: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(workload)
+    if not rec or rec.get("kernel_src_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ---------------------------------------------------------------- GPU side
+class Workload:
+    """Device buffers for `sets` independent batches and one raw C-ABI call per step."""
+
+    def __init__(self, name: str, sets: int):
+        import numpy as np
+        import torch
+
+        import quant_row_workgroup_amd as qrw
+        from quant_row_workgroup_amd import ledger, synth
+
+        self.name = name
+        self.cfg = dict(synth.WORKLOADS[name])
+        self.inp = synth.make_inputs(name)
+        self.counted = ledger.counted_bytes(self.cfg)
+        self.lib = qrw.load()
+        dev = torch.device("cuda:0")
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+        def up(bits, dt):
+            if dt == "f32":
+                return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt[dt]).to(dev)
+
+        op = self.cfg["op"]
+        dt = self.cfg["dtype"]
+        code = {"f16": 1, "bf16": 2, "f32": 3}
+        base = {k: up(v, self.cfg.get("cs_dtype", dt) if k in ("cos", "sin") else dt)
+                for k, v in self.inp.items() if k in ("x", "w", "gamma", "beta", "cos", "sin")}
+        self.sets = []
+        for _ in range(sets):
+            s = {k: v.clone() for k, v in base.items()}
+            if op == "fused":
+                T = self.cfg["tokens"]
+                n = self.cfg["heads"] * self.cfg["head_dim"]
+                s["q"] = torch.empty((T, n), dtype=torch.uint8, device=dev)
+                s["scales"] = torch.empty((T,), dtype=torch.float32, device=dev)
+            else:
+                s["y"] = torch.empty_like(s["x"])
+            self.sets.append(s)
+        self.op = op
+        self.code = code
+        torch.cuda.synchronize()
+
+    def launch(self, i: int, stream_ptr: int) -> None:
+        s = self.sets[i % len(self.sets)]
+        c = self.cfg
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(stream_ptr)
+        if self.op == "fused":
+            T, H, D, R = c["tokens"], c["heads"], c["head_dim"], c["rope_dim"]
+            rc = self.lib.rmsnorm_rope_fp8_fwd(p(s["x"]), p(s["w"]), p(s["cos"]), p(s["sin"]),
+                                               p(s["q"]), p(s["scales"]), T, H, D, R, H * D,
+                                               H * D, self.code[c["dtype"]],
+                                               self.code[c["cs_dtype"]], int(c["neox"]),
+                                               c["eps"], st)
+        elif self.op == "rmsnorm":
+            rc = self.lib.rmsnorm_fwd(p(s["x"]), p(s["w"]), p(s["y"]), c["rows"], c["n"], c["n"],
+                                      c["n"], self.code[c["dtype"]], c["eps"], st)
+        elif self.op == "layernorm":
+            rc = self.lib.layernorm_fwd(p(s["x"]), p(s["gamma"]), p(s["beta"]), p(s["y"]),
+                                        c["rows"], c["n"], c["n"], c["n"], self.code[c["dtype"]],
+                                        c["eps"], st)
+        else:
+            T, H, D, R = c["tokens"], c["heads"], c["head_dim"], c["rope_dim"]
+            fn = self.lib.rope_apply_neox if c.get("neox", True) else self.lib.rope_apply_interleaved
+            rc = fn(p(s["x"]), p(s["cos"]), p(s["sin"]), p(s["y"]), T, H, D, R, H * D, H * D,
+                    self.code[c["dtype"]], self.code[c["cs_dtype"]], st)
+        if rc != 0:
+            raise RuntimeError(f"{self.name}: launch returned status {rc}")
+
+    def outputs(self, i: int):
+        s = self.sets[i % len(self.sets)]
+        return [s[k].clone() for k in ("q", "scales", "y") if k in s]
+
+
+def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
+    import torch
+
+    cur = torch.cuda.current_stream()
+    for i in range(warmup):
+        wl.launch(i, cur.cuda_stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(cur)
+        with torch.cuda.graph(g, stream=cap):
+            sp = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                wl.launch(i, sp)
+        torch.cuda.synchronize()
+        g.replay()  # untimed replay: first-launch costs of the graph
+        torch.cuda.synchronize()
+        # the graph's outputs match an eager launch bit for bit
+        ref = wl.outputs(steps - 1)
+        wl.launch(steps - 1, cur.cuda_stream)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, wl.outputs(steps - 1)):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from eager launch")
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+    else:
+        start.record()
+        for i in range(steps):
+            wl.launch(i, cur.cuda_stream)
+        end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+# ---------------------------------------------------------------- CPU side
+def cpu_baseline(name: str, seconds: float):
+    import oracle
+    from quant_row_workgroup_amd import ledger, synth
+
+    rows = 256
+    inp = synth.make_inputs(name, rows=rows)
+    cfg = dict(synth.WORKLOADS[name])
+    op = cfg["op"]
+    key = "tokens" if op in ("rope", "fused") else "rows"
+    cfg[key] = rows
+    bytes_per_call = ledger.counted_bytes(cfg)
+
+    def call():
+        if op == "fused":
+            oracle.rmsnorm_rope_fp8(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg["heads"],
+                                    cfg["head_dim"], cfg["rope_dim"], cfg["dtype"],
+                                    cfg["cs_dtype"], cfg["neox"], cfg["eps"])
+        elif op == "rmsnorm":
+            oracle.rmsnorm(inp["x"], inp["w"], cfg["dtype"], cfg["eps"])
+        elif op == "layernorm":
+            oracle.layernorm(inp["x"], inp["gamma"], inp["beta"], cfg["dtype"], cfg["eps"])
+        else:
+            oracle.rope(inp["x"], inp["cos"], inp["sin"], cfg["heads"], cfg["head_dim"],
+                        cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], True)
+
+    call()  # warm-up
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        call()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = bytes_per_call * reps / el / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{rows} of {synth.WORKLOADS[name].get('tokens', synth.WORKLOADS[name].get('rows'))} "
+                   f"rows of the same workload, {reps} calls in {el:.1f} s, single-threaded "
+                   f"float64 C checker on {cpu_model()} ({os.cpu_count()} logical CPUs present)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the row operators shard by tokens "
+              "with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no ROCm device visible", file=sys.stderr)
+        return 1
+
+    from quant_row_workgroup_amd import synth
+
+    wl = Workload(args.workload, args.sets)
+    print(f"[bench] {args.workload}: {args.sets} sets, warmup {args.warmup}, steps {args.steps}, "
+          f"mode {args.mode}", file=sys.stderr, flush=True)
+    ms = time_gpu(wl, args.steps, args.warmup, args.mode)
+    gbs = wl.counted / (ms * 1e-3) / 1e9
+    print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+    src_hash = kernel_source_hash()
+    traffic = stored_traffic(args.workload, src_hash)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    c = wl.cfg
+    if c["op"] == "fused":
+        cfg = {"workload": (f"fused RMSNorm+RoPE(NeoX)+per-token E4M3 quant, {c['tokens']} tokens x "
+                            f"{c['heads'] * c['head_dim']} ({c['heads']} heads x {c['head_dim']}) "
+                            f"{c['dtype']} in, {c['cs_dtype']} cos/sin [{c['tokens']},"
+                            f"{c['rope_dim'] // 2}], e4m3 codes + f32 scales out"),
+               "tokens": c["tokens"], "hidden": c["heads"] * c["head_dim"], "heads": c["heads"],
+               "head_dim": c["head_dim"], "rope_dim": c["rope_dim"]}
+    else:
+        cfg = {"workload": args.workload}
+    cfg.update({"input_sets": args.sets, "counted_bytes_per_step": wl.counted,
+                "timing": f"{args.mode}, HIP events on the launch stream"})
+
+    line = {
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else f"achieved HBM GB/s, {args.workload}",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": cfg,
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "kernel_src_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

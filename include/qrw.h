@@ -1,0 +1,142 @@
+/*
+ * qrw.h -- C ABI of the fused row-operator library (libqrw.so, gfx950).
+ *
+ * The operations are those defined on the page "TileLang tutorial, ch. 13:
+ * elementwise, normalisation and RoPE operators" (tilelang-tutorial.huandu.me,
+ * chapter 13), cited below by section:
+ *   s3.2.1  reference RMSNorm and LayerNorm
+ *   s3.3.1  the two RoPE pairings, the (positions, rope_dim/2) cos/sin table,
+ *           and partial rotation of the tail span of a head
+ *   s3.3.2  reference RoPE (fp32 math, one final cast)
+ *   s3.1.5  per-token FP8 cast (amax -> scale -> clamp -> cast)
+ *   s3.3.4  the fused RMSNorm + RoPE + per-token quantisation operator
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or synchronises, keeps no mutable
+ *   global state and is safe to call from several host threads.
+ * Layout.  Row-major.  A "row" (or a token) is `n` contiguous elements; rows
+ *   are `*_row_stride` ELEMENTS apart.  Heads are packed inside a token:
+ *   head h occupies elements [h*head_dim, (h+1)*head_dim).
+ * Granules.  Rows are moved in 16-byte granules, so: `n` (or head_dim) is a
+ *   multiple of 8, row strides are multiples of 8 elements, and every tensor
+ *   base pointer is 16-byte aligned.  Weight vectors and tables are packed.
+ *   With zero rows (tokens) nothing is read or written and pointers may be
+ *   NULL.
+ * Dtypes.  `dtype` is QRW_F16 or QRW_BF16 and applies to x, y and the weight
+ *   vectors.  RoPE tables have `cs_dtype`, either QRW_F32 or equal to dtype.
+ * Numerics.  All arithmetic is binary32; every 16-bit or FP8 output is
+ *   rounded once, to nearest-even, from the binary32 result.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *   asynchronous on it; argument errors are reported before anything is
+ *   enqueued.
+ * Errors.  Each call returns QRW_OK or a negative QRW_ERR_* code.  A call that
+ *   fails validation has no side effects and launches nothing.  Empty inputs
+ *   (rows or tokens == 0) are valid and launch nothing.  QRW_ERR_LAUNCH means
+ *   the HIP launch itself failed (hipGetLastError after the launch).
+ */
+#ifndef QRW_H_
+#define QRW_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum qrw_dtype { QRW_F16 = 1, QRW_BF16 = 2, QRW_F32 = 3 };
+
+/* status codes */
+enum qrw_status {
+  QRW_OK = 0,
+  QRW_ERR_NULL = -1,    /* a required pointer is NULL */
+  QRW_ERR_DTYPE = -2,   /* unsupported dtype / cs_dtype code */
+  QRW_ERR_SHAPE = -3,   /* a size is negative, not a multiple of its granule, or too large */
+  QRW_ERR_STRIDE = -4,  /* a row stride is shorter than the row or not a multiple of 8 */
+  QRW_ERR_ALIGN = -5,   /* a pointer is not 16-byte aligned */
+  QRW_ERR_ALIAS = -6,   /* output overlaps an input other than as an exact in-place alias */
+  QRW_ERR_LAUNCH = -7,  /* the kernel launch failed */
+  QRW_ERR_VALUE = -8    /* a scalar argument is out of range (eps negative or not finite) */
+};
+
+/* Largest row length, in elements, that one call handles (8192). */
+#define QRW_MAX_ROW 8192
+
+/*
+ * RMSNorm forward (s3.2.1):
+ *   rstd_r = 1 / sqrt( (1/n) * sum_j x[r,j]^2 + eps )
+ *   y[r,j] = x[r,j] * rstd_r * weight[j]          (weight == NULL: weight = 1)
+ * x, y: [rows, n] with row strides x_row_stride / y_row_stride (elements).
+ * weight: [n], packed, same dtype, or NULL.
+ * y == x (same stride) computes in place; any other overlap is QRW_ERR_ALIAS.
+ */
+int rmsnorm_fwd(const void* x, const void* weight, void* y, int64_t rows, int64_t n,
+                int64_t x_row_stride, int64_t y_row_stride, int dtype, float eps,
+                void* stream);
+
+/*
+ * LayerNorm forward (s3.2.1, torch.nn.functional.layer_norm semantics):
+ *   mu_r = (1/n) sum_j x[r,j];   var_r = (1/n) sum_j (x[r,j] - mu_r)^2  (biased)
+ *   y[r,j] = (x[r,j] - mu_r) / sqrt(var_r + eps) * gamma[j] + beta[j]
+ * gamma / beta: [n] or NULL (1 and 0).  Layout and aliasing as rmsnorm_fwd.
+ */
+int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                  int64_t n, int64_t x_row_stride, int64_t y_row_stride, int dtype,
+                  float eps, void* stream);
+
+/*
+ * RoPE, interleaved pairing (s3.3.1, s3.3.2).  x, y: [tokens, heads*head_dim]
+ * with token strides (elements).  In each head the tail span of rope_dim
+ * channels starting at S = head_dim - rope_dim rotates; channels before S are
+ * copied unchanged.  With R = rope_dim and pair p in [0, R/2):
+ *   a = S + 2p, b = S + 2p + 1,  c = cos[t, p],  s = sin[t, p]
+ *   y[a] = x[a] c - x[b] s;      y[b] = x[a] s + x[b] c
+ * cos, sin: [tokens, R/2] packed, cs_dtype (QRW_F32 or dtype); row t is the
+ * angle table of token t, shared by all heads.
+ * Requires head_dim % 8 == 0, rope_dim % 16 == 0, 16 <= rope_dim <= head_dim.
+ * y == x (same stride) rotates in place; other overlap is QRW_ERR_ALIAS.
+ */
+int rope_apply_interleaved(const void* x, const void* cos, const void* sin, void* y,
+                           int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_dim,
+                           int64_t x_token_stride, int64_t y_token_stride, int dtype,
+                           int cs_dtype, void* stream);
+
+/*
+ * RoPE, NeoX half-split pairing (s3.3.1, s3.3.2): as rope_apply_interleaved
+ * but with a = S + p, b = S + p + R/2.
+ */
+int rope_apply_neox(const void* x, const void* cos, const void* sin, void* y, int64_t tokens,
+                    int64_t heads, int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
+                    int64_t y_token_stride, int dtype, int cs_dtype, void* stream);
+
+/*
+ * Fused RMSNorm -> RoPE -> per-token FP8 quantisation (s3.3.4 with the
+ * per-token cast of s3.1.5).  Per token t, over its n = heads*head_dim channels:
+ *   z      = RoPE( x[t,:] * rstd_t * weight )       (no rounding in between;
+ *            RoPE on each head's tail span, pairing chosen by `neox`:
+ *            1 = NeoX half-split, 0 = interleaved; formulas as above)
+ *   amax_t = max_j |z_j|
+ *   scales[t] = max(amax_t, 1e-4) / 448                         (binary32)
+ *   q[t,j]    = E4M3FN( clamp(z_j / scales[t], -448, 448) )     (OCP FP8, RNE)
+ * x: [tokens, n] with x_token_stride (elements); weight: [n] or NULL;
+ * cos, sin: [tokens, rope_dim/2] (cs_dtype); q: [tokens, n] uint8 codes with
+ * q_token_stride (bytes, a multiple of 8); scales: [tokens] float, 4-byte
+ * aligned.  Requires n <= QRW_MAX_ROW and the head/rope constraints of RoPE.
+ * Dequantisation is q * scales[t].
+ */
+int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, const void* sin,
+                         uint8_t* q, float* scales, int64_t tokens, int64_t heads,
+                         int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
+                         int64_t q_token_stride, int dtype, int cs_dtype, int neox, float eps,
+                         void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* qrw_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QRW_H_ */

@@ -1,0 +1,18 @@
+"""Fused memory-bound LLM row operators for AMD MI355X (gfx950).
+
+RMSNorm, LayerNorm, RoPE (interleaved and NeoX half-split) and the fused
+RMSNorm -> RoPE -> per-token FP8 (E4M3FN) quantisation, as hand-written HIP
+kernels behind a C ABI (include/qrw.h, libqrw.so).  The Python functions here
+are a thin ctypes binding with the same names.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    QrwError,
+    layernorm_fwd,
+    load,
+    rmsnorm_fwd,
+    rmsnorm_rope_fp8_fwd,
+    rope_apply_interleaved,
+    rope_apply_neox,
+)

@@ -1,0 +1,172 @@
+"""ctypes binding of libqrw.so: argument marshalling only.
+
+Each function takes torch tensors that live on a ROCm device, turns them into
+the pointers, sizes and strides of the C ABI (include/qrw.h) and calls the
+entry point of the same name on torch's current stream.  Every step of the
+computation runs in the library's HIP kernels; nothing here computes, and
+there is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # the library shares torch's HIP runtime: load torch first
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqrw.so")
+
+F16, BF16, F32 = 1, 2, 3
+_DTYPE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+STATUS = {
+    0: "QRW_OK", -1: "QRW_ERR_NULL", -2: "QRW_ERR_DTYPE", -3: "QRW_ERR_SHAPE",
+    -4: "QRW_ERR_STRIDE", -5: "QRW_ERR_ALIGN", -6: "QRW_ERR_ALIAS", -7: "QRW_ERR_LAUNCH",
+    -8: "QRW_ERR_VALUE",
+}
+
+EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
+           "rmsnorm_rope_fp8_fwd", "qrw_status_string")
+
+
+class QrwError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libqrw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m quant_row_workgroup_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, f32, vp]
+    L.layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, vp]
+    rope_args = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.rope_apply_interleaved.argtypes = rope_args
+    L.rope_apply_neox.argtypes = rope_args
+    L.rmsnorm_rope_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                       i32, i32, i32, f32, vp]
+    for name in EXPORTS[:-1]:
+        getattr(L, name).restype = i32
+    L.qrw_status_string.argtypes = [i32]
+    L.qrw_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QrwError(fn, status, load().qrw_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t):
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with a unit last stride, got {tuple(t.shape)} "
+                         f"strides {t.stride()}")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _vec(t, n, name):
+    if t is None:
+        return None
+    if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a packed vector of length {n}")
+    return t
+
+
+# ------------------------------------------------------------------ entry points
+def rmsnorm_fwd(x, weight=None, eps: float = 1e-6, out=None):
+    """RMSNorm over the last dim of 2-D ``x``; returns ``out``."""
+    rows, n, xs = _rows(x, "x")
+    out = torch.empty((rows, n), dtype=x.dtype, device=x.device) if out is None else out
+    _, _, ys = _rows(out, "out")
+    st = load().rmsnorm_fwd(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(out), rows, n, xs,
+                            ys, _dtype(x), eps, _stream(x))
+    _check("rmsnorm_fwd", st)
+    return out
+
+
+def layernorm_fwd(x, gamma=None, beta=None, eps: float = 1e-5, out=None):
+    rows, n, xs = _rows(x, "x")
+    out = torch.empty((rows, n), dtype=x.dtype, device=x.device) if out is None else out
+    _, _, ys = _rows(out, "out")
+    st = load().layernorm_fwd(_ptr(x), _ptr(_vec(gamma, n, "gamma")),
+                              _ptr(_vec(beta, n, "beta")), _ptr(out), rows, n, xs, ys,
+                              _dtype(x), eps, _stream(x))
+    _check("layernorm_fwd", st)
+    return out
+
+
+def _rope(fn, x, cos, sin, heads, head_dim, rope_dim, out):
+    tokens, n, xs = _rows(x, "x")
+    if heads * head_dim != n:
+        raise ValueError("heads * head_dim must equal the row length")
+    out = torch.empty((tokens, n), dtype=x.dtype, device=x.device) if out is None else out
+    _, _, ys = _rows(out, "out")
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    st = getattr(load(), fn)(_ptr(x), _ptr(cos), _ptr(sin), _ptr(out), tokens, heads, head_dim,
+                             rope_dim, xs, ys, _dtype(x), _dtype(cos), _stream(x))
+    _check(fn, st)
+    return out
+
+
+def rope_apply_interleaved(x, cos, sin, heads: int, head_dim: int, rope_dim: int | None = None,
+                           out=None):
+    return _rope("rope_apply_interleaved", x, cos, sin, heads, head_dim,
+                 head_dim if rope_dim is None else rope_dim, out)
+
+
+def rope_apply_neox(x, cos, sin, heads: int, head_dim: int, rope_dim: int | None = None,
+                    out=None):
+    return _rope("rope_apply_neox", x, cos, sin, heads, head_dim,
+                 head_dim if rope_dim is None else rope_dim, out)
+
+
+def rmsnorm_rope_fp8_fwd(x, weight, cos, sin, heads: int, head_dim: int,
+                         rope_dim: int | None = None, neox: bool = True, eps: float = 1e-6,
+                         q=None, scales=None):
+    """Returns (codes uint8 [tokens, n], scales float32 [tokens])."""
+    tokens, n, xs = _rows(x, "x")
+    if heads * head_dim != n:
+        raise ValueError("heads * head_dim must equal the row length")
+    rd = head_dim if rope_dim is None else rope_dim
+    if q is None:
+        q = torch.empty((tokens, n), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((tokens,), dtype=torch.float32, device=x.device)
+    _, _, qs = _rows(q, "q")
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    st = load().rmsnorm_rope_fp8_fwd(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(cos),
+                                     _ptr(sin), _ptr(q), _ptr(scales), tokens, heads, head_dim,
+                                     rd, xs, qs, _dtype(x), _dtype(cos), int(bool(neox)), eps,
+                                     _stream(x))
+    _check("rmsnorm_rope_fp8_fwd", st)
+    return q, scales

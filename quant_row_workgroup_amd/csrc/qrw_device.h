@@ -1,0 +1,176 @@
+// qrw_device.h -- device primitives shared by the row-operator kernels (gfx950).
+//
+// * 16-byte granules: each lane moves 8 x 16-bit elements with one
+//   global_load_dwordx4 / global_store_dwordx4.
+// * widening of f16/bf16 to f32 (exact) and narrowing with one
+//   round-to-nearest-even step (v_cvt_pk_bf16_f32, v_cvt_f16_f32).
+// * wave64 reductions: a DPP butterfly inside each 16-lane row (quad_perm
+//   xor-1, xor-2, half-row mirror, row mirror), then the four row results are
+//   read with v_readlane and combined in a fixed order.  Every lane of a wave
+//   ends with the same bits, and the reduction tree does not depend on the
+//   launch shape, so a row gives the same result in any batch.
+// * E4M3FN packing with v_cvt_pk_fp8_f32 (OCP FP8 on gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qrw {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- memory
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// ------------------------------------------------------- element formats
+struct F16 {
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+struct BF16 {
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return __builtin_bit_cast(float, u << 16);
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return __builtin_bit_cast(float, u & 0xFFFF0000u);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+// Widen one granule (8 elements) to f32.
+template <typename T>
+__device__ __forceinline__ void widen8(u32x4 g, float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = T::lo(g[k]);
+    v[2 * k + 1] = T::hi(g[k]);
+  }
+}
+
+// Narrow 8 f32 values to one granule.
+template <typename T>
+__device__ __forceinline__ u32x4 narrow8(const float (&v)[8]) {
+  u32x4 g;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) g[k] = T::pack(v[2 * k], v[2 * k + 1]);
+  return g;
+}
+
+// Eight f32 table entries starting at element 8*s of a table row.  (The
+// entries are read as float vectors: __builtin_bit_cast applied directly to an
+// element of an ext_vector_type value reads the wrong lane with this compiler,
+// so no vector element is ever bit-cast in place.)
+template <typename CS>
+struct Table8;
+template <>
+struct Table8<float> {
+  static __device__ __forceinline__ void load(const void* row, int s, float (&v)[8]) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row) + 2 * s;
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[4 + k] = b[k];
+    }
+  }
+};
+template <>
+struct Table8<F16> {
+  static __device__ __forceinline__ void load(const void* row, int s, float (&v)[8]) {
+    widen8<F16>(ld16(reinterpret_cast<const uint16_t*>(row) + 8 * s), v);
+  }
+};
+template <>
+struct Table8<BF16> {
+  static __device__ __forceinline__ void load(const void* row, int s, float (&v)[8]) {
+    widen8<BF16>(ld16(reinterpret_cast<const uint16_t*>(row) + 8 * s), v);
+  }
+};
+
+// ----------------------------------------------------------- wave64 reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
+
+// Sum over the 64 lanes; every lane receives the same value.  All lanes must
+// be active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// Max over the 64 lanes (inputs are >= 0 or -0).  All lanes must be active.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// Sum of squares of the two 16-bit elements of a packed pair, added to acc,
+// in one v_dot2c_f32_{bf16,f16}: the products of 16-bit values are exact in
+// binary32.  (The pair is taken by value: see the note on Table8<float>.)
+__device__ __forceinline__ float sumsq2(F16, uint32_t u, float acc) {
+  const f16x2 h = __builtin_bit_cast(f16x2, u);
+  return __builtin_amdgcn_fdot2(h, h, acc, false);
+}
+__device__ __forceinline__ float sumsq2(BF16, uint32_t u, float acc) {
+  const bf16x2 h = __builtin_bit_cast(bf16x2, u);
+  return __builtin_amdgcn_fdot2_f32_bf16(h, h, acc, false);
+}
+
+// Pairwise sum of eight per-slot partial sums, in a fixed tree.
+__device__ __forceinline__ float tree8(const float (&a)[8]) {
+  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// ----------------------------------------------------------------- FP8
+// Eight f32 values (already scaled into [-448, 448]) to eight E4M3FN codes,
+// element k in byte k.
+__device__ __forceinline__ u32x2 fp8x8(const float (&v)[8]) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+  return (u32x2){(uint32_t)lo, (uint32_t)hi};
+}
+
+}  // namespace qrw

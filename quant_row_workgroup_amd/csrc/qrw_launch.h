@@ -1,0 +1,35 @@
+// qrw_launch.h -- internal launchers behind the C ABI.  Arguments arrive here
+// already validated (qrw_api.hip); each launcher picks a kernel instance for
+// the row length and enqueues it on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qrw {
+
+// Threads per workgroup for the row kernels: four waves, one row per wave.
+constexpr int kBlock = 256;
+constexpr int kRowsPerBlock = kBlock / 64;
+
+hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t n,
+                          int64_t xs, int64_t ys, int dtype, float eps, hipStream_t stream);
+
+hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y, int64_t rows,
+                            int64_t n, int64_t xs, int64_t ys, int dtype, float eps,
+                            hipStream_t stream);
+
+hipError_t launch_rope(const void* x, const void* cos, const void* sin, void* y, int64_t tokens,
+                       int64_t heads, int64_t head_dim, int64_t rope_dim, int64_t xs,
+                       int64_t ys, int dtype, int cs_dtype, bool neox, hipStream_t stream);
+
+hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos,
+                                   const void* sin, uint8_t* q, float* scales, int64_t tokens,
+                                   int64_t heads, int64_t head_dim, int64_t rope_dim,
+                                   int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
+                                   float eps, hipStream_t stream);
+
+// Number of "items" (pairs of granules) one token of the fused operator holds.
+int64_t fused_items(int64_t heads, int64_t head_dim, int64_t rope_dim);
+
+}  // namespace qrw

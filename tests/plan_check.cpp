@@ -1,0 +1,114 @@
+// CPU check of the token-row plan used by the RoPE and fused kernels
+// (quant_row_workgroup_amd/csrc/qrw_plan.h): every offset a lane can form is
+// inside the row, every granule is covered exactly once, rotation pairs sit
+// in one item, and the one-table-granule-per-lane shortcut is valid when
+// enabled.  Built with g++ by tests/test_plan.py; prints "OK" on success.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "qrw_plan.h"
+
+using namespace qrw;
+
+static int fails = 0;
+#define CHECK(c, ...)                 \
+  do {                                \
+    if (!(c)) {                       \
+      if (fails < 20) {               \
+        std::printf(__VA_ARGS__);     \
+        std::printf("\n");            \
+      }                               \
+      ++fails;                        \
+    }                                 \
+  } while (0)
+
+static void check_shape(int heads, int head_dim, int rope_dim, bool neox, int kmax) {
+  RowPlan p = make_plan(heads, head_dim, rope_dim);
+  const int n = heads * head_dim;
+  std::vector<int> cover(n / 8, 0);
+  // the kernels visit items lane + 64*i for i < K (fused: one pass, K = kmax;
+  // RoPE: passes of 64*K) -- visit a generous superset of indices
+  const int limit = p.n_items + 64 * kmax;
+  for (int it = 0; it < limit; ++it) {
+    int a, b, s;
+    int kind = item_offsets(p, it, neox, a, b, s);
+    if (it >= p.n_items) {
+      CHECK(kind == kItemNone, "item %d beyond n_items has kind %d", it, kind);
+      continue;
+    }
+    CHECK(kind != kItemNone, "item %d < n_items=%d is empty (h=%d D=%d R=%d)", it, p.n_items,
+          heads, head_dim, rope_dim);
+    CHECK(a >= 0 && a % 8 == 0 && a + 8 <= n, "A out of row: it=%d a=%d n=%d", it, a, n);
+    if (b >= 0) CHECK(b % 8 == 0 && b + 8 <= n, "B out of row: it=%d b=%d n=%d", it, b, n);
+    if (a >= 0 && a + 8 <= n) cover[a / 8]++;
+    if (b >= 0 && b + 8 <= n) cover[b / 8]++;
+    if (kind == kItemRope) {
+      CHECK(b >= 0, "rope item without B");
+      CHECK(s >= 0 && s < p.gph && 8 * s + 8 <= rope_dim / 2, "table granule out of range");
+      const int h = a / head_dim;
+      const int off = a - h * head_dim;  // offset inside the head
+      const int start = head_dim - rope_dim;
+      CHECK(off >= start, "rope granule before the span");
+      CHECK(b / head_dim == h, "pair crosses heads");
+      if (neox) {
+        CHECK(off - start == 8 * s && b - a == rope_dim / 2, "neox pairing wrong");
+      } else {
+        CHECK(off - start == 16 * s && b - a == 8, "interleaved pairing wrong");
+      }
+      if (p.lane_hoist) CHECK(s == (it % 64) % p.gph, "lane hoist invalid at it=%d", it);
+    } else if (kind == kItemPlain) {
+      const int off = a % head_dim;
+      CHECK(off < head_dim - rope_dim, "plain granule inside the span");
+      if (b >= 0) CHECK(b % head_dim < head_dim - rope_dim, "plain B inside the span");
+    }
+  }
+  for (int g = 0; g < n / 8; ++g)
+    CHECK(cover[g] == 1, "granule %d covered %d times (h=%d D=%d R=%d)", g, cover[g], heads,
+          head_dim, rope_dim);
+}
+
+int main() {
+  // exhaustive: the largest item count over every accepted shape fits one
+  // fused launch (64 lanes x 8 items)
+  int worst = 0;
+  for (int D = 8; D <= 8192; D += 8)
+    for (int R = 16; R <= D; R += 16)
+      for (int H = 1; H * D <= 8192; ++H) {
+        RowPlan p = make_plan(H, D, R);
+        if (p.n_items > worst) worst = p.n_items;
+      }
+  CHECK(worst <= 512, "an accepted shape needs %d items > 512", worst);
+  std::printf("max items per token: %d\n", worst);
+  // fast-division identity over the whole range used
+  for (int d = 1; d < 1100; ++d) {
+    FastDiv f = make_fastdiv(d);
+    for (int x = 0; x < 4200; ++x) CHECK(fastdiv(f, x) == x / d, "fastdiv %d / %d", x, d);
+  }
+  // coverage of a spread of shapes, including the benchmark ones
+  const int shapes[][3] = {{32, 128, 128}, {1, 4096, 128}, {32, 128, 64}, {8, 64, 16},
+                           {3, 48, 32},    {1, 8192, 16},  {64, 128, 128}, {5, 24, 16},
+                           {2, 8, 8},      {7, 96, 96},    {1, 16, 16},    {4, 256, 128},
+                           {1, 1000, 16},  {13, 40, 32},   {16, 512, 512}, {2, 4096, 4096},
+                           {1, 8184, 16},  {11, 72, 48}};
+  for (auto& s : shapes) {
+    if (s[2] % 16 != 0) continue;
+    for (int nx = 0; nx < 2; ++nx) check_shape(s[0], s[1], s[2], nx == 1, 8);
+  }
+  // a random sweep
+  std::srand(1234);
+  for (int k = 0; k < 3000; ++k) {
+    int D = 8 * (1 + std::rand() % 256);
+    if (D < 16) D = 16;
+    int R = 16 * (1 + std::rand() % (D / 16));
+    int Hmax = 8192 / D;
+    int H = 1 + std::rand() % (Hmax < 40 ? Hmax : 40);
+    check_shape(H, D, R, (k & 1) != 0, 8);
+  }
+  if (fails) {
+    std::printf("FAILED %d checks\n", fails);
+    return 1;
+  }
+  std::printf("OK\n");
+  return 0;
+}

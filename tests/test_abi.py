@@ -1,0 +1,135 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/qrw.h declares, and rejects bad arguments with the documented status
+before touching the device.  Every call below is invalid (or empty) by
+construction, so none reaches a HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quant_row_workgroup_amd as qrw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qrw.h")
+
+OK, NULL, DTYPE, SHAPE, STRIDE, ALIGN, ALIAS, LAUNCH, VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F16, BF16, F32 = 1, 2, 3
+
+# fake, 16-byte aligned, far-apart "device" addresses; never dereferenced
+X, Y, W, C, S, Q, SC = (ctypes.c_void_p(a << 32) for a in range(1, 8))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_operators():
+    assert declared_functions() == sorted(qrw.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qrw.load()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = qrw.load()
+    for code in (OK, NULL, DTYPE, SHAPE, STRIDE, ALIGN, ALIAS, LAUNCH, VALUE):
+        s = L.qrw_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.qrw_status_string(-99).decode() == "unknown status"
+
+
+def rms(**kw):
+    a = dict(x=X, w=W, y=Y, rows=4, n=64, xs=64, ys=64, dtype=BF16, eps=1e-6)
+    a.update(kw)
+    return qrw.load().rmsnorm_fwd(a["x"], a["w"], a["y"], a["rows"], a["n"], a["xs"], a["ys"],
+                                  a["dtype"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(y=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(dtype=0), DTYPE), (dict(dtype=7), DTYPE),
+    (dict(n=60), SHAPE), (dict(n=0), SHAPE), (dict(n=8200), SHAPE), (dict(rows=-1), SHAPE),
+    (dict(xs=56), STRIDE), (dict(ys=60, n=56), STRIDE), (dict(xs=68), STRIDE),
+    (dict(x=ctypes.c_void_p((1 << 32) + 8)), ALIGN), (dict(y=ctypes.c_void_p((2 << 32) + 4)), ALIGN),
+    (dict(w=ctypes.c_void_p((3 << 32) + 2)), ALIGN),
+    (dict(eps=-1e-6), VALUE), (dict(eps=float("nan")), VALUE), (dict(eps=float("inf")), VALUE),
+    (dict(y=ctypes.c_void_p((1 << 32) + 64)), ALIAS),          # partial overlap with x
+    (dict(y=X, ys=72), ALIAS),                                  # same base, other stride
+    (dict(w=ctypes.c_void_p((2 << 32) + 32)), ALIAS),           # weight inside the output
+    (dict(rows=0), OK),                                         # empty: nothing launched
+    (dict(rows=0, x=None, y=None, w=None), OK),                 # empty tensors may have no storage
+    (dict(rows=0, dtype=F32), DTYPE),                           # but still a valid call
+])
+def test_rmsnorm_validation(kw, want):
+    assert rms(**kw) == want
+
+
+def ln(**kw):
+    a = dict(x=X, g=W, b=C, y=Y, rows=4, n=64, xs=64, ys=64, dtype=F16, eps=1e-5)
+    a.update(kw)
+    return qrw.load().layernorm_fwd(a["x"], a["g"], a["b"], a["y"], a["rows"], a["n"], a["xs"],
+                                    a["ys"], a["dtype"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(dtype=F32), DTYPE), (dict(n=12), SHAPE), (dict(xs=32), STRIDE),
+    (dict(b=ctypes.c_void_p((4 << 32) + 8)), ALIGN), (dict(eps=-1.0), VALUE),
+    (dict(y=ctypes.c_void_p((1 << 32) + 16)), ALIAS), (dict(rows=0), OK),
+])
+def test_layernorm_validation(kw, want):
+    assert ln(**kw) == want
+
+
+def rope(neox=True, **kw):
+    a = dict(x=X, c=C, s=S, y=Y, T=4, H=2, D=64, R=64, xs=128, ys=128, dtype=F16, cs=F32)
+    a.update(kw)
+    fn = qrw.load().rope_apply_neox if neox else qrw.load().rope_apply_interleaved
+    return fn(a["x"], a["c"], a["s"], a["y"], a["T"], a["H"], a["D"], a["R"], a["xs"], a["ys"],
+              a["dtype"], a["cs"], None)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("kw,want", [
+    (dict(c=None), NULL), (dict(s=None), NULL),
+    (dict(cs=BF16), DTYPE), (dict(dtype=F32), DTYPE),
+    (dict(R=8), SHAPE), (dict(R=24), SHAPE), (dict(R=80), SHAPE), (dict(D=60, R=16), SHAPE),
+    (dict(H=0), SHAPE), (dict(T=-2), SHAPE), (dict(H=200, D=64), SHAPE),
+    (dict(xs=120), STRIDE), (dict(ys=130), STRIDE),
+    (dict(c=ctypes.c_void_p((4 << 32) + 4)), ALIGN),
+    (dict(y=ctypes.c_void_p((1 << 32) + 128)), ALIAS),
+    (dict(c=ctypes.c_void_p((2 << 32) + 64)), ALIAS),
+    (dict(T=0), OK), (dict(T=0, x=None, y=None, c=None, s=None), OK),
+])
+def test_rope_validation(neox, kw, want):
+    assert rope(neox, **kw) == want
+
+
+def fused(**kw):
+    a = dict(x=X, w=W, c=C, s=S, q=Q, sc=SC, T=4, H=32, D=128, R=128, xs=4096, qs=4096,
+             dtype=BF16, cs=BF16, neox=1, eps=1e-6)
+    a.update(kw)
+    return qrw.load().rmsnorm_rope_fp8_fwd(a["x"], a["w"], a["c"], a["s"], a["q"], a["sc"],
+                                           a["T"], a["H"], a["D"], a["R"], a["xs"], a["qs"],
+                                           a["dtype"], a["cs"], a["neox"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(q=None), NULL), (dict(sc=None), NULL), (dict(c=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(cs=F16), DTYPE),
+    (dict(H=65), SHAPE), (dict(R=136), SHAPE), (dict(R=0), SHAPE),
+    (dict(xs=4000), STRIDE), (dict(qs=4100), STRIDE),
+    (dict(q=ctypes.c_void_p((5 << 32) + 8)), ALIGN), (dict(sc=ctypes.c_void_p((6 << 32) + 2)), ALIGN),
+    (dict(eps=float("-inf")), VALUE), (dict(neox=2), VALUE),
+    (dict(sc=ctypes.c_void_p((5 << 32) + 64)), ALIAS),   # scales inside the codes
+    (dict(q=ctypes.c_void_p((1 << 32) + 4096)), ALIAS),  # codes inside x
+    (dict(T=0), OK), (dict(T=0, x=None, q=None, sc=None, c=None, s=None), OK),
+    (dict(T=0, R=24), SHAPE),
+])
+def test_fused_validation(kw, want):
+    assert fused(**kw) == want

@@ -1,0 +1,103 @@
+"""GPU parity of rmsnorm_rope_fp8_fwd against the fp64 oracle through the C
+ABI: the benchmark configuration in full (32 heads x 128, NeoX, bf16 tables),
+the pages' own reading (one 4096-wide head rotating its last 128 channels),
+the interleaved pairing, binary16 inputs with binary32 tables, no weight,
+zero rows, the row-size limit, determinism and batch invariance.
+
+Bar: per-token scales within 1e-6 relative; codes bit-exact on >= 99.9% of
+elements and never more than one E4M3 step apart."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quant_row_workgroup_amd as qrw
+from quant_row_workgroup_amd import synth
+from tests.gpu_util import assert_codes, assert_scales, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, w, c, s, H, D, R, dt, cs, neox, eps=1e-6):
+    q, sc = qrw.rmsnorm_rope_fp8_fwd(dev(x, dt), None if w is None else dev(w, dt), dev(c, cs),
+                                     dev(s, cs), H, D, R, neox=neox, eps=eps)
+    return host(q), host(sc)
+
+
+def _check(x, w, c, s, H, D, R, dt, cs, neox, what, eps=1e-6):
+    q, sc = _run(x, w, c, s, H, D, R, dt, cs, neox, eps)
+    wq, wsc = oracle.rmsnorm_rope_fp8(x, w, c, s, H, D, R, dt, cs, neox, eps)
+    rel = assert_scales(sc, wsc, what=what)
+    st = assert_codes(q, wq, what=what)
+    return q, sc, dict(st, scale_rel=rel)
+
+
+def test_fused_workload():
+    name = "rmsnorm_rope_fp8_4096x4096_bf16"
+    inp = synth.make_inputs(name)
+    _, _, st = _check(inp["x"], inp["w"], inp["cos"], inp["sin"], inp["heads"],
+                      inp["head_dim"], inp["rope_dim"], inp["dtype"], inp["cs_dtype"],
+                      inp["neox"], name, inp["eps"])
+    print(name, st)
+
+
+def test_fused_pages_reading_one_head_tail_rotation():
+    # same tensor sizes, the rotation confined to the last 128 of 4096 channels
+    inp = synth.make_inputs("rmsnorm_rope_fp8_4096x4096_bf16", rows=1024)
+    _, _, st = _check(inp["x"], inp["w"], inp["cos"], inp["sin"], 1, 4096, 128, "bf16", "bf16",
+                      True, "one head")
+    print(st)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("dt,cs", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"),
+                                   ("f16", "f16")])
+@pytest.mark.parametrize("T,H,D,R", [(64, 32, 128, 128), (16, 8, 128, 64), (9, 3, 48, 32),
+                                     (8, 5, 96, 96), (5, 64, 128, 128), (7, 1, 1000, 16),
+                                     (3, 2, 24, 16), (1, 1, 16, 16), (12, 1, 8192, 512)])
+def test_fused_shapes(neox, dt, cs, T, H, D, R):
+    x = synth.normal(T + H + D + R, (T, H * D), 0.0, 3.0, dt, outlier_frac=0.01,
+                     outlier_mul=10.0)
+    w = synth.normal(T + H + D + R + 1, (H * D,), 1.0, 0.1, dt)
+    c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 10 else 5.0)
+    _check(x, w, c, s, H, D, R, dt, cs, neox, f"fused {T}x{H}x{D}/{R}")
+
+
+def test_fused_without_weight_and_zero_rows():
+    T, H, D = 40, 32, 128
+    x = synth.normal(21, (T, H * D), 0.0, 3.0, "bf16")
+    x[5] = 0
+    x[17] = 0
+    c, s = synth.rope_table(T, D, "bf16")
+    q, sc, _ = _check(x, None, c, s, H, D, D, "bf16", "bf16", True, "no weight")
+    # a zero row gives signed zeros (a zero times a negative cosine is -0 in both)
+    assert np.all((q[5] & 0x7F) == 0) and np.all((q[17] & 0x7F) == 0)
+    assert sc[5] == np.float32(1e-4) / np.float32(448)
+    # the largest magnitude of every nonzero row maps to the largest finite code
+    nz = np.ones(T, bool)
+    nz[[5, 17]] = False
+    assert np.all((q[nz] & 0x7F).max(axis=1) == 0x7E)
+
+
+def test_fused_strided_deterministic_batch_invariant():
+    inp = synth.make_inputs("rmsnorm_rope_fp8_4096x4096_bf16", rows=512)
+    n = 4096
+    xw = np.zeros((512, n + 64), dtype=np.uint16)
+    xw[:, :n] = inp["x"]
+    xt = dev(xw, "bf16")[:, :n]
+    wt, ct, st = dev(inp["w"], "bf16"), dev(inp["cos"], "bf16"), dev(inp["sin"], "bf16")
+    qbuf = torch.full((512, n + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    q1, s1 = qrw.rmsnorm_rope_fp8_fwd(xt, wt, ct, st, 32, 128, q=qbuf[:, :n])
+    q1, s1 = host(qbuf), host(s1)
+    assert np.all(q1[:, n:] == 0xAB)
+    wq, wsc = oracle.rmsnorm_rope_fp8(inp["x"], inp["w"], inp["cos"], inp["sin"], 32, 128, 128,
+                                      "bf16", "bf16", True, 1e-6)
+    assert_codes(q1[:, :n], wq)
+    assert_scales(s1, wsc)
+    q2, s2 = qrw.rmsnorm_rope_fp8_fwd(xt, wt, ct, st, 32, 128)
+    assert np.array_equal(host(q2), q1[:, :n]) and np.array_equal(host(s2), s1)
+    for r in (0, 123, 511):
+        qr, sr = qrw.rmsnorm_rope_fp8_fwd(xt[r:r + 1], wt, ct[r:r + 1], st[r:r + 1], 32, 128)
+        assert np.array_equal(host(qr)[0], q1[r, :n]) and host(sr)[0] == s1[r]
+    qe, se = qrw.rmsnorm_rope_fp8_fwd(xt[:0], wt, ct[:0], st[:0], 32, 128)
+    assert qe.shape == (0, n) and se.shape == (0,)
