@@ -18,8 +18,8 @@ read once, every output written once): 51,404,800 B for this workload.
 
 `traffic` reports HBM bytes per launch measured with rocprofv3 counters
 (FETCH_SIZE, WRITE_SIZE, scaled by the same counters on a plain copy of known
-size) as stored in profiles/traffic.json, and only while the kernel sources
-are the ones those counters were taken on; otherwise null.
+size) as recorded in profiles/<workload>_traffic.txt, and only while the
+kernel sources are the ones those counters were taken on; otherwise null.
 
 `cpu_baseline` times the CPU checker (single-threaded C, float64) on a bounded
 sample of the same workload on this host.
@@ -57,14 +57,23 @@ def kernel_source_hash() -> str:
 
 
 def stored_traffic(workload: str, src_hash: str):
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed counter summary of this workload, if
+    it was taken on the current kernel sources (``key: value`` lines at its end)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as fh:
-        rec = json.load(fh).get(workload)
-    if not rec or rec.get("kernel_src_hash") != src_hash:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("workload") != workload or rec.get("kernel_src_hash") != src_hash:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_model() -> str:
@@ -252,6 +261,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run 5 plain device copies of MIB MiB (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,6 +286,15 @@ def main() -> int:
     ms = time_gpu(wl, args.steps, args.warmup, args.mode)
     gbs = wl.counted / (ms * 1e-3) / 1e9
     print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        nb = args.calibrate_copy << 20
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda").random_(0, 255)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: 5 copies of {nb} B", file=sys.stderr, flush=True)
 
     src_hash = kernel_source_hash()
     traffic = stored_traffic(args.workload, src_hash)

@@ -32,6 +32,16 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+// Streaming forms (non-temporal hint): data touched once per launch.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 // ------------------------------------------------------- element formats
 struct F16 {
@@ -97,6 +107,29 @@ struct Table8<float> {
     }
   }
 };
+// Four table entries starting at element 4*j of a table row.
+template <typename CS>
+struct Table4;
+template <>
+struct Table4<float> {
+  static __device__ __forceinline__ void load(const void* row, int j, float (&v)[4]) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(row)[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = a[k];
+  }
+};
+template <typename T>
+struct Table4 {
+  static __device__ __forceinline__ void load(const void* row, int j, float (&v)[4]) {
+    const u32x2 a = reinterpret_cast<const u32x2*>(row)[j];
+    const uint32_t a0 = a[0], a1 = a[1];
+    v[0] = T::lo(a0);
+    v[1] = T::hi(a0);
+    v[2] = T::lo(a1);
+    v[3] = T::hi(a1);
+  }
+};
+
 template <>
 struct Table8<F16> {
   static __device__ __forceinline__ void load(const void* row, int s, float (&v)[8]) {
@@ -124,6 +157,21 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
+
+// Value of lane (l ^ X) for lane l, for the partner distances of the NeoX
+// pairing in the contiguous layout: DPP quad permutes for 1 and 2, a DPP
+// rotate by 8 inside each 16-lane row for 8 (which is xor 8 there), and the
+// LDS crossbar (ds_swizzle, bit mode) for 4 and 16.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8 || X == 16, "unsupported distance");
+  if constexpr (X == 1) return dpp<kDppXor1>(v);
+  else if constexpr (X == 2) return dpp<kDppXor2>(v);
+  else if constexpr (X == 8) return dpp<0x128>(v);  // row_ror:8
+  else
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (X << 10)));
+}
 
 // Sum over the 64 lanes; every lane receives the same value.  All lanes must
 // be active.

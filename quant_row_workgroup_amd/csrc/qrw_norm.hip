@@ -10,6 +10,10 @@
 // partial sums (one per element slot of a granule, a shallow serial chain),
 // a fixed pairwise tree, then the wave64 DPP reduction.
 //
+// Cache hints (measured on MI355X at 4096 x 4096): the rows are touched once
+// per launch, so outputs are written with non-temporal stores; LayerNorm also
+// reads x non-temporally, RMSNorm reads it normally (faster there).
+//
 // Arithmetic (binary32, one final rounding):
 //   RMSNorm   y = (x * w) * rstd      x*w is exact in binary32 for 16-bit x, w
 //   LayerNorm y = fma(((x - mu0) - r) * rstd, gamma, beta), mu = mu0 + r
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
       }
-      st16(yr + 8 * gi, narrow8<T>(v));
+      st16_stream(yr + 8 * gi, narrow8<T>(v));
     }
   }
 }
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (FULL || gi < ng) raw[g] = ld16(xr + 8 * gi);
+    if (FULL || gi < ng) raw[g] = ld16_stream(xr + 8 * gi);
   }
 
   // Mean in two parts: mu0 is the binary32 mean; the mean r of the residuals
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = fmaf(((v[k] - mu0) - r) * rstd, gv[k], bv[k]);
-      st16(yr + 8 * gi, narrow8<T>(v));
+      st16_stream(yr + 8 * gi, narrow8<T>(v));
     }
   }
 }

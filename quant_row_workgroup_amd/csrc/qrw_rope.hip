@@ -15,6 +15,10 @@
 // computes, then stores.  When rope_dim/16 divides 64, each lane only ever
 // needs one 8-entry granule of the token's cos/sin row, loaded once.
 //
+// Cache hints (measured on MI355X at the benchmark sizes): x is read with
+// non-temporal loads everywhere; RoPE also writes y non-temporally, while the
+// fused kernel's FP8 codes are stored normally (faster there).
+//
 // Fused arithmetic (binary32).  Because RoPE is linear and rstd is a per-row
 // scalar, the kernel evaluates z = RoPE(x * w) * rstd: u = x * w is exact in
 // binary32 for 16-bit operands, the rotation rounds once per output (fma),
@@ -95,8 +99,8 @@ __global__ __launch_bounds__(kBlock) void rope_kernel(const uint16_t* x, const v
       if (kind[i] == kItemPlain && !copy_plain) kind[i] = kItemNone;
       ra[i] = (u32x4){0u, 0u, 0u, 0u};
       rb[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (kind[i] != kItemNone) ra[i] = ld16(xr + oa[i]);
-      if (kind[i] != kItemNone && ob[i] >= 0) rb[i] = ld16(xr + ob[i]);
+      if (kind[i] != kItemNone) ra[i] = ld16_stream(xr + oa[i]);
+      if (kind[i] != kItemNone && ob[i] >= 0) rb[i] = ld16_stream(xr + ob[i]);
     }
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -115,11 +119,11 @@ __global__ __launch_bounds__(kBlock) void rope_kernel(const uint16_t* x, const v
         widen8<T>(ra[i], a);
         widen8<T>(rb[i], b);
         rotate<NEOX>(a, b, c, s);
-        st16(yr + oa[i], narrow8<T>(a));
-        st16(yr + ob[i], narrow8<T>(b));
+        st16_stream(yr + oa[i], narrow8<T>(a));
+        st16_stream(yr + ob[i], narrow8<T>(b));
       } else if (kind[i] == kItemPlain) {
-        st16(yr + oa[i], ra[i]);
-        if (ob[i] >= 0) st16(yr + ob[i], rb[i]);
+        st16_stream(yr + oa[i], ra[i]);
+        if (ob[i] >= 0) st16_stream(yr + ob[i], rb[i]);
       }
     }
   }
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
     kind[i] = item_offsets(pl, lane + kWave * i, NEOX, oa[i], ob[i], si[i]);
     ra[i] = (u32x4){0u, 0u, 0u, 0u};
     rb[i] = (u32x4){0u, 0u, 0u, 0u};
-    if (kind[i] != kItemNone) ra[i] = ld16(xr + oa[i]);
-    if (kind[i] != kItemNone && ob[i] >= 0) rb[i] = ld16(xr + ob[i]);
+    if (kind[i] != kItemNone) ra[i] = ld16_stream(xr + oa[i]);
+    if (kind[i] != kItemNone && ob[i] >= 0) rb[i] = ld16_stream(xr + ob[i]);
   }
   float hc[8], hs[8];
   if (pl.lane_hoist) {
@@ -236,44 +240,126 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
 }
 
 
-// ------------------------------------------------------------------ fused, dense
-// The same operator when every lane owns exactly K rope items and a single
-// table granule: no pass-through channels, rope_dim/16 a power of two that
-// divides 64, and heads * rope_dim/16 == 64 * K (e.g. 32 heads x 128 with
-// K = 4).  Offsets are closed-form, nothing is predicated, and the sum of
-// squares runs on the packed pairs with v_dot2c.
-template <typename T, typename CS, bool NEOX, int K, bool HAS_W>
-__global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_dense_kernel(
+// ------------------------------------------------------------------ fused, contiguous
+// The operator when every head rotates whole (rope_dim == head_dim), a head is
+// 2*XD granules with XD = head_dim/16 in {1, 2, 4, 8, 16}, and the row is G
+// whole wave blocks (n == 512 * G).  Lane l takes granules l, l+64, ..., so
+// every load and store instruction of the wave covers one contiguous block
+// (1 KiB of x, 512 B of codes).  A head then occupies 2*XD consecutive lanes:
+// in the NeoX pairing the partner of lane l is lane l ^ XD, read with a lane
+// exchange (lane_xor); in the interleaved pairing both members of a pair sit
+// in the same granule.  Each lane needs a single table granule per token.
+// The arithmetic is that of rotate(): first of a pair x_a c - x_b s as
+// fma(x_a, c, x_b * (-s)), second x_b c + x_a s as fma(x_b, c, x_a * s).
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD>
+__global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_contig_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
-    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int head_dim,
-    int half, int lg_gph, float n_f, float eps) {
+    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, float n_f,
+    float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (t >= tokens) return;
   const uint16_t* xr = x + t * xs;
   uint8_t* qr = q + t * qs;
-  const int s = lane & ((1 << lg_gph) - 1);
-  const int bo = NEOX ? half : 8;  // B granule offset from A
+  const int j = lane & (2 * XD - 1);  // granule index inside the head
 
-  int oa[K];
-  u32x4 ra[K], rb[K], wa[K], wb[K];
+  u32x4 r[G], wr[G];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    oa[i] = ((lane + kWave * i) >> lg_gph) * head_dim + (NEOX ? 8 * s : 16 * s);
-    ra[i] = ld16(xr + oa[i]);
-    rb[i] = ld16(xr + oa[i] + bo);
-  }
+  for (int g = 0; g < G; ++g) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
   if (HAS_W) {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      wa[i] = ld16(w + oa[i]);
-      wb[i] = ld16(w + oa[i] + bo);
-    }
+    for (int g = 0; g < G; ++g) wr[g] = ld16(w + 8 * (kWave * g + lane));
   }
   float c[8], sn[8];
-  Table8<CS>::load(table_row<CS>(cosv, t, half), s, c);
-  Table8<CS>::load(table_row<CS>(sinv, t, half), s, sn);
+  const char* crow = table_row<CS>(cosv, t, half);
+  const char* srow = table_row<CS>(sinv, t, half);
+  if (NEOX) {
+    Table8<CS>::load(crow, j & (XD - 1), c);
+    Table8<CS>::load(srow, j & (XD - 1), sn);
+    if (j < XD) {  // first half of the head: y = x c - x_partner s
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sn[e] = -sn[e];
+    }
+  } else {
+    float c4[4], s4[4];
+    Table4<CS>::load(crow, j, c4);
+    Table4<CS>::load(srow, j, s4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[k] = c4[k];
+      sn[k] = s4[k];
+    }
+  }
 
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[(2 * g + k) & 7] = sumsq2(T{}, r[g][k], acc[(2 * g + k) & 7]);
+  }
+  const float ss = wave_sum(tree8(acc));
+  const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+
+  float v[G][8];
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    widen8<T>(r[g], v[g]);
+    if (HAS_W) {
+      float f[8];
+      widen8<T>(wr[g], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[g][e] *= f[e];
+    }
+    if (NEOX) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[g][e] = fmaf(v[g][e], c[e], lane_xor<XD>(v[g][e]) * sn[e]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = v[g][2 * k], x1 = v[g][2 * k + 1];
+        v[g][2 * k] = fmaf(x0, c[k], -(x1 * sn[k]));
+        v[g][2 * k + 1] = fmaf(x1, c[k], x0 * sn[k]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      m[(e >> 1) & 3] = fmaxf(m[(e >> 1) & 3], fmaxf(fabsf(v[g][e]), fabsf(v[g][e + 1])));
+  }
+  const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  const float amax_z = wave_max(amax) * rstd;
+  const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
+  const float kq = rstd / scale;
+  if (lane == 0) scales[t] = scale;
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = v[g][e] * kq;
+    st8(qr + 8 * (kWave * g + lane), fp8x8(a));
+  }
+}
+
+// ------------------------------------------------------------------ fused, dense
+// The same operator when every lane owns exactly K rope items and a single
+// table granule: no pass-through channels, rope_dim/16 a power of two that
+// divides 64, and heads * rope_dim/16 == 64 * K (e.g. 32 heads x 128 with
+// K = 4).  Offsets are closed-form and nothing is predicated; the sum of
+// squares runs on the packed pairs with v_dot2c.
+//
+// Each wave handles RPW tokens, t = wave, wave + W, ... (W waves in the
+// grid), software-pipelined: the loads of token k+1 are issued as soon as
+// token k's data is in registers, before token k is computed and stored, so
+// reads of later tokens overlap the arithmetic and the stores of earlier ones
+// instead of every wave waiting for the last of all reads.  The weight
+// granules are loaded once per wave and reused for all of its tokens.
+template <typename T, typename CS, bool NEOX, int K, bool HAS_W>
+__device__ __forceinline__ void dense_token(const u32x4 (&ra)[K], const u32x4 (&rb)[K],
+                                            const u32x4 (&wa)[K], const u32x4 (&wb)[K],
+                                            const float (&c)[8], const float (&sn)[8],
+                                            const int (&oa)[K], int bo, uint8_t* qr,
+                                            float* scale_out, int lane, float n_f, float eps) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < K; ++i) {
@@ -287,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_dense_kernel(
   const float rstd = 1.0f / sqrtf(ss / n_f + eps);
 
   float va[K][8], vb[K][8];
-  float amax = 0.0f;
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     widen8<T>(ra[i], va[i]);
@@ -304,13 +390,14 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_dense_kernel(
     }
     rotate<NEOX>(va[i], vb[i], c, sn);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(va[i][e]), fabsf(vb[i][e])));
+    for (int e = 0; e < 8; ++e)
+      m[e & 3] = fmaxf(m[e & 3], fmaxf(fabsf(va[i][e]), fabsf(vb[i][e])));
   }
-
+  const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   const float amax_z = wave_max(amax) * rstd;
   const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
   const float kq = rstd / scale;
-  if (lane == 0) scales[t] = scale;
+  if (lane == 0) *scale_out = scale;
 
 #pragma unroll
   for (int i = 0; i < K; ++i) {
@@ -327,6 +414,84 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_dense_kernel(
     } else {
       st16(qr + oa[i], (u32x4){ca[0], ca[1], cb[0], cb[1]});
     }
+  }
+}
+
+template <typename T, typename CS, bool NEOX, int K, bool HAS_W, int RPW>
+__global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_dense_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
+    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int head_dim,
+    int half, int lg_gph, float n_f, float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kRowsPerBlock;
+  if (wave >= tokens) return;  // wave-uniform; later tokens of this wave are further out
+  const int s = lane & ((1 << lg_gph) - 1);
+  const int bo = NEOX ? half : 8;  // B granule offset from A
+
+  int oa[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    oa[i] = ((lane + kWave * i) >> lg_gph) * head_dim + (NEOX ? 8 * s : 16 * s);
+
+  u32x4 wa[K], wb[K];
+  if (HAS_W) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      wa[i] = ld16(w + oa[i]);
+      wb[i] = ld16(w + oa[i] + bo);
+    }
+  }
+
+  // token `wave`: loads
+  int64_t t = wave;
+  u32x4 ra[K], rb[K];
+  {
+    const uint16_t* xr = x + t * xs;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      ra[i] = ld16_stream(xr + oa[i]);
+      rb[i] = ld16_stream(xr + oa[i] + bo);
+    }
+  }
+  float c[8], sn[8];
+  Table8<CS>::load(table_row<CS>(cosv, t, half), s, c);
+  Table8<CS>::load(table_row<CS>(sinv, t, half), s, sn);
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t tn = t + nwaves;
+    const bool more = (r + 1 < RPW) && tn < tokens;  // wave-uniform
+    u32x4 na[K], nb[K];
+    float nc[8], ns[8];
+    if (r + 1 < RPW) {
+      // Issue the next token's loads before this token's arithmetic.  They are
+      // unconditional (a past-the-end token reloads the last one) so that the
+      // wait for this token's data does not also wait for them.
+      const int64_t tl = more ? tn : tokens - 1;
+      const uint16_t* xn = x + tl * xs;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        na[i] = ld16_stream(xn + oa[i]);
+        nb[i] = ld16_stream(xn + oa[i] + bo);
+      }
+      Table8<CS>::load(table_row<CS>(cosv, tl, half), s, nc);
+      Table8<CS>::load(table_row<CS>(sinv, tl, half), s, ns);
+    }
+    dense_token<T, CS, NEOX, K, HAS_W>(ra, rb, wa, wb, c, sn, oa, bo, q + t * qs, scales + t,
+                                       lane, n_f, eps);
+    if (!more) break;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      ra[i] = na[i];
+      rb[i] = nb[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      c[e] = nc[e];
+      sn[e] = ns[e];
+    }
+    t = tn;
   }
 }
 
@@ -355,17 +520,29 @@ void rope_go2(bool neox, int kk, dim3 grid, hipStream_t st, const uint16_t* x, c
   else rope_go<T, CS, false>(kk, grid, st, x, c, s, y, tokens, xs, ys, pl, copy);
 }
 
+// Tokens per wave of the dense kernel (fixed at build time; 1 = no pipelining).
+#ifndef QRW_DENSE_RPW
+#define QRW_DENSE_RPW 1
+#endif
+#ifndef QRW_DENSE_LDS
+#define QRW_DENSE_LDS 0
+#endif
+
 template <typename T, typename CS, bool NEOX, int K>
 void dense_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
               const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
               const RowPlan& pl, float n_f, float eps) {
+  constexpr int kRpw = QRW_DENSE_RPW;
   int lg = 0;
   while ((1 << lg) < pl.gph) ++lg;
+  const dim3 g((unsigned)((tokens + (int64_t)kRowsPerBlock * kRpw - 1) /
+                          ((int64_t)kRowsPerBlock * kRpw)));
+  (void)grid;
   if (w)
-    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, true><<<grid, kBlock, 0, st>>>(
+    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, true, kRpw><<<g, kBlock, QRW_DENSE_LDS, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.head_dim, pl.half, lg, n_f, eps);
   else
-    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, false><<<grid, kBlock, 0, st>>>(
+    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, false, kRpw><<<g, kBlock, QRW_DENSE_LDS, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.head_dim, pl.half, lg, n_f, eps);
 }
 
@@ -376,10 +553,53 @@ bool dense_ok(const RowPlan& pl, int kk) {
   return pl.n_plain == 0 && pl.lane_hoist && pow2 && pl.n_rope == kWave * kk;
 }
 
+template <typename T, typename CS, bool NEOX, int G, int XD>
+void contig_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
+               const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
+               const RowPlan& pl, float n_f, float eps) {
+  if (w)
+    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD><<<grid, kBlock, 0, st>>>(
+        x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+  else
+    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD><<<grid, kBlock, 0, st>>>(
+        x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+}
+
+template <typename T, typename CS, bool NEOX, int G>
+void contig_go_xd(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
+                  const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
+                  const RowPlan& pl, float n_f, float eps) {
+  switch (pl.head_dim / 16) {
+    case 1: contig_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 2: contig_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 4: contig_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 8: contig_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    default: contig_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+  }
+}
+
+// Granules per lane of the contiguous path, or 0 if it does not apply: whole
+// heads rotate, head_dim / 16 is 1, 2, 4, 8 or 16, and the row is 1, 2, 4 or
+// 8 blocks of 512 channels.
+int contig_blocks(const RowPlan& pl) {
+  const int xd = pl.head_dim / 16;
+  const bool xd_ok = pl.head_dim % 16 == 0 && (xd == 1 || xd == 2 || xd == 4 || xd == 8 || xd == 16);
+  if (pl.pass != 0 || !xd_ok || pl.n % 512 != 0) return 0;
+  const int g = pl.n / 512;
+  return (g == 1 || g == 2 || g == 4 || g == 8) ? g : 0;
+}
+
 template <typename T, typename CS, bool NEOX>
 void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w,
               const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
               int64_t qs, const RowPlan& pl, float n_f, float eps) {
+  switch (contig_blocks(pl)) {
+    case 1: contig_go_xd<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
+    case 2: contig_go_xd<T, CS, NEOX, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
+    case 4: contig_go_xd<T, CS, NEOX, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
+    case 8: contig_go_xd<T, CS, NEOX, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
+    default: break;
+  }
   if (dense_ok(pl, kk)) {
     switch (kk) {
       case 1: dense_go<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
