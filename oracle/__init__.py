@@ -12,8 +12,8 @@ are used (a row may be wider than ``n``, which models a row stride).
 The definitions followed are those of the page "TileLang tutorial, ch. 13:
 elementwise, normalisation and RoPE operators": RMSNorm and LayerNorm from
 its reference implementations (s3.2.1), the two RoPE pairings (s3.3.1,
-s3.3.2), the per-token FP8 cast (s3.1.5) and the fused norm/rotate/quantise
-operator (s3.3.4).  The C source states each step.
+s3.3.2), the per-token / per-group FP8 cast (s3.1.5) and the fused
+norm/rotate/quantise operator (s3.3.4).  The C source states each step.
 """
 from __future__ import annotations
 
@@ -72,6 +72,8 @@ def _load():
     L.oracle_rmsnorm_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                           i64, i64, i32, i32, i32, f32, vp]
     L.oracle_rmsnorm_rope_fp8.restype = None
+    L.oracle_act_quant_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32]
+    L.oracle_act_quant_fp8.restype = None
     _lib = L
     return L
 
@@ -185,3 +187,20 @@ def rmsnorm_rope_fp8(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int, d
                               tokens, heads, head_dim, rope_dim, xs, qs, DTYPE_CODE[dtype],
                               DTYPE_CODE[cs_dtype], int(bool(neox)), eps, _ptr(z))
     return (q, scales, z) if want_z else (q, scales)
+
+
+def act_quant_fp8(x, dtype: str, group: int | None = None, n: int | None = None,
+                  q_stride: int | None = None, fill: int = 0):
+    """E4M3FN codes and scales of x[:, :n] with one scale per ``group`` channels
+    (None: one per row).  Returns (codes [rows, q_stride], scales [rows, n/group])."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    rows, xs = x.shape
+    n = xs if n is None else n
+    g = n if group is None else group
+    assert n % g == 0
+    qs = n if q_stride is None else q_stride
+    q = np.full((rows, qs), fill, dtype=np.uint8)
+    scales = np.zeros((rows, n // g), dtype=np.float32)
+    L.oracle_act_quant_fp8(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, DTYPE_CODE[dtype])
+    return q, scales

@@ -372,3 +372,34 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
     }
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* Activation quantisation to E4M3FN, per token or per group            */
+/* ([EW] s3.1.5: amax per group -> scale = max(amax, 1e-4) / fp8_max -> */
+/* q = clamp(x / scale, -fp8_max, fp8_max) -> fp8).  `group` consecutive */
+/* channels share a scale (group == n: one scale per row).  scales is    */
+/* [rows, n / group], packed.                                            */
+/* ------------------------------------------------------------------ */
+void oracle_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
+                          int64_t group, int64_t x_stride, int64_t q_stride, int dtype) {
+  const double fp8_max = 448.0;
+  const double floor_amax = (double)1e-4f;
+  const int64_t groups = n / group;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < groups; ++k) {
+      double amax = 0.0;
+      for (int64_t j = k * group; j < (k + 1) * group; ++j) {
+        double v = fabs(load_el(x, r * x_stride + j, dtype));
+        if (v > amax) amax = v;
+      }
+      float scale = (float)(fmax(amax, floor_amax) / fp8_max);
+      scales[r * groups + k] = scale;
+      for (int64_t j = k * group; j < (k + 1) * group; ++j) {
+        double v = load_el(x, r * x_stride + j, dtype) / (double)scale;
+        if (v > fp8_max) v = fp8_max;
+        if (v < -fp8_max) v = -fp8_max;
+        q[r * q_stride + j] = oracle_encode_e4m3(v);
+      }
+    }
+  }
+}

@@ -204,3 +204,18 @@ def fused_ref(xrow, wrow, crow, srow, heads, head_dim, rope_dim, fmt, cs_fmt, ne
         q = min(max(q, Decimal(-448)), Decimal(448))
         codes.append(round_to(q, "e4m3"))
     return codes, scale, z
+
+
+def act_quant_ref(xrow, fmt, group):
+    """Exact per-group E4M3 quantisation of one row; returns (codes, scales)."""
+    xs = [dec(b, fmt) for b in xrow]
+    floor = Decimal(float(np.float32(1e-4)))
+    codes, scales = [], []
+    for k in range(0, len(xs), group):
+        grp = xs[k:k + group]
+        scale = round_f32(max(max(abs(v) for v in grp), floor) / 448)
+        scales.append(scale)
+        S = Decimal(scale)
+        for v in grp:
+            codes.append(round_to(min(max(v / S, Decimal(-448)), Decimal(448)), "e4m3"))
+    return codes, scales
