@@ -22,7 +22,10 @@
  * Readings of points the pages leave open (each is listed in the design doc):
  *  - FP8 is OCP E4M3FN (bias 7, max finite 448 = 0x7E, S.1111.111 is NaN, no
  *    infinities); the quantisation divides by the scale and clamps to +-448
- *    before encoding, as the per-token cast in [EW] s3.1.5 does.
+ *    before encoding, as the per-token cast in [EW] s3.1.5 does.  That cast
+ *    divides in float32 fragments, so the code is decided on the binary32
+ *    quotient: (float)(v / (double)scale) is the correctly rounded binary32
+ *    quotient (a double quotient of two binary32 values rounds innocuously).
  *  - The per-token scale is max(amax, floor)/448 with the floor 1e-4 taken as
  *    the binary32 constant the kernels hold; the scale is stored as binary32.
  *  - The fused operator does not round between the norm and the rotation.
@@ -284,7 +287,7 @@ void oracle_rope(const void* x, const void* cosv, const void* sinv, void* y,
 /* per-token cast of s3.1.5)                                               */
 /*   z = RoPE(x * rstd * w)          (double, no intermediate rounding)    */
 /*   amax = max_j |z_j|;  scale = binary32(max(amax, 1e-4f) / 448)         */
-/*   q_j = E4M3FN(clamp(z_j / scale, -448, 448))                           */
+/*   q_j = E4M3FN(clamp(binary32(z_j / scale), -448, 448))                 */
 /* The row is the whole token: n = heads * head_dim; the norm and amax     */
 /* run over all of it; the rotation acts on each head's tail span.         */
 /* `z_out` (nullable) receives z as double, for the tests' composition pin. */
@@ -346,7 +349,7 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
       for (int64_t j = 0; j < start; ++j) {
         double wj = w ? load_el(w, h * head_dim + j, dtype) : 1.0;
         double z = load_el(x, xb + j, dtype) * rstd * wj;
-        double v = z / (double)scale;
+        double v = (double)(float)(z / (double)scale);
         if (v > fp8_max) v = fp8_max;
         if (v < -fp8_max) v = -fp8_max;
         q[qb + j] = oracle_encode_e4m3(v);
@@ -363,7 +366,7 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
         double zz[2] = {na * c - nb * s, na * s + nb * c};
         int64_t idx[2] = {a, b};
         for (int k = 0; k < 2; ++k) {
-          double v = zz[k] / (double)scale;
+          double v = (double)(float)(zz[k] / (double)scale);
           if (v > fp8_max) v = fp8_max;
           if (v < -fp8_max) v = -fp8_max;
           q[qb + start + idx[k]] = oracle_encode_e4m3(v);
@@ -395,7 +398,7 @@ void oracle_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows
       float scale = (float)(fmax(amax, floor_amax) / fp8_max);
       scales[r * groups + k] = scale;
       for (int64_t j = k * group; j < (k + 1) * group; ++j) {
-        double v = load_el(x, r * x_stride + j, dtype) / (double)scale;
+        double v = (double)(float)(load_el(x, r * x_stride + j, dtype) / (double)scale);
         if (v > fp8_max) v = fp8_max;
         if (v < -fp8_max) v = -fp8_max;
         q[r * q_stride + j] = oracle_encode_e4m3(v);

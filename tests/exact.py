@@ -200,7 +200,7 @@ def fused_ref(xrow, wrow, crow, srow, heads, head_dim, rope_dim, fmt, cs_fmt, ne
     S = Decimal(scale)
     codes = []
     for v in z:
-        q = v / S
+        q = Decimal(round_f32(v / S))  # the code is decided on the binary32 quotient
         q = min(max(q, Decimal(-448)), Decimal(448))
         codes.append(round_to(q, "e4m3"))
     return codes, scale, z
@@ -217,5 +217,6 @@ def act_quant_ref(xrow, fmt, group):
         scales.append(scale)
         S = Decimal(scale)
         for v in grp:
-            codes.append(round_to(min(max(v / S, Decimal(-448)), Decimal(448)), "e4m3"))
+            q = Decimal(round_f32(v / S))  # the code is decided on the binary32 quotient
+            codes.append(round_to(min(max(q, Decimal(-448)), Decimal(448)), "e4m3"))
     return codes, scales
