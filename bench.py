@@ -46,12 +46,22 @@ METRIC = "achieved HBM GB/s (% of MI355X peak), fused RMSNorm+RoPE+FP8 4096x4096
 DEFAULT_WORKLOAD = "rmsnorm_rope_fp8_4096x4096_bf16"
 
 
-def kernel_source_hash() -> str:
+# Source files that define each operator's kernels and their launch.
+KERNEL_SOURCES = {
+    "rmsnorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
+    "layernorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
+    "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
+    "fused": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
+    "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
+}
+
+
+def kernel_source_hash(op: str = "fused") -> str:
+    """sha256 (first 16 hex digits) of the sources of one operator's kernels."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "quant_row_workgroup_amd", "csrc", "*")))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in KERNEL_SOURCES[op]:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "quant_row_workgroup_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -119,7 +129,12 @@ class Workload:
         self.sets = []
         for _ in range(sets):
             s = {k: v.clone() for k, v in base.items()}
-            if op == "fused":
+            if op == "act_quant":
+                R, n = self.cfg["rows"], self.cfg["n"]
+                g = self.cfg.get("group") or n
+                s["q"] = torch.empty((R, n), dtype=torch.uint8, device=dev)
+                s["scales"] = torch.empty((R, n // g), dtype=torch.float32, device=dev)
+            elif op == "fused":
                 T = self.cfg["tokens"]
                 n = self.cfg["heads"] * self.cfg["head_dim"]
                 s["q"] = torch.empty((T, n), dtype=torch.uint8, device=dev)
@@ -143,6 +158,10 @@ class Workload:
                                                H * D, self.code[c["dtype"]],
                                                self.code[c["cs_dtype"]], int(c["neox"]),
                                                c["eps"], st)
+        elif self.op == "act_quant":
+            g = c.get("group") or c["n"]
+            rc = self.lib.act_quant_fp8_fwd(p(s["x"]), p(s["q"]), p(s["scales"]), c["rows"],
+                                            c["n"], g, c["n"], c["n"], self.code[c["dtype"]], st)
         elif self.op == "rmsnorm":
             rc = self.lib.rmsnorm_fwd(p(s["x"]), p(s["w"]), p(s["y"]), c["rows"], c["n"], c["n"],
                                       c["n"], self.code[c["dtype"]], c["eps"], st)
@@ -222,6 +241,8 @@ def cpu_baseline(name: str, seconds: float):
             oracle.rmsnorm_rope_fp8(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg["heads"],
                                     cfg["head_dim"], cfg["rope_dim"], cfg["dtype"],
                                     cfg["cs_dtype"], cfg["neox"], cfg["eps"])
+        elif op == "act_quant":
+            oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
         elif op == "rmsnorm":
             oracle.rmsnorm(inp["x"], inp["w"], cfg["dtype"], cfg["eps"])
         elif op == "layernorm":
@@ -296,7 +317,7 @@ def main() -> int:
         torch.cuda.synchronize()
         print(f"[bench] calibration: 5 copies of {nb} B", file=sys.stderr, flush=True)
 
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(wl.cfg["op"])
     traffic = stored_traffic(args.workload, src_hash)
     cpu = None
     if not args.no_cpu_baseline:

@@ -8,7 +8,7 @@
  *   s3.3.1  the two RoPE pairings, the (positions, rope_dim/2) cos/sin table,
  *           and partial rotation of the tail span of a head
  *   s3.3.2  reference RoPE (fp32 math, one final cast)
- *   s3.1.5  per-token FP8 cast (amax -> scale -> clamp -> cast)
+ *   s3.1.5  per-token / per-group FP8 cast (amax -> scale -> clamp -> cast)
  *   s3.3.4  the fused RMSNorm + RoPE + per-token quantisation operator
  *
  * Conventions shared by every entry point
@@ -131,6 +131,21 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
                          int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
                          int64_t q_token_stride, int dtype, int cs_dtype, int neox, float eps,
                          void* stream);
+
+/*
+ * Activation quantisation to OCP E4M3FN (s3.1.5), one scale per group of
+ * `group` consecutive channels of a row, or per row (group == n):
+ *   amax_{r,k}   = max |x[r,j]| over group k of row r
+ *   scales[r,k]  = max(amax_{r,k}, 1e-4) / 448                     (binary32)
+ *   q[r,j]       = E4M3FN( clamp(x[r,j] / scales[r,k], -448, 448) )
+ * x: [rows, n] with x_row_stride (elements); q: [rows, n] codes with
+ * q_row_stride (bytes, a multiple of 8); scales: [rows, n / group] float,
+ * packed, 4-byte aligned.  group is n, or one of 8, 16, 32, 64, 128, 256, 512
+ * dividing n.  Requires n <= QRW_MAX_ROW.  Dequantisation is q * scale.
+ */
+int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
+                      int64_t group, int64_t x_row_stride, int64_t q_row_stride, int dtype,
+                      void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* qrw_status_string(int status);

@@ -1,7 +1,8 @@
 """Fused memory-bound LLM row operators for AMD MI355X (gfx950).
 
-RMSNorm, LayerNorm, RoPE (interleaved and NeoX half-split) and the fused
-RMSNorm -> RoPE -> per-token FP8 (E4M3FN) quantisation, as hand-written HIP
+RMSNorm, LayerNorm, RoPE (interleaved and NeoX half-split), the fused
+RMSNorm -> RoPE -> per-token FP8 (E4M3FN) quantisation and per-token /
+per-group FP8 activation quantisation, as hand-written HIP
 kernels behind a C ABI (include/qrw.h, libqrw.so).  The Python functions here
 are a thin ctypes binding with the same names.
 """
@@ -9,6 +10,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     QrwError,
+    act_quant_fp8_fwd,
     layernorm_fwd,
     load,
     rmsnorm_fwd,

@@ -27,7 +27,7 @@ STATUS = {
 }
 
 EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
-           "rmsnorm_rope_fp8_fwd", "qrw_status_string")
+           "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qrw_status_string")
 
 
 class QrwError(RuntimeError):
@@ -56,6 +56,7 @@ def load():
     L.rope_apply_neox.argtypes = rope_args
     L.rmsnorm_rope_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                        i32, i32, i32, f32, vp]
+    L.act_quant_fp8_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = i32
     L.qrw_status_string.argtypes = [i32]
@@ -169,4 +170,22 @@ def rmsnorm_rope_fp8_fwd(x, weight, cos, sin, heads: int, head_dim: int,
                                      rd, xs, qs, _dtype(x), _dtype(cos), int(bool(neox)), eps,
                                      _stream(x))
     _check("rmsnorm_rope_fp8_fwd", st)
+    return q, scales
+
+
+def act_quant_fp8_fwd(x, group: int | None = None, q=None, scales=None):
+    """E4M3FN codes of 2-D ``x`` with one scale per ``group`` channels (None: per
+    row).  Returns (codes uint8 [rows, n], scales float32 [rows, n / group])."""
+    rows, n, xs = _rows(x, "x")
+    g = n if group is None else group
+    if q is None:
+        q = torch.empty((rows, n), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, max(n // g, 1)), dtype=torch.float32, device=x.device)
+    _, _, qs = _rows(q, "q")
+    if not scales.is_contiguous():
+        raise ValueError("scales must be packed")
+    st = load().act_quant_fp8_fwd(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, _dtype(x),
+                                  _stream(x))
+    _check("act_quant_fp8_fwd", st)
     return q, scales

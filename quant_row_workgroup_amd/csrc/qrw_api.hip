@@ -183,6 +183,29 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
                                              static_cast<hipStream_t>(stream)));
 }
 
+int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
+                      int64_t group, int64_t x_row_stride, int64_t q_row_stride, int dtype,
+                      void* stream) {
+  if (!is_16bit(dtype)) return QRW_ERR_DTYPE;
+  if (rows < 0 || n < 8 || n % 8 != 0 || n > QRW_MAX_ROW) return QRW_ERR_SHAPE;
+  if (rows > (int64_t)0x7FFFFFFF * 4) return QRW_ERR_SHAPE;
+  const bool pow2_group = group >= 8 && group <= 512 && (group & (group - 1)) == 0;
+  if (group != n && !(pow2_group && n % group == 0)) return QRW_ERR_SHAPE;
+  if (x_row_stride < n || x_row_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (q_row_stride < n || q_row_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (rows == 0) return QRW_OK;
+  if (!x || !q || !scales) return QRW_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return QRW_ERR_ALIGN;
+  const Span qspan = span_of(q, rows, n, q_row_stride, 1);
+  const uintptr_t s_lo = reinterpret_cast<uintptr_t>(scales);
+  const Span sspan = {s_lo, s_lo + (uintptr_t)(rows * (n / group) * 4)};
+  const Span xspan = span_of(x, rows, n, x_row_stride, 2);
+  if (overlap(qspan, sspan) || overlap(xspan, qspan) || overlap(xspan, sspan)) return QRW_ERR_ALIAS;
+  return finish(qrw::launch_act_quant_fp8(x, q, scales, rows, n, group, x_row_stride,
+                                          q_row_stride, dtype, static_cast<hipStream_t>(stream)));
+}
+
 const char* qrw_status_string(int status) {
   switch (status) {
     case QRW_OK: return "ok";

@@ -29,6 +29,10 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
                                    float eps, hipStream_t stream);
 
+hipError_t launch_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows,
+                                int64_t n, int64_t group, int64_t xs, int64_t qs, int dtype,
+                                hipStream_t stream);
+
 // Number of "items" (pairs of granules) one token of the fused operator holds.
 int64_t fused_items(int64_t heads, int64_t head_dim, int64_t rope_dim);
 

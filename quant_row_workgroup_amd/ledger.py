@@ -110,6 +110,14 @@ def rmsnorm_rope_fp8(tokens: int, n: int, rope_dim: int, elt: int = 2, cs_elt: i
     return k_norm + k_rope + k_quant, fused, flops
 
 
+def act_quant(rows: int, n: int, group: int, elt: int = 2):
+    """Per-group FP8 cast as one kernel: read x, write codes and one fp32 scale
+    per group.  FLOPs: |x|, max, scale multiply per element (3)."""
+    E = rows * n * elt
+    fused = _kernel([E], [rows * n, rows * (n // group) * 4])
+    return fused, fused, 3 * rows * n
+
+
 def page_scenarios():
     """The five scenarios of the ledger table, with the pages' shapes."""
     return {
@@ -136,6 +144,9 @@ def counted_bytes(cfg: dict) -> int:
         xy = 2 * T * n * e
         tab = 2 * T * (R // 2) * ELT[cfg["cs_dtype"]]
         return xy + tab
+    if op == "act_quant":
+        return act_quant(cfg["rows"], cfg["n"], cfg.get("group") or cfg["n"],
+                         ELT[cfg["dtype"]])[1]
     if op == "fused":
         n = cfg["heads"] * cfg["head_dim"]
         return rmsnorm_rope_fp8(cfg["tokens"], n, cfg["rope_dim"], ELT[cfg["dtype"]],

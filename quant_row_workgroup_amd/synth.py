@@ -83,6 +83,10 @@ WORKLOADS = {
                                      seed=3),
     "rope_4096x32x128_f16": dict(op="rope", tokens=4096, heads=32, head_dim=128, rope_dim=128,
                                  dtype="f16", cs_dtype="f32", seed=4),
+    "act_quant_4096x4096_bf16_g128": dict(op="act_quant", rows=4096, n=4096, group=128,
+                                          dtype="bf16", seed=6),
+    "act_quant_4096x4096_bf16_token": dict(op="act_quant", rows=4096, n=4096, group=None,
+                                           dtype="bf16", seed=7),
     "rmsnorm_rope_fp8_4096x4096_bf16": dict(op="fused", tokens=4096, heads=32, head_dim=128,
                                             rope_dim=128, dtype="bf16", cs_dtype="bf16",
                                             eps=1e-6, neox=True, seed=5),
@@ -113,6 +117,11 @@ def make_inputs(name: str, seed: int | None = None, rows: int | None = None) -> 
         x = normal(s, (T, n), 0.0, 1.0, cfg["dtype"])
         c, sn = rope_table(T, cfg["rope_dim"], cfg["cs_dtype"])
         return dict(cfg, tokens=T, x=x, cos=c, sin=sn)
+    if op == "act_quant":
+        R = cfg["rows"] if rows is None else rows
+        x = normal(s, (R, cfg["n"]), 0.0, 3.0, cfg["dtype"], outlier_frac=0.01,
+                   outlier_mul=10.0)
+        return dict(cfg, rows=R, x=x)
     if op == "fused":
         T = cfg["tokens"] if rows is None else rows
         n = cfg["heads"] * cfg["head_dim"]

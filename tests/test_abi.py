@@ -18,6 +18,17 @@ F16, BF16, F32 = 1, 2, 3
 
 # fake, 16-byte aligned, far-apart "device" addresses; never dereferenced
 X, Y, W, C, S, Q, SC = (ctypes.c_void_p(a << 32) for a in range(1, 8))
+Q_ADDR = 6 << 32
+
+
+@pytest.fixture(autouse=True)
+def _host_only():
+    # every case below is meant to fail validation (or be empty) before any HIP
+    # call; the fake addresses must never meet a visible device
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("argument-validation cases use fake device addresses: run without a GPU")
 
 
 def declared_functions():
@@ -126,10 +137,32 @@ def fused(**kw):
     (dict(xs=4000), STRIDE), (dict(qs=4100), STRIDE),
     (dict(q=ctypes.c_void_p((5 << 32) + 8)), ALIGN), (dict(sc=ctypes.c_void_p((6 << 32) + 2)), ALIGN),
     (dict(eps=float("-inf")), VALUE), (dict(neox=2), VALUE),
-    (dict(sc=ctypes.c_void_p((5 << 32) + 64)), ALIAS),   # scales inside the codes
+    (dict(sc=ctypes.c_void_p(Q_ADDR + 64)), ALIAS),      # scales inside the codes
     (dict(q=ctypes.c_void_p((1 << 32) + 4096)), ALIAS),  # codes inside x
     (dict(T=0), OK), (dict(T=0, x=None, q=None, sc=None, c=None, s=None), OK),
     (dict(T=0, R=24), SHAPE),
 ])
 def test_fused_validation(kw, want):
     assert fused(**kw) == want
+
+
+def aq(**kw):
+    a = dict(x=X, q=Q, sc=SC, rows=4, n=4096, group=128, xs=4096, qs=4096, dtype=BF16)
+    a.update(kw)
+    return qrw.load().act_quant_fp8_fwd(a["x"], a["q"], a["sc"], a["rows"], a["n"], a["group"],
+                                        a["xs"], a["qs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(q=None), NULL), (dict(sc=None), NULL),
+    (dict(dtype=F32), DTYPE),
+    (dict(group=96), SHAPE), (dict(group=1024), SHAPE), (dict(group=4), SHAPE),
+    (dict(n=1000, xs=1000, qs=1000, group=128), SHAPE), (dict(n=8200), SHAPE),
+    (dict(xs=4088), STRIDE), (dict(qs=4100), STRIDE),
+    (dict(q=ctypes.c_void_p((5 << 32) + 8)), ALIGN), (dict(sc=ctypes.c_void_p((6 << 32) + 2)), ALIGN),
+    (dict(sc=ctypes.c_void_p(Q_ADDR + 64)), ALIAS),      # scales inside the codes
+    (dict(q=ctypes.c_void_p((1 << 32) + 256)), ALIAS),   # codes inside x
+    (dict(rows=0), OK), (dict(rows=0, x=None, q=None, sc=None), OK),
+])
+def test_act_quant_validation(kw, want):
+    assert aq(**kw) == want
