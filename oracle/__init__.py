@@ -74,6 +74,9 @@ def _load():
     L.oracle_rmsnorm_rope_fp8.restype = None
     L.oracle_act_quant_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32]
     L.oracle_act_quant_fp8.restype = None
+    L.oracle_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                      i32, i32, i32, f32]
+    L.oracle_qk_norm_rope.restype = None
     _lib = L
     return L
 
@@ -204,3 +207,25 @@ def act_quant_fp8(x, dtype: str, group: int | None = None, n: int | None = None,
     scales = np.zeros((rows, n // g), dtype=np.float32)
     L.oracle_act_quant_fp8(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, DTYPE_CODE[dtype])
     return q, scales
+
+
+def qk_norm_rope(x, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: int, head_dim: int,
+                 rope_dim: int, dtype: str, cs_dtype: str, neox: bool, eps: float,
+                 y_stride: int | None = None, fill: int = 0):
+    """Per-head RMSNorm (weights of length head_dim) then RoPE on the q and k heads
+    of x [tokens, (q_heads + 2 kv_heads) * head_dim]; v heads are copied."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    q_weight = _check(q_weight, dtype, "q_weight")
+    k_weight = _check(k_weight, dtype, "k_weight")
+    cos = _check(cos, cs_dtype, "cos")
+    sin = _check(sin, cs_dtype, "sin")
+    tokens, xs = x.shape
+    n = (q_heads + 2 * kv_heads) * head_dim
+    assert cos.shape == (tokens, rope_dim // 2) and sin.shape == cos.shape
+    ys = n if y_stride is None else y_stride
+    y = np.full((tokens, ys), fill, dtype=_STORAGE[dtype])
+    L.oracle_qk_norm_rope(_ptr(x), _ptr(q_weight), _ptr(k_weight), _ptr(cos), _ptr(sin), _ptr(y),
+                          tokens, q_heads, kv_heads, head_dim, rope_dim, xs, ys,
+                          DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)), eps)
+    return y

@@ -406,3 +406,56 @@ void oracle_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows
     }
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* Per-head QK RMSNorm followed by RoPE, as one operator ([EW] s2.4:     */
+/* each q/k value gets a weighted RMSNorm and then RoPE; q/k columns are  */
+/* read and written back, v columns are not touched).                    */
+/* A token row holds q_heads query heads, then kv_heads key heads, then   */
+/* kv_heads value heads, each of head_dim channels.  For every q (k)      */
+/* head: r = 1/sqrt(mean over the head of x^2 + eps); z = RoPE(x * r * w) */
+/* with w = q_weight (k_weight) of length head_dim (nullable), RoPE on the */
+/* head's tail span; one rounding at the output.  v is copied.            */
+/* ------------------------------------------------------------------ */
+void oracle_qk_norm_rope(const void* x, const void* q_weight, const void* k_weight,
+                         const void* cosv, const void* sinv, void* y, int64_t tokens,
+                         int64_t q_heads, int64_t kv_heads, int64_t head_dim, int64_t rope_dim,
+                         int64_t x_stride, int64_t y_stride, int dtype, int cs_dtype, int neox,
+                         float eps) {
+  int64_t half = rope_dim / 2;
+  int64_t start = head_dim - rope_dim;
+  int64_t heads = q_heads + 2 * kv_heads;
+  for (int64_t t = 0; t < tokens; ++t) {
+    for (int64_t h = 0; h < heads; ++h) {
+      int64_t xb = t * x_stride + h * head_dim;
+      int64_t yb = t * y_stride + h * head_dim;
+      if (h >= q_heads + kv_heads) { /* value head: untouched */
+        for (int64_t j = 0; j < head_dim; ++j) copy_el(x, xb + j, y, yb + j, dtype);
+        continue;
+      }
+      const void* w = h < q_heads ? q_weight : k_weight;
+      double ss = 0.0;
+      for (int64_t j = 0; j < head_dim; ++j) {
+        double v = load_el(x, xb + j, dtype);
+        ss += v * v;
+      }
+      double rstd = 1.0 / sqrt(ss / (double)head_dim + (double)eps);
+      for (int64_t j = 0; j < start; ++j) {
+        double wj = w ? load_el(w, j, dtype) : 1.0;
+        store_el(y, yb + j, dtype, load_el(x, xb + j, dtype) * rstd * wj);
+      }
+      for (int64_t p = 0; p < half; ++p) {
+        int64_t a, b;
+        rope_pair_index(p, half, neox, &a, &b);
+        double wa = w ? load_el(w, start + a, dtype) : 1.0;
+        double wb = w ? load_el(w, start + b, dtype) : 1.0;
+        double na = load_el(x, xb + start + a, dtype) * rstd * wa;
+        double nb = load_el(x, xb + start + b, dtype) * rstd * wb;
+        double c = load_el(cosv, t * half + p, cs_dtype);
+        double s = load_el(sinv, t * half + p, cs_dtype);
+        store_el(y, yb + start + a, dtype, na * c - nb * s);
+        store_el(y, yb + start + b, dtype, na * s + nb * c);
+      }
+    }
+  }
+}

@@ -220,3 +220,23 @@ def act_quant_ref(xrow, fmt, group):
             q = Decimal(round_f32(v / S))  # the code is decided on the binary32 quotient
             codes.append(round_to(min(max(q, Decimal(-448)), Decimal(448)), "e4m3"))
     return codes, scales
+
+
+def qk_norm_rope_ref(xrow, qw, kw, crow, srow, q_heads, kv_heads, head_dim, rope_dim, fmt,
+                     cs_fmt, neox, eps32):
+    """Exact per-head RMSNorm + RoPE of one token row; returns output codes."""
+    cs = [dec(b, cs_fmt) for b in crow]
+    ss = [dec(b, cs_fmt) for b in srow]
+    out = [int(b) for b in xrow]
+    eps = Decimal(float(np.float32(eps32)))
+    for h in range(q_heads + kv_heads):
+        wrow = qw if h < q_heads else kw
+        base = h * head_dim
+        xs = [dec(b, fmt) for b in xrow[base:base + head_dim]]
+        ws = [dec(b, fmt) for b in wrow] if wrow is not None else [Decimal(1)] * head_dim
+        r = 1 / sqrt(sum(v * v for v in xs) / head_dim + eps)
+        normed = [a * r * b for a, b in zip(xs, ws)]
+        z = rope_values(normed, cs, ss, 1, head_dim, rope_dim, neox)
+        for j, v in enumerate(z):
+            out[base + j] = round_to(v, fmt)
+    return out
