@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
     "fused": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
+    "qk_norm_rope": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
 }
 
 
@@ -125,7 +126,8 @@ class Workload:
         dt = self.cfg["dtype"]
         code = {"f16": 1, "bf16": 2, "f32": 3}
         base = {k: up(v, self.cfg.get("cs_dtype", dt) if k in ("cos", "sin") else dt)
-                for k, v in self.inp.items() if k in ("x", "w", "gamma", "beta", "cos", "sin")}
+                for k, v in self.inp.items()
+                if k in ("x", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight")}
         self.sets = []
         for _ in range(sets):
             s = {k: v.clone() for k, v in base.items()}
@@ -139,12 +141,19 @@ class Workload:
                 n = self.cfg["heads"] * self.cfg["head_dim"]
                 s["q"] = torch.empty((T, n), dtype=torch.uint8, device=dev)
                 s["scales"] = torch.empty((T,), dtype=torch.float32, device=dev)
-            else:
+            elif op != "qk_norm_rope":  # qk_norm_rope works in place on x
                 s["y"] = torch.empty_like(s["x"])
             self.sets.append(s)
         self.op = op
         self.code = code
+        self.pristine = base["x"]
         torch.cuda.synchronize()
+
+    def reset(self) -> None:
+        """Restore the inputs an in-place operator overwrote."""
+        if self.op == "qk_norm_rope":
+            for s in self.sets:
+                s["x"].copy_(self.pristine)
 
     def launch(self, i: int, stream_ptr: int) -> None:
         s = self.sets[i % len(self.sets)]
@@ -158,6 +167,14 @@ class Workload:
                                                H * D, self.code[c["dtype"]],
                                                self.code[c["cs_dtype"]], int(c["neox"]),
                                                c["eps"], st)
+        elif self.op == "qk_norm_rope":
+            T, D = c["tokens"], c["head_dim"]
+            n = (c["q_heads"] + 2 * c["kv_heads"]) * D
+            rc = self.lib.qk_norm_rope_fwd(p(s["x"]), p(s["q_weight"]), p(s["k_weight"]),
+                                           p(s["cos"]), p(s["sin"]), T, c["q_heads"],
+                                           c["kv_heads"], D, c["rope_dim"], n,
+                                           self.code[c["dtype"]], self.code[c["cs_dtype"]],
+                                           int(c["neox"]), c["eps"], st)
         elif self.op == "act_quant":
             g = c.get("group") or c["n"]
             rc = self.lib.act_quant_fp8_fwd(p(s["x"]), p(s["q"]), p(s["scales"]), c["rows"],
@@ -179,7 +196,8 @@ class Workload:
 
     def outputs(self, i: int):
         s = self.sets[i % len(self.sets)]
-        return [s[k].clone() for k in ("q", "scales", "y") if k in s]
+        keys = ("x",) if self.op == "qk_norm_rope" else ("q", "scales", "y")
+        return [s[k].clone() for k in keys if k in s]
 
 
 def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
@@ -200,15 +218,20 @@ def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
             for i in range(steps):
                 wl.launch(i, sp)
         torch.cuda.synchronize()
-        g.replay()  # untimed replay: first-launch costs of the graph
+        # the graph's outputs match the same launches made eagerly, bit for bit
+        # (from the same starting inputs, since an in-place operator consumes them)
+        wl.reset()
         torch.cuda.synchronize()
-        # the graph's outputs match an eager launch bit for bit
+        g.replay()
+        torch.cuda.synchronize()
         ref = wl.outputs(steps - 1)
-        wl.launch(steps - 1, cur.cuda_stream)
+        wl.reset()
+        for i in range(steps):
+            wl.launch(i, cur.cuda_stream)
         torch.cuda.synchronize()
         for a, b in zip(ref, wl.outputs(steps - 1)):
             if not torch.equal(a, b):
-                raise RuntimeError("graph replay differs from eager launch")
+                raise RuntimeError("graph replay differs from eager launches")
         torch.cuda.synchronize()
         start.record()
         g.replay()
@@ -232,7 +255,7 @@ def cpu_baseline(name: str, seconds: float):
     inp = synth.make_inputs(name, rows=rows)
     cfg = dict(synth.WORKLOADS[name])
     op = cfg["op"]
-    key = "tokens" if op in ("rope", "fused") else "rows"
+    key = "tokens" if op in ("rope", "fused", "qk_norm_rope") else "rows"
     cfg[key] = rows
     bytes_per_call = ledger.counted_bytes(cfg)
 
@@ -243,6 +266,11 @@ def cpu_baseline(name: str, seconds: float):
                                     cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "act_quant":
             oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
+        elif op == "qk_norm_rope":
+            oracle.qk_norm_rope(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
+                                inp["sin"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                                cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], cfg["neox"],
+                                cfg["eps"])
         elif op == "rmsnorm":
             oracle.rmsnorm(inp["x"], inp["w"], cfg["dtype"], cfg["eps"])
         elif op == "layernorm":

@@ -10,6 +10,7 @@
  *   s3.3.2  reference RoPE (fp32 math, one final cast)
  *   s3.1.5  per-token / per-group FP8 cast (amax -> scale -> clamp -> cast)
  *   s3.3.4  the fused RMSNorm + RoPE + per-token quantisation operator
+ *   s2.4    cross-module fusion: per-head q/k RMSNorm + RoPE, v untouched
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -146,6 +147,23 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
 int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
                       int64_t group, int64_t x_row_stride, int64_t q_row_stride, int dtype,
                       void* stream);
+
+/*
+ * Per-head QK RMSNorm + RoPE, IN PLACE on a packed QKV activation (s2.4 with
+ * s3.2.1 and s3.3.1).  qkv: [tokens, (q_heads + 2*kv_heads) * head_dim] with
+ * token_stride (elements); a row holds q_heads query heads, then kv_heads key
+ * heads, then kv_heads value heads.  For every query (key) head of a token:
+ *   rstd = 1 / sqrt( (1/head_dim) sum_j x_j^2 + eps )     over that head
+ *   x   <- RoPE( x * rstd * w )   w = q_weight (k_weight) [head_dim], or NULL
+ * with RoPE on the head's tail span of rope_dim channels (neox: 1 = NeoX
+ * half-split, 0 = interleaved) using cos/sin [tokens, rope_dim/2] (cs_dtype).
+ * Value heads are neither read nor written.  Requires head_dim in
+ * {64, 128, 256} and rope_dim a power of two with 16 <= rope_dim <= head_dim.
+ */
+int qk_norm_rope_fwd(void* qkv, const void* q_weight, const void* k_weight, const void* cos,
+                     const void* sin, int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                     int64_t head_dim, int64_t rope_dim, int64_t token_stride, int dtype,
+                     int cs_dtype, int neox, float eps, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* qrw_status_string(int status);

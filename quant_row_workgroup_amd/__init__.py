@@ -2,7 +2,8 @@
 
 RMSNorm, LayerNorm, RoPE (interleaved and NeoX half-split), the fused
 RMSNorm -> RoPE -> per-token FP8 (E4M3FN) quantisation and per-token /
-per-group FP8 activation quantisation, as hand-written HIP
+per-group FP8 activation quantisation and per-head QK RMSNorm + RoPE, as
+hand-written HIP
 kernels behind a C ABI (include/qrw.h, libqrw.so).  The Python functions here
 are a thin ctypes binding with the same names.
 """
@@ -13,6 +14,7 @@ from ._binding import (  # noqa: F401
     act_quant_fp8_fwd,
     layernorm_fwd,
     load,
+    qk_norm_rope_fwd,
     rmsnorm_fwd,
     rmsnorm_rope_fp8_fwd,
     rope_apply_interleaved,

@@ -27,7 +27,8 @@ STATUS = {
 }
 
 EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
-           "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qrw_status_string")
+           "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qk_norm_rope_fwd",
+           "qrw_status_string")
 
 
 class QrwError(RuntimeError):
@@ -57,6 +58,8 @@ def load():
     L.rmsnorm_rope_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                        i32, i32, i32, f32, vp]
     L.act_quant_fp8_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    L.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32,
+                                   i32, f32, vp]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = i32
     L.qrw_status_string.argtypes = [i32]
@@ -81,6 +84,8 @@ def _dtype(t):
 
 
 def _rows(t, name):
+    if t.dim() == 2 and t.shape[0] == 0:  # empty: strides carry no meaning
+        return 0, t.shape[1], t.shape[1]
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError(f"{name} must be 2-D with a unit last stride, got {tuple(t.shape)} "
                          f"strides {t.stride()}")
@@ -189,3 +194,22 @@ def act_quant_fp8_fwd(x, group: int | None = None, q=None, scales=None):
                                   _stream(x))
     _check("act_quant_fp8_fwd", st)
     return q, scales
+
+
+def qk_norm_rope_fwd(qkv, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: int,
+                     head_dim: int, rope_dim: int | None = None, neox: bool = True,
+                     eps: float = 1e-6):
+    """Per-head RMSNorm + RoPE on the q and k heads of 2-D ``qkv``, in place."""
+    tokens, n, xs = _rows(qkv, "qkv")
+    if (q_heads + 2 * kv_heads) * head_dim != n:
+        raise ValueError("(q_heads + 2 * kv_heads) * head_dim must equal the row length")
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    rd = head_dim if rope_dim is None else rope_dim
+    st = load().qk_norm_rope_fwd(_ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight")),
+                                 _ptr(_vec(k_weight, head_dim, "k_weight")), _ptr(cos), _ptr(sin),
+                                 tokens, q_heads, kv_heads, head_dim, rd, xs, _dtype(qkv),
+                                 _dtype(cos), int(bool(neox)), eps, _stream(qkv))
+    _check("qk_norm_rope_fwd", st)
+    return qkv

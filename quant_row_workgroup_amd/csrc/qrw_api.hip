@@ -206,6 +206,41 @@ int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, in
                                           q_row_stride, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int qk_norm_rope_fwd(void* qkv, const void* q_weight, const void* k_weight, const void* cos,
+                     const void* sin, int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                     int64_t head_dim, int64_t rope_dim, int64_t token_stride, int dtype,
+                     int cs_dtype, int neox, float eps, void* stream) {
+  if (!is_16bit(dtype) || !cs_ok(dtype, cs_dtype)) return QRW_ERR_DTYPE;
+  if (tokens < 0 || q_heads < 1 || kv_heads < 0) return QRW_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return QRW_ERR_SHAPE;
+  if (rope_dim < 16 || rope_dim > head_dim || (rope_dim & (rope_dim - 1)) != 0)
+    return QRW_ERR_SHAPE;
+  if (q_heads > (1 << 16) || kv_heads > (1 << 16)) return QRW_ERR_SHAPE;
+  const int64_t n = (q_heads + 2 * kv_heads) * head_dim;
+  if (tokens > (int64_t)0x7FFFFFFF) return QRW_ERR_SHAPE;
+  if (token_stride < n || token_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (!eps_ok(eps)) return QRW_ERR_VALUE;
+  if (neox != 0 && neox != 1) return QRW_ERR_VALUE;
+  if (tokens == 0) return QRW_OK;
+  if (!qkv || !cos || !sin) return QRW_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(cos) || !aligned16(sin) ||
+      (q_weight && !aligned16(q_weight)) || (k_weight && !aligned16(k_weight)))
+    return QRW_ERR_ALIGN;
+  const Span out = span_of(qkv, tokens, (q_heads + kv_heads) * head_dim, token_stride, 2);
+  const int64_t tab = tokens * (rope_dim / 2) * (cs_dtype == QRW_F32 ? 4 : 2);
+  if (check_disjoint(q_weight, 2 * head_dim, out) != QRW_OK ||
+      check_disjoint(k_weight, 2 * head_dim, out) != QRW_OK ||
+      check_disjoint(cos, tab, out) != QRW_OK || check_disjoint(sin, tab, out) != QRW_OK)
+    return QRW_ERR_ALIAS;
+  // chunks of one token row: (q_heads + kv_heads) * head_dim / 1024, rounded up
+  if (tokens * (((q_heads + kv_heads) * head_dim + 1023) / 1024) > (int64_t)0x7FFFFFFF * 4)
+    return QRW_ERR_SHAPE;
+  return finish(qrw::launch_qk_norm_rope(qkv, q_weight, k_weight, cos, sin, tokens, q_heads,
+                                         kv_heads, head_dim, rope_dim, token_stride, dtype,
+                                         cs_dtype, neox == 1, eps,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 const char* qrw_status_string(int status) {
   switch (status) {
     case QRW_OK: return "ok";

@@ -33,6 +33,12 @@ hipError_t launch_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_
                                 int64_t n, int64_t group, int64_t xs, int64_t qs, int dtype,
                                 hipStream_t stream);
 
+hipError_t launch_qk_norm_rope(void* qkv, const void* q_weight, const void* k_weight,
+                               const void* cos, const void* sin, int64_t tokens, int64_t q_heads,
+                               int64_t kv_heads, int64_t head_dim, int64_t rope_dim,
+                               int64_t stride, int dtype, int cs_dtype, bool neox, float eps,
+                               hipStream_t stream);
+
 // Number of "items" (pairs of granules) one token of the fused operator holds.
 int64_t fused_items(int64_t heads, int64_t head_dim, int64_t rope_dim);
 

@@ -118,6 +118,22 @@ def act_quant(rows: int, n: int, group: int, elt: int = 2):
     return fused, fused, 3 * rows * n
 
 
+def qk_norm_rope(tokens: int, q_heads: int, kv_heads: int, head_dim: int, rope_dim: int,
+                 elt: int = 2, cs_elt: int = 2):
+    """Per-head QK RMSNorm + RoPE in place: q and k columns are read and written
+    once, v is not touched; two weight vectors and the cos/sin tables are read.
+    Unfused: a per-head RMSNorm kernel then a RoPE kernel on q and k.  FLOPs: 4 per
+    q/k value for the weighted RMSNorm and 3 per rotated value (the TileOPs
+    formula the page cites in s2.4)."""
+    qk = tokens * (q_heads + kv_heads) * head_dim * elt
+    w = 2 * head_dim * elt
+    tab = tokens * (rope_dim // 2) * cs_elt
+    fused = _kernel([qk, w, tab, tab], [qk])
+    unfused = _kernel([qk, w], [qk]) + _kernel([qk, tab, tab], [qk])
+    flops = 4 * tokens * (q_heads + kv_heads) * head_dim + 3 * tokens * (q_heads + kv_heads) * rope_dim
+    return unfused, fused, flops
+
+
 def page_scenarios():
     """The five scenarios of the ledger table, with the pages' shapes."""
     return {
@@ -147,6 +163,9 @@ def counted_bytes(cfg: dict) -> int:
     if op == "act_quant":
         return act_quant(cfg["rows"], cfg["n"], cfg.get("group") or cfg["n"],
                          ELT[cfg["dtype"]])[1]
+    if op == "qk_norm_rope":
+        return qk_norm_rope(cfg["tokens"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                            cfg["rope_dim"], ELT[cfg["dtype"]], ELT[cfg["cs_dtype"]])[1]
     if op == "fused":
         n = cfg["heads"] * cfg["head_dim"]
         return rmsnorm_rope_fp8(cfg["tokens"], n, cfg["rope_dim"], ELT[cfg["dtype"]],

@@ -87,6 +87,10 @@ WORKLOADS = {
                                           dtype="bf16", seed=6),
     "act_quant_4096x4096_bf16_token": dict(op="act_quant", rows=4096, n=4096, group=None,
                                            dtype="bf16", seed=7),
+    "qk_norm_rope_4096_q32_kv8_d128_bf16": dict(op="qk_norm_rope", tokens=4096, q_heads=32,
+                                                kv_heads=8, head_dim=128, rope_dim=128,
+                                                dtype="bf16", cs_dtype="bf16", eps=1e-6,
+                                                neox=True, seed=8),
     "rmsnorm_rope_fp8_4096x4096_bf16": dict(op="fused", tokens=4096, heads=32, head_dim=128,
                                             rope_dim=128, dtype="bf16", cs_dtype="bf16",
                                             eps=1e-6, neox=True, seed=5),
@@ -122,6 +126,15 @@ def make_inputs(name: str, seed: int | None = None, rows: int | None = None) -> 
         x = normal(s, (R, cfg["n"]), 0.0, 3.0, cfg["dtype"], outlier_frac=0.01,
                    outlier_mul=10.0)
         return dict(cfg, rows=R, x=x)
+    if op == "qk_norm_rope":
+        T = cfg["tokens"] if rows is None else rows
+        D = cfg["head_dim"]
+        n = (cfg["q_heads"] + 2 * cfg["kv_heads"]) * D
+        x = normal(s, (T, n), 0.0, 1.0, cfg["dtype"])
+        qw = normal(s + 1000, (D,), 1.0, 0.1, cfg["dtype"])
+        kw = normal(s + 2000, (D,), 1.0, 0.1, cfg["dtype"])
+        c, sn = rope_table(T, cfg["rope_dim"], cfg["cs_dtype"])
+        return dict(cfg, tokens=T, x=x, q_weight=qw, k_weight=kw, cos=c, sin=sn)
     if op == "fused":
         T = cfg["tokens"] if rows is None else rows
         n = cfg["heads"] * cfg["head_dim"]

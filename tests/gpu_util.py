@@ -95,6 +95,11 @@ def rope_terms(x, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox):
     pass-through channels get 0."""
     T = x.shape[0]
     xv = synth.storage_to_f64(x, dtype)[:, : heads * head_dim].reshape(T, heads, head_dim)
+    return _pair_terms(xv, cos, sin, rope_dim, cs_dtype, neox).reshape(T, heads * head_dim)
+
+
+def _pair_terms(xv, cos, sin, rope_dim, cs_dtype, neox):
+    head_dim = xv.shape[-1]
     c = synth.storage_to_f64(cos, cs_dtype)[:, None, :]
     s = synth.storage_to_f64(sin, cs_dtype)[:, None, :]
     half = rope_dim // 2
@@ -108,7 +113,24 @@ def rope_terms(x, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox):
     out = np.zeros_like(xv)
     out[..., a] = m
     out[..., b] = m
-    return out.reshape(T, heads * head_dim)
+    return out
+
+
+def qk_terms(x, q_weight, k_weight, cos, sin, q_heads, kv_heads, head_dim, rope_dim, dtype,
+             cs_dtype, neox, eps):
+    """rope_terms of u = x * w for the q/k heads, times each head's rstd (float64);
+    shape [tokens, (q_heads + kv_heads) * head_dim]."""
+    T = x.shape[0]
+    H = q_heads + kv_heads
+    xv = synth.storage_to_f64(x, dtype)[:, : H * head_dim].reshape(T, H, head_dim)
+    rstd = 1.0 / np.sqrt((xv ** 2).mean(axis=2, keepdims=True) + float(np.float32(eps)))
+    w = np.ones((H, head_dim))
+    if q_weight is not None:
+        w[:q_heads] = synth.storage_to_f64(q_weight, dtype)
+    if k_weight is not None:
+        w[q_heads:] = synth.storage_to_f64(k_weight, dtype)
+    terms = _pair_terms(xv * w[None], cos, sin, rope_dim, cs_dtype, neox) * rstd
+    return terms.reshape(T, H * head_dim)
 
 
 def assert_codes(got, want, min_exact=0.999, max_step=1, what=""):

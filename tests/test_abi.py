@@ -37,7 +37,7 @@ def declared_functions():
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_five_operators():
+def test_header_declares_every_exported_function():
     assert declared_functions() == sorted(qrw.EXPORTS)
 
 
@@ -166,3 +166,29 @@ def aq(**kw):
 ])
 def test_act_quant_validation(kw, want):
     assert aq(**kw) == want
+
+
+def qk(**kw):
+    a = dict(x=X, wq=W, wk=Y, c=C, s=S, T=4, Hq=32, Hkv=8, D=128, R=128, xs=6144,
+             dtype=BF16, cs=BF16, neox=1, eps=1e-6)
+    a.update(kw)
+    return qrw.load().qk_norm_rope_fwd(a["x"], a["wq"], a["wk"], a["c"], a["s"], a["T"],
+                                       a["Hq"], a["Hkv"], a["D"], a["R"], a["xs"], a["dtype"],
+                                       a["cs"], a["neox"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(c=None), NULL), (dict(s=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(cs=F16), DTYPE),
+    (dict(D=96, xs=4608), SHAPE), (dict(D=512, xs=24576), SHAPE), (dict(R=8), SHAPE),
+    (dict(R=96), SHAPE), (dict(R=256), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE),
+    (dict(xs=6136), STRIDE), (dict(xs=6148), STRIDE),
+    (dict(x=ctypes.c_void_p((1 << 32) + 8)), ALIGN), (dict(wk=ctypes.c_void_p((2 << 32) + 4)), ALIGN),
+    (dict(eps=float("nan")), VALUE), (dict(neox=-1), VALUE),
+    (dict(c=ctypes.c_void_p((1 << 32) + 1024)), ALIAS),   # table inside the q/k columns
+    (dict(wq=ctypes.c_void_p((1 << 32) + 12288)), ALIAS),  # weight inside row 1
+    (dict(T=0), OK), (dict(T=0, x=None, c=None, s=None), OK),
+    (dict(T=0, R=24), SHAPE),
+])
+def test_qk_norm_rope_validation(kw, want):
+    assert qk(**kw) == want

@@ -58,3 +58,13 @@ def test_counted_bytes_of_the_workloads():
     }
     for name, b in want.items():
         assert ledger.counted_bytes(synth.WORKLOADS[name]) == b, name
+
+
+def test_qk_norm_rope_bytes_count_only_q_and_k():
+    # 4096 tokens, 32 query + 8 key heads of 128 bf16 channels read and written,
+    # two 128-wide weights, bf16 cos/sin of 64 entries per token; value heads free
+    cfg = synth.WORKLOADS["qk_norm_rope_4096_q32_kv8_d128_bf16"]
+    qk = 4096 * 40 * 128 * 2
+    assert ledger.counted_bytes(cfg) == 2 * qk + 2 * 128 * 2 + 2 * 4096 * 64 * 2 == 84_935_168
+    unfused, fused, _ = ledger.qk_norm_rope(4096, 32, 8, 128, 128)
+    assert unfused - fused == 2 * qk  # the intermediate is written once and read once
