@@ -77,6 +77,10 @@ def _load():
     L.oracle_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                       i32, i32, i32, f32]
     L.oracle_qk_norm_rope.restype = None
+    L.oracle_qk_norm_rope_fp8_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                             i64, i64, i64, i64, i64, i64, i64, i64, i32, i32,
+                                             i32, f32]
+    L.oracle_qk_norm_rope_fp8_kv.restype = None
     _lib = L
     return L
 
@@ -229,3 +233,37 @@ def qk_norm_rope(x, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: int, h
                           tokens, q_heads, kv_heads, head_dim, rope_dim, xs, ys,
                           DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)), eps)
     return y
+
+
+def qk_norm_rope_fp8_kv(x, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: int,
+                        head_dim: int, rope_dim: int, dtype: str, cs_dtype: str, neox: bool,
+                        eps: float, slots=None, num_slots: int | None = None,
+                        cache_stride: int | None = None, fill: int = 0):
+    """QK RMSNorm + RoPE with the FP8 KV-cache write.  Returns (q_out [tokens,
+    q_heads*head_dim], k_cache, v_cache [num_slots, cache_stride] uint8, k_scales,
+    v_scales [num_slots, kv_heads] float32).  Cache rows no token maps to keep
+    ``fill`` (codes) and NaN (scales)."""
+    L = _load()
+    x = _check(x, dtype, "x")
+    q_weight = _check(q_weight, dtype, "q_weight")
+    k_weight = _check(k_weight, dtype, "k_weight")
+    cos = _check(cos, cs_dtype, "cos")
+    sin = _check(sin, cs_dtype, "sin")
+    tokens, xs = x.shape
+    assert cos.shape == (tokens, rope_dim // 2) and sin.shape == cos.shape
+    ns = tokens if num_slots is None else num_slots
+    cst = kv_heads * head_dim if cache_stride is None else cache_stride
+    if slots is not None:
+        slots = np.ascontiguousarray(slots, dtype=np.int64)
+        assert slots.shape == (tokens,)
+    qs = q_heads * head_dim
+    q = np.full((tokens, qs), fill, dtype=_STORAGE[dtype])
+    kc = np.full((ns, cst), fill, dtype=np.uint8)
+    vc = np.full((ns, cst), fill, dtype=np.uint8)
+    ksc = np.full((ns, kv_heads), np.nan, dtype=np.float32)
+    vsc = np.full((ns, kv_heads), np.nan, dtype=np.float32)
+    L.oracle_qk_norm_rope_fp8_kv(_ptr(x), _ptr(q_weight), _ptr(k_weight), _ptr(cos), _ptr(sin),
+                                 _ptr(q), _ptr(kc), _ptr(vc), _ptr(ksc), _ptr(vsc), _ptr(slots),
+                                 ns, tokens, q_heads, kv_heads, head_dim, rope_dim, xs, qs, cst,
+                                 DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)), eps)
+    return q, kc, vc, ksc, vsc

@@ -30,12 +30,18 @@
  *    the binary32 constant the kernels hold; the scale is stored as binary32.
  *  - The fused operator does not round between the norm and the rotation.
  *  - eps enters as the binary32 value the caller passes.
+ *  - The quantised KV-cache write of the QK-norm fusion ([EW] s2.4) uses the
+ *    per-token cast with each (token, head) of k and of v as its own group,
+ *    k after its norm and rotation (unrounded), v as stored; cache rows are
+ *    addressed through a slot per token, and slots outside the cache are
+ *    skipped.
  *
  * Every function below has a pin in tests/ (brute force, closed forms or
  * invariants); none is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define OR_F16 1
@@ -458,4 +464,94 @@ void oracle_qk_norm_rope(const void* x, const void* q_weight, const void* k_weig
       }
     }
   }
+}
+
+/* ------------------------------------------------------------------ */
+/* One head's values quantised as in the per-token cast ([EW] s3.1.5)   */
+/* with the head as the group: scale = max(amax, 1e-4) / 448, codes of  */
+/* the binary32 quotient z / scale, clamped to +-448.                   */
+/* ------------------------------------------------------------------ */
+static void quant_head_e4m3(const double* z, int64_t n, uint8_t* codes, float* scale_out) {
+  const double fp8_max = 448.0;
+  double amax = 0.0;
+  for (int64_t j = 0; j < n; ++j)
+    if (fabs(z[j]) > amax) amax = fabs(z[j]);
+  float scale = (float)(fmax(amax, (double)1e-4f) / fp8_max);
+  *scale_out = scale;
+  for (int64_t j = 0; j < n; ++j) {
+    double v = (double)(float)(z[j] / (double)scale);
+    if (v > fp8_max) v = fp8_max;
+    if (v < -fp8_max) v = -fp8_max;
+    codes[j] = oracle_encode_e4m3(v);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* QK RMSNorm + RoPE with the quantised KV-cache write ([EW] s2.4: the  */
+/* cross-module fusion Q/K RMSNorm + RoPE + quantised write of the KV   */
+/* cache).  Per token t (row layout as in oracle_qk_norm_rope):         */
+/*   q heads: q_out = round_T(RoPE(x * r * q_weight))                   */
+/*   k heads: z = RoPE(x * r * k_weight), unrounded; v heads: z = x     */
+/*   k and v heads are each quantised with one scale per (token, head)  */
+/*   and written to cache row slot = slots[t] (t when slots is NULL):   */
+/*   k_cache[slot * cache_stride + h * head_dim + j],                   */
+/*   k_scales[slot * kv_heads + h]; likewise v.  A slot outside          */
+/*   [0, num_slots) writes nothing to the caches (q is still written).  */
+/* ------------------------------------------------------------------ */
+void oracle_qk_norm_rope_fp8_kv(const void* x, const void* q_weight, const void* k_weight,
+                                const void* cosv, const void* sinv, void* q_out,
+                                uint8_t* k_cache, uint8_t* v_cache, float* k_scales,
+                                float* v_scales, const int64_t* slots, int64_t num_slots,
+                                int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                                int64_t head_dim, int64_t rope_dim, int64_t x_stride,
+                                int64_t q_stride, int64_t cache_stride, int dtype, int cs_dtype,
+                                int neox, float eps) {
+  int64_t half = rope_dim / 2;
+  int64_t start = head_dim - rope_dim;
+  double* z = (double*)malloc((size_t)head_dim * sizeof(double));
+  uint8_t* codes = (uint8_t*)malloc((size_t)head_dim);
+  for (int64_t t = 0; t < tokens; ++t) {
+    int64_t slot = slots ? slots[t] : t;
+    int cached = slot >= 0 && slot < num_slots;
+    for (int64_t h = 0; h < q_heads + 2 * kv_heads; ++h) {
+      int64_t xb = t * x_stride + h * head_dim;
+      if (h < q_heads + kv_heads) {
+        const void* w = h < q_heads ? q_weight : k_weight;
+        double ss = 0.0;
+        for (int64_t j = 0; j < head_dim; ++j) {
+          double v = load_el(x, xb + j, dtype);
+          ss += v * v;
+        }
+        double rstd = 1.0 / sqrt(ss / (double)head_dim + (double)eps);
+        for (int64_t j = 0; j < head_dim; ++j)
+          z[j] = load_el(x, xb + j, dtype) * rstd * (w ? load_el(w, j, dtype) : 1.0);
+        for (int64_t p = 0; p < half; ++p) {
+          int64_t a, b;
+          rope_pair_index(p, half, neox, &a, &b);
+          double na = z[start + a], nb = z[start + b];
+          double c = load_el(cosv, t * half + p, cs_dtype);
+          double s = load_el(sinv, t * half + p, cs_dtype);
+          z[start + a] = na * c - nb * s;
+          z[start + b] = na * s + nb * c;
+        }
+        if (h < q_heads) {
+          for (int64_t j = 0; j < head_dim; ++j)
+            store_el(q_out, t * q_stride + h * head_dim + j, dtype, z[j]);
+          continue;
+        }
+      } else {
+        for (int64_t j = 0; j < head_dim; ++j) z[j] = load_el(x, xb + j, dtype);
+      }
+      if (!cached) continue;
+      int is_k = h < q_heads + kv_heads;
+      int64_t hk = h - q_heads - (is_k ? 0 : kv_heads);
+      float scale;
+      quant_head_e4m3(z, head_dim, codes, &scale);
+      uint8_t* dst = (is_k ? k_cache : v_cache) + slot * cache_stride + hk * head_dim;
+      for (int64_t j = 0; j < head_dim; ++j) dst[j] = codes[j];
+      (is_k ? k_scales : v_scales)[slot * kv_heads + hk] = scale;
+    }
+  }
+  free(z);
+  free(codes);
 }

@@ -240,3 +240,45 @@ def qk_norm_rope_ref(xrow, qw, kw, crow, srow, q_heads, kv_heads, head_dim, rope
         for j, v in enumerate(z):
             out[base + j] = round_to(v, fmt)
     return out
+
+
+def _quant_values(vals):
+    """E4M3 codes and scale of a group of exact values (per-token cast, one group)."""
+    floor = Decimal(float(np.float32(1e-4)))
+    scale = round_f32(max(max(abs(v) for v in vals), floor) / 448)
+    S = Decimal(scale)
+    codes = []
+    for v in vals:
+        q = Decimal(round_f32(v / S))  # the code is decided on the binary32 quotient
+        codes.append(round_to(min(max(q, Decimal(-448)), Decimal(448)), "e4m3"))
+    return codes, scale
+
+
+def qk_kv_ref(xrow, qw, kw, crow, srow, q_heads, kv_heads, head_dim, rope_dim, fmt, cs_fmt,
+              neox, eps32):
+    """Exact QK RMSNorm + RoPE with the FP8 KV write, one token row.  Returns
+    (q output codes, k codes, k scales, v codes, v scales); k/v codes are the
+    concatenation of the heads."""
+    cs = [dec(b, cs_fmt) for b in crow]
+    ss = [dec(b, cs_fmt) for b in srow]
+    eps = Decimal(float(np.float32(eps32)))
+    q, kc, ks, vc, vs = [], [], [], [], []
+    for h in range(q_heads + 2 * kv_heads):
+        base = h * head_dim
+        xs = [dec(b, fmt) for b in xrow[base:base + head_dim]]
+        if h >= q_heads + kv_heads:
+            c, s = _quant_values(xs)
+            vc += c
+            vs.append(s)
+            continue
+        wrow = qw if h < q_heads else kw
+        ws = [dec(b, fmt) for b in wrow] if wrow is not None else [Decimal(1)] * head_dim
+        r = 1 / sqrt(sum(v * v for v in xs) / head_dim + eps)
+        z = rope_values([a * r * b for a, b in zip(xs, ws)], cs, ss, 1, head_dim, rope_dim, neox)
+        if h < q_heads:
+            q += [round_to(v, fmt) for v in z]
+        else:
+            c, s = _quant_values(z)
+            kc += c
+            ks.append(s)
+    return q, kc, ks, vc, vs
