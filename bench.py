@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "fused": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
+    "qk_kv": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
 }
 
 
@@ -118,6 +119,8 @@ class Workload:
         tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
         def up(bits, dt):
+            if bits.dtype == np.int64:
+                return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
             if dt == "f32":
                 return torch.from_numpy(np.ascontiguousarray(bits)).to(dev)
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt[dt]).to(dev)
@@ -127,7 +130,7 @@ class Workload:
         code = {"f16": 1, "bf16": 2, "f32": 3}
         base = {k: up(v, self.cfg.get("cs_dtype", dt) if k in ("cos", "sin") else dt)
                 for k, v in self.inp.items()
-                if k in ("x", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight")}
+                if k in ("x", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight", "slots")}
         self.sets = []
         for _ in range(sets):
             s = {k: v.clone() for k, v in base.items()}
@@ -141,6 +144,13 @@ class Workload:
                 n = self.cfg["heads"] * self.cfg["head_dim"]
                 s["q"] = torch.empty((T, n), dtype=torch.uint8, device=dev)
                 s["scales"] = torch.empty((T,), dtype=torch.float32, device=dev)
+            elif op == "qk_kv":
+                ns, kvn = self.cfg["num_slots"], self.cfg["kv_heads"] * self.cfg["head_dim"]
+                for k in ("k_cache", "v_cache"):
+                    s[k] = torch.zeros((ns, kvn), dtype=torch.uint8, device=dev)
+                for k in ("k_scales", "v_scales"):
+                    s[k] = torch.zeros((ns, self.cfg["kv_heads"]), dtype=torch.float32,
+                                       device=dev)
             elif op != "qk_norm_rope":  # qk_norm_rope works in place on x
                 s["y"] = torch.empty_like(s["x"])
             self.sets.append(s)
@@ -151,7 +161,7 @@ class Workload:
 
     def reset(self) -> None:
         """Restore the inputs an in-place operator overwrote."""
-        if self.op == "qk_norm_rope":
+        if self.op in ("qk_norm_rope", "qk_kv"):
             for s in self.sets:
                 s["x"].copy_(self.pristine)
 
@@ -175,6 +185,15 @@ class Workload:
                                            c["kv_heads"], D, c["rope_dim"], n,
                                            self.code[c["dtype"]], self.code[c["cs_dtype"]],
                                            int(c["neox"]), c["eps"], st)
+        elif self.op == "qk_kv":
+            T, D = c["tokens"], c["head_dim"]
+            n = (c["q_heads"] + 2 * c["kv_heads"]) * D
+            rc = self.lib.qk_norm_rope_fp8_kv_fwd(
+                p(s["x"]), p(s["q_weight"]), p(s["k_weight"]), p(s["cos"]), p(s["sin"]),
+                p(s["k_cache"]), p(s["v_cache"]), p(s["k_scales"]), p(s["v_scales"]),
+                p(s["slots"]), c["num_slots"], T, c["q_heads"], c["kv_heads"], D, c["rope_dim"],
+                n, c["kv_heads"] * D, self.code[c["dtype"]], self.code[c["cs_dtype"]],
+                int(c["neox"]), c["eps"], st)
         elif self.op == "act_quant":
             g = c.get("group") or c["n"]
             rc = self.lib.act_quant_fp8_fwd(p(s["x"]), p(s["q"]), p(s["scales"]), c["rows"],
@@ -196,7 +215,9 @@ class Workload:
 
     def outputs(self, i: int):
         s = self.sets[i % len(self.sets)]
-        keys = ("x",) if self.op == "qk_norm_rope" else ("q", "scales", "y")
+        keys = {"qk_norm_rope": ("x",),
+                "qk_kv": ("x", "k_cache", "v_cache", "k_scales", "v_scales")}.get(
+                    self.op, ("q", "scales", "y"))
         return [s[k].clone() for k in keys if k in s]
 
 
@@ -255,7 +276,7 @@ def cpu_baseline(name: str, seconds: float):
     inp = synth.make_inputs(name, rows=rows)
     cfg = dict(synth.WORKLOADS[name])
     op = cfg["op"]
-    key = "tokens" if op in ("rope", "fused", "qk_norm_rope") else "rows"
+    key = "tokens" if op in ("rope", "fused", "qk_norm_rope", "qk_kv") else "rows"
     cfg[key] = rows
     bytes_per_call = ledger.counted_bytes(cfg)
 
@@ -266,6 +287,12 @@ def cpu_baseline(name: str, seconds: float):
                                     cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "act_quant":
             oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
+        elif op == "qk_kv":
+            oracle.qk_norm_rope_fp8_kv(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
+                                       inp["sin"], cfg["q_heads"], cfg["kv_heads"],
+                                       cfg["head_dim"], cfg["rope_dim"], cfg["dtype"],
+                                       cfg["cs_dtype"], cfg["neox"], cfg["eps"],
+                                       slots=inp["slots"], num_slots=cfg["num_slots"])
         elif op == "qk_norm_rope":
             oracle.qk_norm_rope(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
                                 inp["sin"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],

@@ -10,7 +10,8 @@
  *   s3.3.2  reference RoPE (fp32 math, one final cast)
  *   s3.1.5  per-token / per-group FP8 cast (amax -> scale -> clamp -> cast)
  *   s3.3.4  the fused RMSNorm + RoPE + per-token quantisation operator
- *   s2.4    cross-module fusion: per-head q/k RMSNorm + RoPE, v untouched
+ *   s2.4    cross-module fusion: per-head q/k RMSNorm + RoPE, v untouched, and
+ *           the variant that writes k and v to an FP8 KV cache
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -164,6 +165,34 @@ int qk_norm_rope_fwd(void* qkv, const void* q_weight, const void* k_weight, cons
                      const void* sin, int64_t tokens, int64_t q_heads, int64_t kv_heads,
                      int64_t head_dim, int64_t rope_dim, int64_t token_stride, int dtype,
                      int cs_dtype, int neox, float eps, void* stream);
+
+/*
+ * QK RMSNorm + RoPE with the quantised KV-cache write (s2.4, the cross-module
+ * fusion: Q/K RMSNorm + RoPE + quantised KV-cache write).  Same row layout,
+ * arithmetic and shape limits as qk_norm_rope_fwd, and kv_heads >= 1; then:
+ *   q heads are written back in place into qkv (qkv's k and v columns are
+ *   only read);
+ *   for every k head (after its norm and rotation, unrounded) and every v
+ *   head (as stored) of token t, with s = slots[t] (s = t if slots is NULL):
+ *     scale = max(amax over the head, 1e-4) / 448        (float32)
+ *     code_j = E4M3FN(RN_f32(value_j / scale))            (s3.1.5's cast)
+ *     k_cache[s * cache_stride + h * head_dim + j] = code_j
+ *     k_scales[s * kv_heads + h] = scale                  (v likewise)
+ * k_cache, v_cache: num_slots rows of cache_stride bytes (>= kv_heads *
+ * head_dim, multiple of 8), 16-byte aligned; k_scales, v_scales: float
+ * [num_slots, kv_heads]; slots: int64 [tokens] or NULL (then num_slots >=
+ * tokens).  A token whose slot is outside [0, num_slots) (e.g. -1 for
+ * padding) writes nothing to the caches; its q is still written.  Two tokens
+ * with the same slot race.  Outputs must not overlap one another or any
+ * input (QRW_ERR_ALIAS).
+ */
+int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weight,
+                            const void* cos, const void* sin, uint8_t* k_cache, uint8_t* v_cache,
+                            float* k_scales, float* v_scales, const int64_t* slots,
+                            int64_t num_slots, int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                            int64_t head_dim, int64_t rope_dim, int64_t token_stride,
+                            int64_t cache_stride, int dtype, int cs_dtype, int neox, float eps,
+                            void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* qrw_status_string(int status);

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     act_quant_fp8_fwd,
     layernorm_fwd,
     load,
+    qk_norm_rope_fp8_kv_fwd,
     qk_norm_rope_fwd,
     rmsnorm_fwd,
     rmsnorm_rope_fp8_fwd,

@@ -28,6 +28,7 @@ STATUS = {
 
 EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
            "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qk_norm_rope_fwd",
+           "qk_norm_rope_fp8_kv_fwd",
            "qrw_status_string")
 
 
@@ -60,6 +61,8 @@ def load():
     L.act_quant_fp8_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     L.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32,
                                    i32, f32, vp]
+    L.qk_norm_rope_fp8_kv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                          i64, i64, i64, i64, i64, i32, i32, i32, f32, vp]
     for name in EXPORTS[:-1]:
         getattr(L, name).restype = i32
     L.qrw_status_string.argtypes = [i32]
@@ -212,4 +215,38 @@ def qk_norm_rope_fwd(qkv, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: 
                                  tokens, q_heads, kv_heads, head_dim, rd, xs, _dtype(qkv),
                                  _dtype(cos), int(bool(neox)), eps, _stream(qkv))
     _check("qk_norm_rope_fwd", st)
+    return qkv
+
+
+def qk_norm_rope_fp8_kv_fwd(qkv, q_weight, k_weight, cos, sin, k_cache, v_cache, k_scales,
+                            v_scales, q_heads: int, kv_heads: int, head_dim: int,
+                            rope_dim: int | None = None, slots=None, neox: bool = True,
+                            eps: float = 1e-6):
+    """QK RMSNorm + RoPE with q written back into 2-D ``qkv`` and k/v cast to
+    E4M3 into the cache rows ``slots`` (int64 per token; None: row t)."""
+    tokens, n, xs = _rows(qkv, "qkv")
+    if (q_heads + 2 * kv_heads) * head_dim != n:
+        raise ValueError("(q_heads + 2 * kv_heads) * head_dim must equal the row length")
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    num_slots, kvn, cs = _rows(k_cache, "k_cache")
+    if tuple(v_cache.shape) != (num_slots, kvn) or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must have k_cache's shape and strides")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("caches hold uint8 E4M3 codes")
+    for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (num_slots, kv_heads):
+            raise ValueError(f"{nm} must be packed float32 [num_slots, kv_heads]")
+    if slots is not None and (slots.dtype != torch.int64 or not slots.is_contiguous()
+                              or tuple(slots.shape) != (tokens,)):
+        raise ValueError("slots must be packed int64 [tokens]")
+    rd = head_dim if rope_dim is None else rope_dim
+    st = load().qk_norm_rope_fp8_kv_fwd(
+        _ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight")),
+        _ptr(_vec(k_weight, head_dim, "k_weight")), _ptr(cos), _ptr(sin), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(slots), num_slots, tokens, q_heads,
+        kv_heads, head_dim, rd, xs, cs, _dtype(qkv), _dtype(cos), int(bool(neox)), eps,
+        _stream(qkv))
+    _check("qk_norm_rope_fp8_kv_fwd", st)
     return qkv

@@ -241,6 +241,63 @@ int qk_norm_rope_fwd(void* qkv, const void* q_weight, const void* k_weight, cons
                                          static_cast<hipStream_t>(stream)));
 }
 
+int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weight,
+                            const void* cos, const void* sin, uint8_t* k_cache, uint8_t* v_cache,
+                            float* k_scales, float* v_scales, const int64_t* slots,
+                            int64_t num_slots, int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                            int64_t head_dim, int64_t rope_dim, int64_t token_stride,
+                            int64_t cache_stride, int dtype, int cs_dtype, int neox, float eps,
+                            void* stream) {
+  if (!is_16bit(dtype) || !cs_ok(dtype, cs_dtype)) return QRW_ERR_DTYPE;
+  if (tokens < 0 || q_heads < 1 || kv_heads < 1 || num_slots < 0) return QRW_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return QRW_ERR_SHAPE;
+  if (rope_dim < 16 || rope_dim > head_dim || (rope_dim & (rope_dim - 1)) != 0)
+    return QRW_ERR_SHAPE;
+  if (q_heads > (1 << 16) || kv_heads > (1 << 16)) return QRW_ERR_SHAPE;
+  if (tokens > (int64_t)0x7FFFFFFF) return QRW_ERR_SHAPE;
+  if (!slots && num_slots < tokens) return QRW_ERR_SHAPE;  // token t goes to row t
+  const int64_t n = (q_heads + 2 * kv_heads) * head_dim;
+  const int64_t kvn = kv_heads * head_dim;
+  if (token_stride < n || token_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (cache_stride < kvn || cache_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (!eps_ok(eps)) return QRW_ERR_VALUE;
+  if (neox != 0 && neox != 1) return QRW_ERR_VALUE;
+  if (tokens == 0) return QRW_OK;
+  if (!qkv || !cos || !sin || !k_cache || !v_cache || !k_scales || !v_scales) return QRW_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(cos) || !aligned16(sin) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || (q_weight && !aligned16(q_weight)) ||
+      (k_weight && !aligned16(k_weight)) || (reinterpret_cast<uintptr_t>(k_scales) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(v_scales) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(slots) & 7u) != 0)
+    return QRW_ERR_ALIGN;
+  // outputs (and the rows the kernel reads, which hold the q output) are pairwise
+  // disjoint; read-only inputs overlap none of them
+  Span out[5];
+  int nout = 0;
+  out[nout++] = span_of(qkv, tokens, n, token_stride, 2);
+  if (num_slots > 0) {
+    out[nout++] = span_of(k_cache, num_slots, kvn, cache_stride, 1);
+    out[nout++] = span_of(v_cache, num_slots, kvn, cache_stride, 1);
+    out[nout++] = span_of(k_scales, 1, num_slots * kv_heads, 0, 4);
+    out[nout++] = span_of(v_scales, 1, num_slots * kv_heads, 0, 4);
+  }
+  for (int i = 0; i < nout; ++i)
+    for (int k = i + 1; k < nout; ++k)
+      if (overlap(out[i], out[k])) return QRW_ERR_ALIAS;
+  const int64_t tab = tokens * (rope_dim / 2) * (cs_dtype == QRW_F32 ? 4 : 2);
+  for (int i = 0; i < nout; ++i)
+    if (check_disjoint(q_weight, 2 * head_dim, out[i]) != QRW_OK ||
+        check_disjoint(k_weight, 2 * head_dim, out[i]) != QRW_OK ||
+        check_disjoint(cos, tab, out[i]) != QRW_OK || check_disjoint(sin, tab, out[i]) != QRW_OK ||
+        check_disjoint(slots, 8 * tokens, out[i]) != QRW_OK)
+      return QRW_ERR_ALIAS;
+  if (tokens * ((n + 1023) / 1024) > (int64_t)0x7FFFFFFF * 4) return QRW_ERR_SHAPE;
+  return finish(qrw::launch_qk_norm_rope_fp8_kv(
+      qkv, q_weight, k_weight, cos, sin, k_cache, v_cache, k_scales, v_scales, slots, num_slots,
+      tokens, q_heads, kv_heads, head_dim, rope_dim, token_stride, cache_stride, dtype, cs_dtype,
+      neox == 1, eps, static_cast<hipStream_t>(stream)));
+}
+
 const char* qrw_status_string(int status) {
   switch (status) {
     case QRW_OK: return "ok";

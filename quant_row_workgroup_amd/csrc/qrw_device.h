@@ -193,6 +193,39 @@ __device__ __forceinline__ float wave_max(float v) {
                fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
+// Sum / max over aligned groups of L consecutive lanes (L = 1, 2, 4, ..., 64);
+// every lane of a group receives the group's value.  All lanes must be active.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (L >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (L >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (L >= 32) v += lane_xor<16>(v);
+  if constexpr (L >= 64) v = lane_value(v, 0) + lane_value(v, 32);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (L >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if constexpr (L >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if constexpr (L >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  if constexpr (L >= 32) v = fmaxf(v, lane_xor<16>(v));
+  if constexpr (L >= 64) v = fmaxf(lane_value(v, 0), lane_value(v, 32));
+  return v;
+}
+
+// RN(x / s) given y = RN(1 / s), without a division (Markstein's correction:
+// q = RN(x*y), r = x - q*s exactly by one fma, RN(q + r*y) is the correctly
+// rounded quotient for the |x| <= 448*s range of a quantiser); the sign of a
+// zero x is kept.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = fmaf(-q, s, x);
+  return __builtin_copysignf(fmaf(r, y, q), x);
+}
+
 // Sum of squares of the two 16-bit elements of a packed pair, added to acc,
 // in one v_dot2c_f32_{bf16,f16}: the products of 16-bit values are exact in
 // binary32.  (The pair is taken by value: see the note on Table8<float>.)

@@ -39,6 +39,15 @@ hipError_t launch_qk_norm_rope(void* qkv, const void* q_weight, const void* k_we
                                int64_t stride, int dtype, int cs_dtype, bool neox, float eps,
                                hipStream_t stream);
 
+hipError_t launch_qk_norm_rope_fp8_kv(void* qkv, const void* q_weight, const void* k_weight,
+                                      const void* cos, const void* sin, uint8_t* k_cache,
+                                      uint8_t* v_cache, float* k_scales, float* v_scales,
+                                      const int64_t* slots, int64_t num_slots, int64_t tokens,
+                                      int64_t q_heads, int64_t kv_heads, int64_t head_dim,
+                                      int64_t rope_dim, int64_t stride, int64_t cache_stride,
+                                      int dtype, int cs_dtype, bool neox, float eps,
+                                      hipStream_t stream);
+
 // Number of "items" (pairs of granules) one token of the fused operator holds.
 int64_t fused_items(int64_t heads, int64_t head_dim, int64_t rope_dim);
 

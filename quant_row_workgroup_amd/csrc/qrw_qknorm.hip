@@ -23,6 +23,14 @@
 //
 // Arithmetic (binary32, one rounding at the output): u = x * w (exact for
 // 16-bit operands), the rotation as one fma per output, then * rstd.
+//
+// With the KV-cache write (the same section's fusion table: Q/K RMSNorm +
+// RoPE + quantised KV-cache write), the chunks cover the whole row: q heads
+// are written back in place as above, while k heads (after norm and
+// rotation) and v heads (as stored) are cast to E4M3FN with one scale per
+// (token, head), the per-token cast of s3.1.5 applied to a head: scale =
+// max(amax, 1e-4) / 448 from a DPP max inside the head's lanes, codes of the
+// correctly rounded binary32 quotient, written to cache row slots[t].
 #include <type_traits>
 
 #include "qrw_device.h"
@@ -30,17 +38,18 @@
 
 namespace qrw {
 
-// Sum over aligned groups of L consecutive lanes (L = 8, 16 or 32); every
-// lane of a group receives the same value.
-template <int L>
-__device__ __forceinline__ float head_sum(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  if constexpr (L >= 16) v += dpp<kDppMirror>(v);
-  if constexpr (L >= 32) v += lane_xor<16>(v);
-  return v;
-}
+// Destination of the quantised k and v heads (unused without the KV write).
+struct KvDest {
+  uint8_t* kc;             // [num_slots] rows of cache_stride bytes
+  uint8_t* vc;
+  float* ks;               // [num_slots, kv_heads]
+  float* vs;
+  const int64_t* slots;    // [tokens] or NULL (token t -> row t)
+  int64_t num_slots;
+  int64_t cache_stride;
+  int k_end;               // first v granule of a row
+  int kv_heads;
+};
 
 template <typename CS>
 __device__ __forceinline__ const char* qk_table_row(const void* base, int64_t t, int half) {
@@ -48,11 +57,11 @@ __device__ __forceinline__ const char* qk_table_row(const void* base, int64_t t,
   return static_cast<const char*>(base) + t * (int64_t)half * bytes;
 }
 
-template <typename T, typename CS, bool NEOX, int HG, int XR, int GC>
+template <typename T, typename CS, bool NEOX, int HG, int XR, int GC, bool KV>
 __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
     uint16_t* qkv, const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
     const void* cosv, const void* sinv, int64_t tokens, int64_t stride, int ng, int q_gran,
-    int chunks, int s0, int half, float n_f, float eps) {
+    int chunks, int s0, int half, float n_f, float eps, KvDest kv) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   const int64_t t = wave / chunks;
@@ -62,6 +71,12 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
   const int j = lane & (HG - 1);        // granule position inside the head
   const int js = j - s0;                // position inside the rotated span (< 0: outside)
   const bool span = js >= 0;
+  int64_t slot = t;
+  bool cached = true;
+  if constexpr (KV) {
+    if (kv.slots) slot = kv.slots[t];
+    cached = slot >= 0 && slot < kv.num_slots;
+  }
 
   u32x4 raw[GC];
 #pragma unroll
@@ -113,22 +128,26 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
     acc1 = sumsq2(T{}, raw[g][1], acc1);
     acc0 = sumsq2(T{}, raw[g][2], acc0);
     acc1 = sumsq2(T{}, raw[g][3], acc1);
-    const float ss = head_sum<HG>(acc0 + acc1);
-    const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+    const float ss = group_sum<HG>(acc0 + acc1);
+    const bool is_q = gi < q_gran;
+    const bool is_v = KV && gi >= kv.k_end;
+    const float rstd = is_v ? 1.0f : 1.0f / sqrtf(ss / n_f + eps);
     float v[8];
     widen8<T>(raw[g], v);
-    const bool is_q = gi < q_gran;
+    if (!is_v) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= is_q ? fq[e] : fk[e];
+      for (int e = 0; e < 8; ++e) v[e] *= is_q ? fq[e] : fk[e];
+    }
+    const bool rot = span && !is_v;
     if (NEOX) {
       float r[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = fmaf(v[e], c[e], lane_xor<XR>(v[e]) * sn[e]);
-      if (span) {
+      if (rot) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = r[e];
       }
-    } else if (span) {
+    } else if (rot) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x0 = v[2 * k], x1 = v[2 * k + 1];
@@ -138,7 +157,27 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= rstd;
-    if (gi < ng) st16_stream(row + 8 * gi, narrow8<T>(v));
+    if constexpr (KV) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+      const float am = fmaxf(group_max<HG>(m), 1e-4f);
+      if (gi < ng) {
+        if (is_q) {
+          st16_stream(row + 8 * gi, narrow8<T>(v));
+        } else if (cached) {
+          const float scale = am / 448.0f;
+          const float y = 1.0f / scale;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
+          const int hg = is_v ? gi - kv.k_end : gi - q_gran;  // granule inside the k (v) part
+          st8_stream((is_v ? kv.vc : kv.kc) + slot * kv.cache_stride + 8 * hg, fp8x8(v));
+          if (j == 0) (is_v ? kv.vs : kv.ks)[slot * kv.kv_heads + hg / HG] = scale;
+        }
+      }
+    } else {
+      if (gi < ng) st16_stream(row + 8 * gi, narrow8<T>(v));
+    }
   }
 }
 
@@ -147,44 +186,112 @@ namespace {
 
 constexpr int kQkChunk = 2;  // granules per lane per wave
 
+// Everything a launch needs besides the template arguments.
+struct QkArgs {
+  dim3 grid;
+  hipStream_t st;
+  uint16_t* x;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const void* c;
+  const void* s;
+  int64_t tokens, stride;
+  int ng, qg, chunks, s0, half;
+  float n_f, eps;
+  KvDest kv;
+};
+
 template <typename T, typename CS, bool NEOX, int HG, int XR>
-void qk_go(dim3 grid, hipStream_t st, uint16_t* x, const uint16_t* wq, const uint16_t* wk,
-           const void* c, const void* s, int64_t tokens, int64_t stride, int ng, int qg,
-           int chunks, int s0, int half, float n_f, float eps) {
-  qk_norm_rope_kernel<T, CS, NEOX, HG, XR, kQkChunk><<<grid, kBlock, 0, st>>>(
-      x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
+void qk_go(const QkArgs& a) {
+  if (a.kv.kc)
+    qk_norm_rope_kernel<T, CS, NEOX, HG, XR, kQkChunk, true><<<a.grid, kBlock, 0, a.st>>>(
+        a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
+        a.n_f, a.eps, a.kv);
+  else
+    qk_norm_rope_kernel<T, CS, NEOX, HG, XR, kQkChunk, false><<<a.grid, kBlock, 0, a.st>>>(
+        a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
+        a.n_f, a.eps, a.kv);
 }
 
 template <typename T, typename CS, bool NEOX, int HG>
-void qk_go_xr(int xr, dim3 grid, hipStream_t st, uint16_t* x, const uint16_t* wq,
-              const uint16_t* wk, const void* c, const void* s, int64_t tokens, int64_t stride,
-              int ng, int qg, int chunks, int s0, int half, float n_f, float eps) {
+void qk_go_xr(int xr, const QkArgs& a) {
   if constexpr (!NEOX) {
-    qk_go<T, CS, NEOX, HG, 1>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
+    qk_go<T, CS, NEOX, HG, 1>(a);
   } else {
     switch (xr) {
-      case 1: qk_go<T, CS, NEOX, HG, 1>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
-      case 2: qk_go<T, CS, NEOX, HG, 2>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
-      case 4: qk_go<T, CS, NEOX, HG, 4>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
+      case 1: qk_go<T, CS, NEOX, HG, 1>(a); break;
+      case 2: qk_go<T, CS, NEOX, HG, 2>(a); break;
+      case 4: qk_go<T, CS, NEOX, HG, 4>(a); break;
       case 8:  // rope_dim <= head_dim keeps xr <= hg / 2
-        if constexpr (HG >= 16) qk_go<T, CS, NEOX, HG, 8>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
+        if constexpr (HG >= 16) qk_go<T, CS, NEOX, HG, 8>(a);
         break;
       default:
-        if constexpr (HG >= 32) qk_go<T, CS, NEOX, HG, 16>(grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
+        if constexpr (HG >= 32) qk_go<T, CS, NEOX, HG, 16>(a);
         break;
     }
   }
 }
 
 template <typename T, typename CS, bool NEOX>
-void qk_go_hg(int hg, int xr, dim3 grid, hipStream_t st, uint16_t* x, const uint16_t* wq,
-              const uint16_t* wk, const void* c, const void* s, int64_t tokens, int64_t stride,
-              int ng, int qg, int chunks, int s0, int half, float n_f, float eps) {
+void qk_go_hg(int hg, int xr, const QkArgs& a) {
   switch (hg) {
-    case 8: qk_go_xr<T, CS, NEOX, 8>(xr, grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
-    case 16: qk_go_xr<T, CS, NEOX, 16>(xr, grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
-    default: qk_go_xr<T, CS, NEOX, 32>(xr, grid, st, x, wq, wk, c, s, tokens, stride, ng, qg, chunks, s0, half, n_f, eps); break;
+    case 8: qk_go_xr<T, CS, NEOX, 8>(xr, a); break;
+    case 16: qk_go_xr<T, CS, NEOX, 16>(xr, a); break;
+    default: qk_go_xr<T, CS, NEOX, 32>(xr, a); break;
   }
+}
+
+}  // namespace
+
+namespace {
+
+hipError_t qk_launch(void* qkv, const void* q_weight, const void* k_weight, const void* cos,
+                     const void* sin, int64_t tokens, int64_t q_heads, int64_t kv_heads,
+                     int64_t head_dim, int64_t rope_dim, int64_t stride, int dtype, int cs_dtype,
+                     bool neox, float eps, KvDest kv, hipStream_t stream) {
+  const int hg = (int)(head_dim / 8);
+  const int xr = (int)(rope_dim / 16);
+  const int64_t heads = kv.kc ? q_heads + 2 * kv_heads : q_heads + kv_heads;
+  QkArgs a;
+  a.ng = (int)(heads * hg);
+  a.qg = (int)(q_heads * hg);
+  const int per_wave = kWave * kQkChunk;
+  a.chunks = (a.ng + per_wave - 1) / per_wave;
+  a.s0 = (int)((head_dim - rope_dim) / 8);
+  a.half = (int)(rope_dim / 2);
+  const int64_t waves = tokens * a.chunks;
+  a.grid = dim3((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
+  a.st = stream;
+  a.x = static_cast<uint16_t*>(qkv);
+  a.wq = static_cast<const uint16_t*>(q_weight);
+  a.wk = static_cast<const uint16_t*>(k_weight);
+  a.c = cos;
+  a.s = sin;
+  a.tokens = tokens;
+  a.stride = stride;
+  a.n_f = (float)head_dim;
+  a.eps = eps;
+  kv.k_end = (int)((q_heads + kv_heads) * hg);
+  kv.kv_heads = (int)kv_heads;
+  a.kv = kv;
+  if (dtype == 1) {
+    if (cs_dtype == 3) {
+      if (neox) qk_go_hg<F16, float, true>(hg, xr, a);
+      else qk_go_hg<F16, float, false>(hg, xr, a);
+    } else {
+      if (neox) qk_go_hg<F16, F16, true>(hg, xr, a);
+      else qk_go_hg<F16, F16, false>(hg, xr, a);
+    }
+  } else {
+    if (cs_dtype == 3) {
+      if (neox) qk_go_hg<BF16, float, true>(hg, xr, a);
+      else qk_go_hg<BF16, float, false>(hg, xr, a);
+    } else {
+      if (neox) qk_go_hg<BF16, BF16, true>(hg, xr, a);
+      else qk_go_hg<BF16, BF16, false>(hg, xr, a);
+    }
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -194,38 +301,29 @@ hipError_t launch_qk_norm_rope(void* qkv, const void* q_weight, const void* k_we
                                int64_t kv_heads, int64_t head_dim, int64_t rope_dim,
                                int64_t stride, int dtype, int cs_dtype, bool neox, float eps,
                                hipStream_t stream) {
-  const int hg = (int)(head_dim / 8);
-  const int xr = (int)(rope_dim / 16);
-  const int ng = (int)((q_heads + kv_heads) * hg);
-  const int qg = (int)(q_heads * hg);
-  const int per_wave = kWave * kQkChunk;
-  const int chunks = (ng + per_wave - 1) / per_wave;
-  const int s0 = (int)((head_dim - rope_dim) / 8);
-  const int half = (int)(rope_dim / 2);
-  const int64_t waves = tokens * chunks;
-  const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
-  auto* x = static_cast<uint16_t*>(qkv);
-  const auto* wq = static_cast<const uint16_t*>(q_weight);
-  const auto* wk = static_cast<const uint16_t*>(k_weight);
-  const float n_f = (float)head_dim;
-  if (dtype == 1) {
-    if (cs_dtype == 3) {
-      if (neox) qk_go_hg<F16, float, true>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-      else qk_go_hg<F16, float, false>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-    } else {
-      if (neox) qk_go_hg<F16, F16, true>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-      else qk_go_hg<F16, F16, false>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-    }
-  } else {
-    if (cs_dtype == 3) {
-      if (neox) qk_go_hg<BF16, float, true>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-      else qk_go_hg<BF16, float, false>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-    } else {
-      if (neox) qk_go_hg<BF16, BF16, true>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-      else qk_go_hg<BF16, BF16, false>(hg, xr, grid, stream, x, wq, wk, cos, sin, tokens, stride, ng, qg, chunks, s0, half, n_f, eps);
-    }
-  }
-  return hipGetLastError();
+  KvDest none{};
+  return qk_launch(qkv, q_weight, k_weight, cos, sin, tokens, q_heads, kv_heads, head_dim,
+                   rope_dim, stride, dtype, cs_dtype, neox, eps, none, stream);
+}
+
+hipError_t launch_qk_norm_rope_fp8_kv(void* qkv, const void* q_weight, const void* k_weight,
+                                      const void* cos, const void* sin, uint8_t* k_cache,
+                                      uint8_t* v_cache, float* k_scales, float* v_scales,
+                                      const int64_t* slots, int64_t num_slots, int64_t tokens,
+                                      int64_t q_heads, int64_t kv_heads, int64_t head_dim,
+                                      int64_t rope_dim, int64_t stride, int64_t cache_stride,
+                                      int dtype, int cs_dtype, bool neox, float eps,
+                                      hipStream_t stream) {
+  KvDest kv{};
+  kv.kc = k_cache;
+  kv.vc = v_cache;
+  kv.ks = k_scales;
+  kv.vs = v_scales;
+  kv.slots = slots;
+  kv.num_slots = num_slots;
+  kv.cache_stride = cache_stride;
+  return qk_launch(qkv, q_weight, k_weight, cos, sin, tokens, q_heads, kv_heads, head_dim,
+                   rope_dim, stride, dtype, cs_dtype, neox, eps, kv, stream);
 }
 
 }  // namespace qrw

@@ -25,26 +25,6 @@
 
 namespace qrw {
 
-// RN(x / s) given y = RN(1 / s); the sign of a zero x is kept.
-__device__ __forceinline__ float div_rn(float x, float s, float y) {
-  const float q = x * y;
-  const float r = fmaf(-q, s, x);
-  return __builtin_copysignf(fmaf(r, y, q), x);
-}
-
-// Max over aligned groups of L consecutive lanes (L = 1, 2, 4, 8, 16, 32, 64);
-// every lane of a group receives the group's max.
-template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (L >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-  if constexpr (L >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-  if constexpr (L >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (L >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-  if constexpr (L >= 32) v = fmaxf(v, lane_xor<16>(v));
-  if constexpr (L >= 64) v = fmaxf(lane_value(v, 0), lane_value(v, 32));
-  return v;
-}
-
 template <typename T, int GPL, bool FULL, int L>
 __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t* x, uint8_t* q,
                                                                  float* scales, int64_t rows,

@@ -134,6 +134,26 @@ def qk_norm_rope(tokens: int, q_heads: int, kv_heads: int, head_dim: int, rope_d
     return unfused, fused, flops
 
 
+def qk_norm_rope_fp8_kv(tokens: int, q_heads: int, kv_heads: int, head_dim: int,
+                        rope_dim: int, elt: int = 2, cs_elt: int = 2, slot_bytes: int = 8):
+    """QK RMSNorm + RoPE with the FP8 KV-cache write, one kernel: the whole q/k/v
+    row, the weights, the tables and one slot index per token are read; q is
+    written back at its dtype, k and v as one-byte codes plus one fp32 scale per
+    (token, kv head).  FLOPs: 7 per q/k value (as above) and 3 per quantised
+    k/v value (|x|, max, scale)."""
+    qkv = tokens * (q_heads + 2 * kv_heads) * head_dim * elt
+    w = 2 * head_dim * elt
+    tab = tokens * (rope_dim // 2) * cs_elt
+    slots = tokens * slot_bytes
+    q = tokens * q_heads * head_dim * elt
+    codes = 2 * tokens * kv_heads * head_dim
+    scales = 2 * tokens * kv_heads * 4
+    fused = _kernel([qkv, w, tab, tab, slots], [q, codes, scales])
+    flops = (4 * tokens * (q_heads + kv_heads) * head_dim
+             + 3 * tokens * (q_heads + kv_heads) * rope_dim + 3 * codes)
+    return fused, fused, flops
+
+
 def page_scenarios():
     """The five scenarios of the ledger table, with the pages' shapes."""
     return {
@@ -166,6 +186,10 @@ def counted_bytes(cfg: dict) -> int:
     if op == "qk_norm_rope":
         return qk_norm_rope(cfg["tokens"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
                             cfg["rope_dim"], ELT[cfg["dtype"]], ELT[cfg["cs_dtype"]])[1]
+    if op == "qk_kv":
+        return qk_norm_rope_fp8_kv(cfg["tokens"], cfg["q_heads"], cfg["kv_heads"],
+                                   cfg["head_dim"], cfg["rope_dim"], ELT[cfg["dtype"]],
+                                   ELT[cfg["cs_dtype"]])[1]
     if op == "fused":
         n = cfg["heads"] * cfg["head_dim"]
         return rmsnorm_rope_fp8(cfg["tokens"], n, cfg["rope_dim"], ELT[cfg["dtype"]],

@@ -74,6 +74,13 @@ def rope_table(tokens: int, rope_dim: int, dtype: str, base: float = 10000.0):
     return to_storage(np.cos(theta), dtype), to_storage(np.sin(theta), dtype)
 
 
+def cache_slots(seed: int, tokens: int, num_slots: int) -> np.ndarray:
+    """Distinct cache rows for ``tokens`` tokens, drawn uniformly without
+    replacement from ``num_slots`` (a paged cache's scattered free slots)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.choice(num_slots, size=tokens, replace=False).astype(np.int64)
+
+
 # ------------------------------------------------------------------ workloads
 # The five configurations, named by what they are.
 WORKLOADS = {
@@ -91,6 +98,10 @@ WORKLOADS = {
                                                 kv_heads=8, head_dim=128, rope_dim=128,
                                                 dtype="bf16", cs_dtype="bf16", eps=1e-6,
                                                 neox=True, seed=8),
+    "qk_norm_rope_fp8_kv_4096_q32_kv8_d128_bf16": dict(op="qk_kv", tokens=4096, q_heads=32,
+                                                       kv_heads=8, head_dim=128, rope_dim=128,
+                                                       dtype="bf16", cs_dtype="bf16", eps=1e-6,
+                                                       neox=True, num_slots=16384, seed=9),
     "rmsnorm_rope_fp8_4096x4096_bf16": dict(op="fused", tokens=4096, heads=32, head_dim=128,
                                             rope_dim=128, dtype="bf16", cs_dtype="bf16",
                                             eps=1e-6, neox=True, seed=5),
@@ -135,6 +146,16 @@ def make_inputs(name: str, seed: int | None = None, rows: int | None = None) -> 
         kw = normal(s + 2000, (D,), 1.0, 0.1, cfg["dtype"])
         c, sn = rope_table(T, cfg["rope_dim"], cfg["cs_dtype"])
         return dict(cfg, tokens=T, x=x, q_weight=qw, k_weight=kw, cos=c, sin=sn)
+    if op == "qk_kv":
+        T = cfg["tokens"] if rows is None else rows
+        D = cfg["head_dim"]
+        n = (cfg["q_heads"] + 2 * cfg["kv_heads"]) * D
+        x = normal(s, (T, n), 0.0, 1.0, cfg["dtype"])
+        qw = normal(s + 1000, (D,), 1.0, 0.1, cfg["dtype"])
+        kw = normal(s + 2000, (D,), 1.0, 0.1, cfg["dtype"])
+        c, sn = rope_table(T, cfg["rope_dim"], cfg["cs_dtype"])
+        slots = cache_slots(s + 3000, T, cfg["num_slots"])
+        return dict(cfg, tokens=T, x=x, q_weight=qw, k_weight=kw, cos=c, sin=sn, slots=slots)
     if op == "fused":
         T = cfg["tokens"] if rows is None else rows
         n = cfg["heads"] * cfg["head_dim"]

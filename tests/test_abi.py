@@ -192,3 +192,37 @@ def qk(**kw):
 ])
 def test_qk_norm_rope_validation(kw, want):
     assert qk(**kw) == want
+
+
+KC, VC, KS, VS, SL = (ctypes.c_void_p(a << 32) for a in range(8, 13))
+
+
+def qkv_cache(**kw):
+    a = dict(x=X, wq=W, wk=Y, c=C, s=S, kc=KC, vc=VC, ks=KS, vs=VS, sl=SL, ns=64, T=4, Hq=32,
+             Hkv=8, D=128, R=128, xs=6144, cst=1024, dtype=BF16, cs=BF16, neox=1, eps=1e-6)
+    a.update(kw)
+    return qrw.load().qk_norm_rope_fp8_kv_fwd(
+        a["x"], a["wq"], a["wk"], a["c"], a["s"], a["kc"], a["vc"], a["ks"], a["vs"], a["sl"],
+        a["ns"], a["T"], a["Hq"], a["Hkv"], a["D"], a["R"], a["xs"], a["cst"], a["dtype"],
+        a["cs"], a["neox"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(kc=None), NULL), (dict(vs=None), NULL), (dict(c=None), NULL),
+    (dict(dtype=F32), DTYPE), (dict(cs=F16), DTYPE),
+    (dict(Hkv=0, xs=4096), SHAPE), (dict(D=96, xs=4608), SHAPE), (dict(R=8), SHAPE),
+    (dict(ns=-1), SHAPE), (dict(sl=None, ns=3), SHAPE),
+    (dict(xs=6136), STRIDE), (dict(cst=1000), STRIDE), (dict(cst=1028), STRIDE),
+    (dict(kc=ctypes.c_void_p((8 << 32) + 8)), ALIGN), (dict(ks=ctypes.c_void_p((10 << 32) + 2)), ALIGN),
+    (dict(sl=ctypes.c_void_p((12 << 32) + 4)), ALIGN),
+    (dict(eps=-1.0), VALUE), (dict(neox=3), VALUE),
+    (dict(vc=ctypes.c_void_p((8 << 32) + 4096)), ALIAS),     # v cache inside the k cache
+    (dict(ks=ctypes.c_void_p((1 << 32) + 64)), ALIAS),       # scales inside qkv
+    (dict(vs=ctypes.c_void_p((10 << 32) + 16)), ALIAS),      # v scales inside k scales
+    (dict(sl=ctypes.c_void_p((9 << 32) + 256)), ALIAS),      # slots inside the v cache
+    (dict(c=ctypes.c_void_p((8 << 32) + 1024)), ALIAS),      # table inside the k cache
+    (dict(T=0), OK), (dict(T=0, x=None, kc=None, vc=None, ks=None, vs=None, sl=None, ns=0), OK),
+    (dict(T=0, R=24), SHAPE),
+])
+def test_qk_kv_cache_validation(kw, want):
+    assert qkv_cache(**kw) == want
