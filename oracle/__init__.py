@@ -81,6 +81,8 @@ def _load():
                                              i64, i64, i64, i64, i64, i64, i64, i64, i32, i32,
                                              i32, f32]
     L.oracle_qk_norm_rope_fp8_kv.restype = None
+    L.oracle_ew_scale_add.argtypes = [vp, vp, vp, i64, f32, i32, i32]
+    L.oracle_ew_scale_add.restype = None
     _lib = L
     return L
 
@@ -267,3 +269,17 @@ def qk_norm_rope_fp8_kv(x, q_weight, k_weight, cos, sin, q_heads: int, kv_heads:
                                  ns, tokens, q_heads, kv_heads, head_dim, rope_dim, xs, qs, cst,
                                  DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)), eps)
     return q, kc, vc, ksc, vsc
+
+
+def ew_scale_add(x, b, alpha: float, x_dtype: str, y_dtype: str | None = None):
+    """y = round(x * alpha + b) elementwise over flat arrays (b may be None)."""
+    L = _load()
+    x = _check(np.ascontiguousarray(x), x_dtype, "x")
+    b = None if b is None else _check(np.ascontiguousarray(b), x_dtype, "b")
+    if b is not None:
+        assert b.shape == x.shape
+    yd = x_dtype if y_dtype is None else y_dtype
+    y = np.zeros(x.shape, dtype=_STORAGE[yd])
+    L.oracle_ew_scale_add(_ptr(x), _ptr(b), _ptr(y), x.size, alpha, DTYPE_CODE[x_dtype],
+                          DTYPE_CODE[yd])
+    return y

@@ -30,6 +30,9 @@
  *    the binary32 constant the kernels hold; the scale is stored as binary32.
  *  - The fused operator does not round between the norm and the rotation.
  *  - eps enters as the binary32 value the caller passes.
+ *  - The elementwise family computes x * alpha + b with one rounding at the
+ *    output (the fused kernel's fp32 arithmetic, not eager PyTorch's rounding
+ *    after each step).
  *  - The quantised KV-cache write of the QK-norm fusion ([EW] s2.4) uses the
  *    per-token cast with each (token, head) of k and of v as its own group,
  *    k after its norm and rotation (unrounded), v as stored; cache rows are
@@ -554,4 +557,44 @@ void oracle_qk_norm_rope_fp8_kv(const void* x, const void* q_weight, const void*
   }
   free(z);
   free(codes);
+}
+
+/* ------------------------------------------------------------------ */
+/* p + b for doubles, returned ROUNDED TO ODD at double precision: the   */
+/* truncation of the exact sum, with its last bit forced to 1 when the  */
+/* sum is inexact.  A value rounded to odd with at least two more bits  */
+/* than a target format rounds to nearest in that format exactly as the */
+/* exact sum would (Boldo and Melquiond, "Emulation of FMA and correctly */
+/* rounded sums: proved algorithms using rounding to odd", IEEE TC 2008). */
+/* The exact error of the rounded sum comes from Knuth's TwoSum.         */
+/* ------------------------------------------------------------------ */
+static double sum_round_odd(double p, double b) {
+  double s = p + b;
+  if (isinf(s) || isnan(s)) return s;
+  double bv = s - p;
+  double e = (p - (s - bv)) + (b - bv); /* p + b == s + e exactly */
+  if (e == 0.0) return s;
+  /* truncation toward zero of s + e: s itself when e points away from zero */
+  double t = ((s > 0.0) == (e > 0.0)) ? s : nextafter(s, 0.0);
+  uint64_t bits;
+  memcpy(&bits, &t, 8);
+  if ((bits & 1u) == 0) t = nextafter(t, s > 0.0 ? INFINITY : -INFINITY);
+  return t;
+}
+
+/* ------------------------------------------------------------------ */
+/* Elementwise add / scale / cast ([EW] s3.1.1: a + b, and (x * alpha)  */
+/* cast to the output dtype; s1.2's scale+add scenario y = x * a + b):  */
+/*   y_i = round_out(x_i * alpha + b_i)     (b_i = 0 when b is NULL)    */
+/* rounded once from the exact value: the product of two binary32 values */
+/* is exact in double, and the sum is carried rounded to odd.  x and b   */
+/* share x_dtype; y has y_dtype.  Flat arrays of n elements.            */
+/* ------------------------------------------------------------------ */
+void oracle_ew_scale_add(const void* x, const void* b, void* y, int64_t n, float alpha,
+                         int x_dtype, int y_dtype) {
+  for (int64_t i = 0; i < n; ++i) {
+    double v = load_el(x, i, x_dtype) * (double)alpha;
+    if (b) v = sum_round_odd(v, load_el(b, i, x_dtype));
+    store_el(y, i, y_dtype, v);
+  }
 }
