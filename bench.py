@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_kv": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
+    "ew": ("qrw_ew.hip", "qrw_device.h", "qrw_launch.h"),
 }
 
 
@@ -130,7 +131,8 @@ class Workload:
         code = {"f16": 1, "bf16": 2, "f32": 3}
         base = {k: up(v, self.cfg.get("cs_dtype", dt) if k in ("cos", "sin") else dt)
                 for k, v in self.inp.items()
-                if k in ("x", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight", "slots")}
+                if k in ("x", "b", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight",
+                         "slots")}
         self.sets = []
         for _ in range(sets):
             s = {k: v.clone() for k, v in base.items()}
@@ -144,6 +146,9 @@ class Workload:
                 n = self.cfg["heads"] * self.cfg["head_dim"]
                 s["q"] = torch.empty((T, n), dtype=torch.uint8, device=dev)
                 s["scales"] = torch.empty((T,), dtype=torch.float32, device=dev)
+            elif op == "ew":
+                yd = self.cfg.get("y_dtype", dt)
+                s["y"] = torch.empty(s["x"].shape, dtype=tdt[yd], device=dev)
             elif op == "qk_kv":
                 ns, kvn = self.cfg["num_slots"], self.cfg["kv_heads"] * self.cfg["head_dim"]
                 for k in ("k_cache", "v_cache"):
@@ -185,6 +190,18 @@ class Workload:
                                            c["kv_heads"], D, c["rope_dim"], n,
                                            self.code[c["dtype"]], self.code[c["cs_dtype"]],
                                            int(c["neox"]), c["eps"], st)
+        elif self.op == "ew":
+            n = c["n"]
+            if c["kind"] == "add":
+                rc = self.lib.ew_add_fwd(p(s["x"]), p(s["b"]), p(s["y"]), n,
+                                         self.code[c["dtype"]], st)
+            elif c["kind"] == "scale_add":
+                rc = self.lib.ew_scale_add_fwd(p(s["x"]), p(s["b"]), p(s["y"]), n, c["alpha"],
+                                               self.code[c["dtype"]], st)
+            else:
+                rc = self.lib.ew_scale_cast_fwd(p(s["x"]), p(s["y"]), n, c["alpha"],
+                                                self.code[c["dtype"]],
+                                                self.code[c.get("y_dtype", c["dtype"])], st)
         elif self.op == "qk_kv":
             T, D = c["tokens"], c["head_dim"]
             n = (c["q_heads"] + 2 * c["kv_heads"]) * D
@@ -268,15 +285,37 @@ def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
 
 
 # ---------------------------------------------------------------- CPU side
+def compute_dtype(cfg: dict) -> str:
+    """The arithmetic type of the kernel: binary32, except the elementwise family's
+    16-bit outputs, which are formed in binary64."""
+    if cfg["op"] == "ew" and cfg.get("y_dtype", cfg["dtype"]) != "f32":
+        return "f64"
+    return "f32"
+
+
+def op_of(name: str) -> str:
+    from quant_row_workgroup_amd import synth
+
+    return synth.WORKLOADS[name]["op"]
+
+
+def full_rows(name: str) -> int:
+    from quant_row_workgroup_amd import synth
+
+    c = synth.WORKLOADS[name]
+    return c.get("tokens", c.get("rows", c.get("n")))
+
+
 def cpu_baseline(name: str, seconds: float):
     import oracle
     from quant_row_workgroup_amd import ledger, synth
 
-    rows = 256
+    rows = 1 << 16 if op_of(name) == "ew" else 256
     inp = synth.make_inputs(name, rows=rows)
     cfg = dict(synth.WORKLOADS[name])
     op = cfg["op"]
-    key = "tokens" if op in ("rope", "fused", "qk_norm_rope", "qk_kv") else "rows"
+    key = {"rope": "tokens", "fused": "tokens", "qk_norm_rope": "tokens", "qk_kv": "tokens",
+           "ew": "n"}.get(op, "rows")
     cfg[key] = rows
     bytes_per_call = ledger.counted_bytes(cfg)
 
@@ -287,6 +326,10 @@ def cpu_baseline(name: str, seconds: float):
                                     cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "act_quant":
             oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
+        elif op == "ew":
+            alpha = 1.0 if cfg["kind"] == "add" else cfg["alpha"]
+            oracle.ew_scale_add(inp["x"], inp.get("b"), alpha, cfg["dtype"],
+                                cfg.get("y_dtype", cfg["dtype"]))
         elif op == "qk_kv":
             oracle.qk_norm_rope_fp8_kv(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
                                        inp["sin"], cfg["q_heads"], cfg["kv_heads"],
@@ -321,8 +364,8 @@ def cpu_baseline(name: str, seconds: float):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{rows} of {synth.WORKLOADS[name].get('tokens', synth.WORKLOADS[name].get('rows'))} "
-                   f"rows of the same workload, {reps} calls in {el:.1f} s, single-threaded "
+        "sample": (f"{rows} of {full_rows(name)} "
+                   f"{'elements' if op == 'ew' else 'rows'} of the same workload, {reps} calls in {el:.1f} s, single-threaded "
                    f"float64 C checker on {cpu_model()} ({os.cpu_count()} logical CPUs present)"),
     }
 
@@ -402,7 +445,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": compute_dtype(wl.cfg),
         "data": "synthetic",
         "config": cfg,
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),

@@ -10,6 +10,7 @@
  *   s3.3.2  reference RoPE (fp32 math, one final cast)
  *   s3.1.5  per-token / per-group FP8 cast (amax -> scale -> clamp -> cast)
  *   s3.3.4  the fused RMSNorm + RoPE + per-token quantisation operator
+ *   s3.1.1  elementwise add / scale / cast; s1.2 the scale+add scenario
  *   s2.4    cross-module fusion: per-head q/k RMSNorm + RoPE, v untouched, and
  *           the variant that writes k and v to an FP8 KV cache
  *
@@ -193,6 +194,25 @@ int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weigh
                             int64_t head_dim, int64_t rope_dim, int64_t token_stride,
                             int64_t cache_stride, int dtype, int cs_dtype, int neox, float eps,
                             void* stream);
+
+/*
+ * Elementwise family (s3.1.1: a + b and (x * alpha) cast to another dtype;
+ * s1.2: the scale+add scenario y = x * a + b).  Flat arrays of n elements
+ * (any n >= 0; no multiple-of-8 requirement), 16-byte aligned, F16, BF16 or
+ * F32.  Each output is x * alpha + b rounded once, nearest-even, to y's
+ * dtype (a float32 fma for float32 outputs; for 16-bit outputs a float64 fma
+ * carried to the cast without a second rounding).  y may be exactly x (or b) when it
+ * has the same dtype (in place); any other overlap of y with an input is
+ * QRW_ERR_ALIAS.
+ *   ew_add_fwd:        y = a + b              (a, b, y: dtype)
+ *   ew_scale_cast_fwd: y = (x * alpha)        (x: x_dtype, y: y_dtype)
+ *   ew_scale_add_fwd:  y = x * alpha + b      (x, b, y: dtype)
+ */
+int ew_add_fwd(const void* a, const void* b, void* y, int64_t n, int dtype, void* stream);
+int ew_scale_cast_fwd(const void* x, void* y, int64_t n, float alpha, int x_dtype, int y_dtype,
+                      void* stream);
+int ew_scale_add_fwd(const void* x, const void* b, void* y, int64_t n, float alpha, int dtype,
+                     void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* qrw_status_string(int status);

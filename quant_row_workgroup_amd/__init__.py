@@ -13,6 +13,9 @@ from ._binding import (  # noqa: F401
     QrwError,
     act_quant_fp8_fwd,
     layernorm_fwd,
+    ew_add_fwd,
+    ew_scale_add_fwd,
+    ew_scale_cast_fwd,
     load,
     qk_norm_rope_fp8_kv_fwd,
     qk_norm_rope_fwd,

@@ -28,7 +28,7 @@ STATUS = {
 
 EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
            "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qk_norm_rope_fwd",
-           "qk_norm_rope_fp8_kv_fwd",
+           "qk_norm_rope_fp8_kv_fwd", "ew_add_fwd", "ew_scale_cast_fwd", "ew_scale_add_fwd",
            "qrw_status_string")
 
 
@@ -61,6 +61,9 @@ def load():
     L.act_quant_fp8_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     L.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32,
                                    i32, f32, vp]
+    L.ew_add_fwd.argtypes = [vp, vp, vp, i64, i32, vp]
+    L.ew_scale_cast_fwd.argtypes = [vp, vp, i64, f32, i32, i32, vp]
+    L.ew_scale_add_fwd.argtypes = [vp, vp, vp, i64, f32, i32, vp]
     L.qk_norm_rope_fp8_kv_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                           i64, i64, i64, i64, i64, i32, i32, i32, f32, vp]
     for name in EXPORTS[:-1]:
@@ -250,3 +253,41 @@ def qk_norm_rope_fp8_kv_fwd(qkv, q_weight, k_weight, cos, sin, k_cache, v_cache,
         _stream(qkv))
     _check("qk_norm_rope_fp8_kv_fwd", st)
     return qkv
+
+
+def _flat(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def ew_add_fwd(a, b, out=None):
+    """out = a + b (same shape and dtype), one rounding from fp32."""
+    if a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("a and b must have the same shape and dtype")
+    y = torch.empty_like(a) if out is None else out
+    st = load().ew_add_fwd(_ptr(_flat(a, "a")), _ptr(_flat(b, "b")), _ptr(_flat(y, "out")),
+                           a.numel(), _dtype(a), _stream(a))
+    _check("ew_add_fwd", st)
+    return y
+
+
+def ew_scale_cast_fwd(x, alpha: float, out_dtype=None, out=None):
+    """out = (x * alpha) cast to ``out_dtype`` (default: x's dtype)."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    st = load().ew_scale_cast_fwd(_ptr(_flat(x, "x")), _ptr(_flat(out, "out")), x.numel(), alpha,
+                                  _dtype(x), _dtype(out), _stream(x))
+    _check("ew_scale_cast_fwd", st)
+    return out
+
+
+def ew_scale_add_fwd(x, b, alpha: float, out=None):
+    """out = x * alpha + b (same shape and dtype)."""
+    if x.shape != b.shape or x.dtype != b.dtype:
+        raise ValueError("x and b must have the same shape and dtype")
+    y = torch.empty_like(x) if out is None else out
+    st = load().ew_scale_add_fwd(_ptr(_flat(x, "x")), _ptr(_flat(b, "b")), _ptr(_flat(y, "out")),
+                                 x.numel(), alpha, _dtype(x), _stream(x))
+    _check("ew_scale_add_fwd", st)
+    return y

@@ -70,6 +70,31 @@ int check_heads(int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_di
 
 int finish(hipError_t e) { return e == hipSuccess ? QRW_OK : QRW_ERR_LAUNCH; }
 
+bool is_dtype(int dtype) { return dtype == QRW_F16 || dtype == QRW_BF16 || dtype == QRW_F32; }
+int64_t elt_size(int dtype) { return dtype == QRW_F32 ? 4 : 2; }
+
+constexpr int64_t kMaxFlat = (int64_t)1 << 40;
+
+// The elementwise family: y may be x (or b) exactly when it has the same dtype
+// (each element is read before the same lane writes it); any other overlap of
+// an output with an input is refused.
+int ew_checked(const void* x, const void* b, void* y, int64_t n, float alpha, int x_dtype,
+               int y_dtype, void* stream) {
+  if (!is_dtype(x_dtype) || !is_dtype(y_dtype)) return QRW_ERR_DTYPE;
+  if (n < 0 || n > kMaxFlat) return QRW_ERR_SHAPE;
+  if (n == 0) return QRW_OK;
+  if (!x || !y) return QRW_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (b && !aligned16(b))) return QRW_ERR_ALIGN;
+  const Span ys = span_of(y, 1, n, 0, elt_size(y_dtype));
+  for (const void* in : {x, b}) {
+    if (!in) continue;
+    if (in == y && x_dtype == y_dtype) continue;
+    if (overlap(span_of(in, 1, n, 0, elt_size(x_dtype)), ys)) return QRW_ERR_ALIAS;
+  }
+  return finish(qrw::launch_ew(x, b, y, n, alpha, x_dtype, y_dtype,
+                               static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,6 +321,22 @@ int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weigh
       qkv, q_weight, k_weight, cos, sin, k_cache, v_cache, k_scales, v_scales, slots, num_slots,
       tokens, q_heads, kv_heads, head_dim, rope_dim, token_stride, cache_stride, dtype, cs_dtype,
       neox == 1, eps, static_cast<hipStream_t>(stream)));
+}
+
+int ew_add_fwd(const void* a, const void* b, void* y, int64_t n, int dtype, void* stream) {
+  if (n > 0 && !b) return QRW_ERR_NULL;
+  return ew_checked(a, b, y, n, 1.0f, dtype, dtype, stream);
+}
+
+int ew_scale_cast_fwd(const void* x, void* y, int64_t n, float alpha, int x_dtype, int y_dtype,
+                      void* stream) {
+  return ew_checked(x, nullptr, y, n, alpha, x_dtype, y_dtype, stream);
+}
+
+int ew_scale_add_fwd(const void* x, const void* b, void* y, int64_t n, float alpha, int dtype,
+                     void* stream) {
+  if (n > 0 && !b) return QRW_ERR_NULL;
+  return ew_checked(x, b, y, n, alpha, dtype, dtype, stream);
 }
 
 const char* qrw_status_string(int status) {

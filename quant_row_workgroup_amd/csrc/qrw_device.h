@@ -36,6 +36,9 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+__device__ __forceinline__ u32x2 ld8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 __device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }

@@ -48,6 +48,9 @@ hipError_t launch_qk_norm_rope_fp8_kv(void* qkv, const void* q_weight, const voi
                                       int dtype, int cs_dtype, bool neox, float eps,
                                       hipStream_t stream);
 
+hipError_t launch_ew(const void* x, const void* b, void* y, int64_t n, float alpha, int x_dtype,
+                     int y_dtype, hipStream_t stream);
+
 // Number of "items" (pairs of granules) one token of the fused operator holds.
 int64_t fused_items(int64_t heads, int64_t head_dim, int64_t rope_dim);
 

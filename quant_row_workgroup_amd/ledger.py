@@ -154,6 +154,13 @@ def qk_norm_rope_fp8_kv(tokens: int, q_heads: int, kv_heads: int, head_dim: int,
     return fused, fused, flops
 
 
+def elementwise(n: int, x_elt: int, y_elt: int, has_b: bool):
+    """One elementwise kernel over n elements: x (and b, at x's dtype) read once,
+    y written once.  FLOPs: one multiply (and one add) per element."""
+    fused = _kernel([n * x_elt] + ([n * x_elt] if has_b else []), [n * y_elt])
+    return fused, fused, (2 if has_b else 1) * n
+
+
 def page_scenarios():
     """The five scenarios of the ledger table, with the pages' shapes."""
     return {
@@ -186,6 +193,9 @@ def counted_bytes(cfg: dict) -> int:
     if op == "qk_norm_rope":
         return qk_norm_rope(cfg["tokens"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
                             cfg["rope_dim"], ELT[cfg["dtype"]], ELT[cfg["cs_dtype"]])[1]
+    if op == "ew":
+        return elementwise(cfg["n"], ELT[cfg["dtype"]], ELT[cfg.get("y_dtype", cfg["dtype"])],
+                           cfg["kind"] != "scale_cast")[1]
     if op == "qk_kv":
         return qk_norm_rope_fp8_kv(cfg["tokens"], cfg["q_heads"], cfg["kv_heads"],
                                    cfg["head_dim"], cfg["rope_dim"], ELT[cfg["dtype"]],

@@ -84,6 +84,11 @@ def cache_slots(seed: int, tokens: int, num_slots: int) -> np.ndarray:
 # ------------------------------------------------------------------ workloads
 # The five configurations, named by what they are.
 WORKLOADS = {
+    "scale_add_1M_f32": dict(op="ew", kind="scale_add", n=1 << 20, dtype="f32", alpha=0.5,
+                             seed=10),
+    "add_16M_bf16": dict(op="ew", kind="add", n=1 << 24, dtype="bf16", seed=11),
+    "scale_cast_16M_f32_to_f16": dict(op="ew", kind="scale_cast", n=1 << 24, dtype="f32",
+                                      y_dtype="f16", alpha=0.5, seed=12),
     "rmsnorm_256x1024_f16": dict(op="rmsnorm", rows=256, n=1024, dtype="f16", eps=1e-6, seed=1),
     "rmsnorm_4096x4096_f16": dict(op="rmsnorm", rows=4096, n=4096, dtype="f16", eps=1e-6, seed=2),
     "layernorm_4096x4096_bf16": dict(op="layernorm", rows=4096, n=4096, dtype="bf16", eps=1e-5,
@@ -146,6 +151,13 @@ def make_inputs(name: str, seed: int | None = None, rows: int | None = None) -> 
         kw = normal(s + 2000, (D,), 1.0, 0.1, cfg["dtype"])
         c, sn = rope_table(T, cfg["rope_dim"], cfg["cs_dtype"])
         return dict(cfg, tokens=T, x=x, q_weight=qw, k_weight=kw, cos=c, sin=sn)
+    if op == "ew":
+        n = cfg["n"] if rows is None else rows
+        x = normal(s, (n,), 0.0, 1.0, cfg["dtype"])
+        out = dict(cfg, n=n, x=x)
+        if cfg["kind"] != "scale_cast":
+            out["b"] = normal(s + 1000, (n,), 0.0, 1.0, cfg["dtype"])
+        return out
     if op == "qk_kv":
         T = cfg["tokens"] if rows is None else rows
         D = cfg["head_dim"]

@@ -226,3 +226,25 @@ def qkv_cache(**kw):
 ])
 def test_qk_kv_cache_validation(kw, want):
     assert qkv_cache(**kw) == want
+
+
+@pytest.mark.parametrize("call,want", [
+    (lambda L: L.ew_add_fwd(X, None, Y, 16, BF16, None), NULL),
+    (lambda L: L.ew_add_fwd(None, W, Y, 16, BF16, None), NULL),
+    (lambda L: L.ew_add_fwd(X, W, Y, 16, 4, None), DTYPE),
+    (lambda L: L.ew_add_fwd(X, W, Y, -1, BF16, None), SHAPE),
+    (lambda L: L.ew_add_fwd(X, W, Y, (1 << 40) + 1, BF16, None), SHAPE),
+    (lambda L: L.ew_add_fwd(X, W, ctypes.c_void_p((2 << 32) + 8), 16, BF16, None), ALIGN),
+    (lambda L: L.ew_add_fwd(X, W, ctypes.c_void_p((1 << 32) + 16), 16, BF16, None), ALIAS),
+    (lambda L: L.ew_add_fwd(X, W, Y, 0, BF16, None), OK),
+    (lambda L: L.ew_add_fwd(None, None, None, 0, BF16, None), OK),
+    (lambda L: L.ew_scale_cast_fwd(X, Y, 16, 0.5, F32, 0, None), DTYPE),
+    (lambda L: L.ew_scale_cast_fwd(X, None, 16, 0.5, F32, F16, None), NULL),
+    (lambda L: L.ew_scale_cast_fwd(X, X, 16, 0.5, F32, F16, None), ALIAS),  # in place needs one dtype
+    (lambda L: L.ew_scale_cast_fwd(X, ctypes.c_void_p((1 << 32) + 32), 64, 0.5, F16, F16, None), ALIAS),
+    (lambda L: L.ew_scale_add_fwd(X, None, Y, 16, 0.5, F32, None), NULL),
+    (lambda L: L.ew_scale_add_fwd(X, ctypes.c_void_p((3 << 32) + 4), Y, 16, 0.5, F32, None), ALIGN),
+    (lambda L: L.ew_scale_add_fwd(X, ctypes.c_void_p((2 << 32) + 16), Y, 64, 0.5, F32, None), ALIAS),
+])
+def test_elementwise_validation(call, want):
+    assert call(qrw.load()) == want
