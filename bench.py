@@ -133,6 +133,13 @@ class Workload:
                 for k, v in self.inp.items()
                 if k in ("x", "b", "w", "gamma", "beta", "cos", "sin", "q_weight", "k_weight",
                          "slots")}
+        if op in ("rmsnorm", "layernorm") and self.cfg["n"] % 8:
+            # rows stored padded to a multiple of 8 elements (16-byte aligned rows)
+            n = self.cfg["n"]
+            wide = torch.zeros((self.cfg["rows"], (n + 7) // 8 * 8), dtype=base["x"].dtype,
+                               device=dev)
+            wide[:, :n] = base["x"]
+            base["x"] = wide
         self.sets = []
         for _ in range(sets):
             s = {k: v.clone() for k, v in base.items()}
@@ -216,12 +223,13 @@ class Workload:
             rc = self.lib.act_quant_fp8_fwd(p(s["x"]), p(s["q"]), p(s["scales"]), c["rows"],
                                             c["n"], g, c["n"], c["n"], self.code[c["dtype"]], st)
         elif self.op == "rmsnorm":
-            rc = self.lib.rmsnorm_fwd(p(s["x"]), p(s["w"]), p(s["y"]), c["rows"], c["n"], c["n"],
-                                      c["n"], self.code[c["dtype"]], c["eps"], st)
+            rc = self.lib.rmsnorm_fwd(p(s["x"]), p(s["w"]), p(s["y"]), c["rows"], c["n"],
+                                      s["x"].stride(0), s["y"].stride(0), self.code[c["dtype"]],
+                                      c["eps"], st)
         elif self.op == "layernorm":
             rc = self.lib.layernorm_fwd(p(s["x"]), p(s["gamma"]), p(s["beta"]), p(s["y"]),
-                                        c["rows"], c["n"], c["n"], c["n"], self.code[c["dtype"]],
-                                        c["eps"], st)
+                                        c["rows"], c["n"], s["x"].stride(0), s["y"].stride(0),
+                                        self.code[c["dtype"]], c["eps"], st)
         else:
             T, H, D, R = c["tokens"], c["heads"], c["head_dim"], c["rope_dim"]
             fn = self.lib.rope_apply_neox if c.get("neox", True) else self.lib.rope_apply_interleaved

@@ -64,14 +64,27 @@ enum qrw_status {
   QRW_ERR_VALUE = -8    /* a scalar argument is out of range (eps negative or not finite) */
 };
 
-/* Largest row length, in elements, that one call handles (8192). */
+/* Largest row length, in elements, of the RoPE, fused and quantisation calls
+ * (8192). */
 #define QRW_MAX_ROW 8192
+/* Largest row of rmsnorm_fwd / layernorm_fwd kept in registers (65536); a
+ * longer RMSNorm row takes two passes over x (s3.2.4), up to
+ * QRW_MAX_ROW_SPLIT. */
+#define QRW_MAX_ROW_RESIDENT 65536
+#define QRW_MAX_ROW_SPLIT (1 << 26)
 
 /*
  * RMSNorm forward (s3.2.1):
  *   rstd_r = 1 / sqrt( (1/n) * sum_j x[r,j]^2 + eps )
  *   y[r,j] = x[r,j] * rstd_r * weight[j]          (weight == NULL: weight = 1)
- * x, y: [rows, n] with row strides x_row_stride / y_row_stride (elements).
+ * x, y: [rows, n] with row strides x_row_stride / y_row_stride (elements,
+ * multiples of 8, so every row starts 16-byte aligned).  Any 1 <= n <=
+ * QRW_MAX_ROW_SPLIT: a row whose length is not a multiple of 8 ends in a
+ * partial granule that is read and written element by element (columns at
+ * and past n are never touched; the padding counts as zero and the mean
+ * divides by n, s5.4).  Rows up to QRW_MAX_ROW_RESIDENT are read once; longer
+ * rows are read twice (sum of squares, then the output in reverse chunk
+ * order, s3.2.4).
  * weight: [n], packed, same dtype, or NULL.
  * y == x (same stride) computes in place; any other overlap is QRW_ERR_ALIAS.
  */
@@ -83,7 +96,8 @@ int rmsnorm_fwd(const void* x, const void* weight, void* y, int64_t rows, int64_
  * LayerNorm forward (s3.2.1, torch.nn.functional.layer_norm semantics):
  *   mu_r = (1/n) sum_j x[r,j];   var_r = (1/n) sum_j (x[r,j] - mu_r)^2  (biased)
  *   y[r,j] = (x[r,j] - mu_r) / sqrt(var_r + eps) * gamma[j] + beta[j]
- * gamma / beta: [n] or NULL (1 and 0).  Layout and aliasing as rmsnorm_fwd.
+ * gamma / beta: [n] or NULL (1 and 0).  Layout and aliasing as rmsnorm_fwd,
+ * for 1 <= n <= QRW_MAX_ROW_RESIDENT (one read of x).
  */
 int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
                   int64_t n, int64_t x_row_stride, int64_t y_row_stride, int dtype,

@@ -111,10 +111,15 @@ def _vec(t, n, name):
 
 
 # ------------------------------------------------------------------ entry points
+def _new_rows(rows, n, like):
+    """A [rows, n] output whose rows start 16-byte aligned (stride padded to 8)."""
+    return torch.empty((rows, (n + 7) // 8 * 8), dtype=like.dtype, device=like.device)[:, :n]
+
+
 def rmsnorm_fwd(x, weight=None, eps: float = 1e-6, out=None):
     """RMSNorm over the last dim of 2-D ``x``; returns ``out``."""
     rows, n, xs = _rows(x, "x")
-    out = torch.empty((rows, n), dtype=x.dtype, device=x.device) if out is None else out
+    out = _new_rows(rows, n, x) if out is None else out
     _, _, ys = _rows(out, "out")
     st = load().rmsnorm_fwd(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(out), rows, n, xs,
                             ys, _dtype(x), eps, _stream(x))
@@ -124,7 +129,7 @@ def rmsnorm_fwd(x, weight=None, eps: float = 1e-6, out=None):
 
 def layernorm_fwd(x, gamma=None, beta=None, eps: float = 1e-5, out=None):
     rows, n, xs = _rows(x, "x")
-    out = torch.empty((rows, n), dtype=x.dtype, device=x.device) if out is None else out
+    out = _new_rows(rows, n, x) if out is None else out
     _, _, ys = _rows(out, "out")
     st = load().layernorm_fwd(_ptr(x), _ptr(_vec(gamma, n, "gamma")),
                               _ptr(_vec(beta, n, "beta")), _ptr(out), rows, n, xs, ys,

@@ -50,10 +50,13 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
 // Shape, dtype and scalar checks of a row operator (pointers are checked
 // separately, after the empty case: a zero-row tensor may have no storage).
-int check_row_shape(int64_t rows, int64_t n, int64_t xs, int64_t ys, int dtype, float eps) {
+int check_row_shape(int64_t rows, int64_t n, int64_t max_n, int64_t xs, int64_t ys, int dtype,
+                    float eps) {
   if (!is_16bit(dtype)) return QRW_ERR_DTYPE;
-  if (rows < 0 || n < 8 || n % 8 != 0 || n > QRW_MAX_ROW) return QRW_ERR_SHAPE;
-  if (rows > (int64_t)0x7FFFFFFF * 4) return QRW_ERR_SHAPE;  // grid.x limit
+  if (rows < 0 || n < 1 || n > max_n) return QRW_ERR_SHAPE;
+  // grid.x limit: four rows per workgroup, or one row per workgroup for long rows
+  if (rows > (n > 8 * qrw::kOneWaveGranules ? (int64_t)0x7FFFFFFF : (int64_t)0x7FFFFFFF * 4))
+    return QRW_ERR_SHAPE;
   if (xs < n || ys < n || xs % 8 != 0 || ys % 8 != 0) return QRW_ERR_STRIDE;
   if (!eps_ok(eps)) return QRW_ERR_VALUE;
   return QRW_OK;
@@ -102,7 +105,7 @@ extern "C" {
 int rmsnorm_fwd(const void* x, const void* weight, void* y, int64_t rows, int64_t n,
                 int64_t x_row_stride, int64_t y_row_stride, int dtype, float eps,
                 void* stream) {
-  int st = check_row_shape(rows, n, x_row_stride, y_row_stride, dtype, eps);
+  int st = check_row_shape(rows, n, QRW_MAX_ROW_SPLIT, x_row_stride, y_row_stride, dtype, eps);
   if (st != QRW_OK) return st;
   if (rows == 0) return QRW_OK;
   if (!x || !y) return QRW_ERR_NULL;
@@ -118,7 +121,7 @@ int rmsnorm_fwd(const void* x, const void* weight, void* y, int64_t rows, int64_
 int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
                   int64_t n, int64_t x_row_stride, int64_t y_row_stride, int dtype, float eps,
                   void* stream) {
-  int st = check_row_shape(rows, n, x_row_stride, y_row_stride, dtype, eps);
+  int st = check_row_shape(rows, n, QRW_MAX_ROW_RESIDENT, x_row_stride, y_row_stride, dtype, eps);
   if (st != QRW_OK) return st;
   if (rows == 0) return QRW_OK;
   if (!x || !y) return QRW_ERR_NULL;

@@ -46,6 +46,25 @@ __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// The first `cnt` (0..8) 16-bit elements at p as one granule, the rest zero;
+// nothing at or past p + cnt is read.  (A row's partial last granule: its
+// padding contributes zero to every sum.)
+__device__ __forceinline__ u32x4 ld_partial(const uint16_t* p, int cnt) {
+  uint32_t e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) e[k] = k < cnt ? (uint32_t)p[k] : 0u;
+  return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                 e[6] | (e[7] << 16)};
+}
+// Store the first `cnt` (0..8) elements of a granule; nothing past p + cnt is
+// written.
+__device__ __forceinline__ void st_partial(uint16_t* p, u32x4 g, int cnt) {
+  const uint32_t d[4] = {g[0], g[1], g[2], g[3]};
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < cnt) p[k] = (uint16_t)((k & 1) ? (d[k >> 1] >> 16) : (d[k >> 1] & 0xFFFFu));
+}
+
 // ------------------------------------------------------- element formats
 struct F16 {
   static __device__ __forceinline__ float lo(uint32_t u) {

@@ -12,6 +12,12 @@ namespace qrw {
 constexpr int kBlock = 256;
 constexpr int kRowsPerBlock = kBlock / 64;
 
+// Row lengths of the norm kernels, in 16-byte granules: one wave holds up to
+// 1024 granules (8192 elements) in registers, a workgroup of 16 waves up to
+// 8192 (65536 elements); longer RMSNorm rows take the two-pass kernel.
+constexpr int kOneWaveGranules = 1024;
+constexpr int kResidentGranules = 8192;
+
 hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t n,
                           int64_t xs, int64_t ys, int dtype, float eps, hipStream_t stream);
 

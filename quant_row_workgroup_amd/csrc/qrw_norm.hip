@@ -22,12 +22,37 @@
 
 namespace qrw {
 
-template <typename T, int GPL, bool FULL>
+// The valid elements of granule gi of a row of n elements: 8, except in the
+// partial last granule of a row whose length is not a multiple of 8 (TAIL).
+template <bool TAIL>
+__device__ __forceinline__ int granule_count(int gi, int n) {
+  if constexpr (TAIL) return min(max(n - 8 * gi, 0), 8);
+  return 8;
+}
+template <bool TAIL>
+__device__ __forceinline__ u32x4 ld_row(const uint16_t* p, int gi, int n) {
+  if (TAIL && 8 * gi + 8 > n) return ld_partial(p + 8 * gi, n - 8 * gi);
+  return ld16(p + 8 * gi);
+}
+template <bool TAIL>
+__device__ __forceinline__ u32x4 ld_row_stream(const uint16_t* p, int gi, int n) {
+  if (TAIL && 8 * gi + 8 > n) return ld_partial(p + 8 * gi, n - 8 * gi);
+  return ld16_stream(p + 8 * gi);
+}
+template <bool TAIL>
+__device__ __forceinline__ void st_row_stream(uint16_t* p, int gi, int n, u32x4 g) {
+  if (TAIL && 8 * gi + 8 > n)
+    st_partial(p + 8 * gi, g, n - 8 * gi);
+  else
+    st16_stream(p + 8 * gi, g);
+}
+
+template <typename T, int GPL, bool FULL, bool TAIL>
 __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
                                                          const uint16_t* __restrict__ w,
                                                          uint16_t* y, int64_t rows, int ng,
-                                                         int64_t xs, int64_t ys, float n_f,
-                                                         float eps) {
+                                                         int n, int64_t xs, int64_t ys,
+                                                         float n_f, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // wave-uniform
@@ -40,14 +65,14 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (FULL || gi < ng) raw[g] = ld16(xr + 8 * gi);
+    if (FULL || gi < ng) raw[g] = ld_row<TAIL>(xr, gi, n);
   }
   if (w) {
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave + lane;
       wr[g] = (u32x4){0u, 0u, 0u, 0u};
-      if (FULL || gi < ng) wr[g] = ld16(w + 8 * gi);
+      if (FULL || gi < ng) wr[g] = ld_row<TAIL>(w, gi, n);
     }
   }
 
@@ -77,18 +102,18 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
       }
-      st16_stream(yr + 8 * gi, narrow8<T>(v));
+      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
     }
   }
 }
 
-template <typename T, int GPL, bool FULL>
+template <typename T, int GPL, bool FULL, bool TAIL>
 __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
                                                            const uint16_t* __restrict__ gam,
                                                            const uint16_t* __restrict__ bet,
                                                            uint16_t* y, int64_t rows, int ng,
-                                                           int64_t xs, int64_t ys, float n_f,
-                                                           float eps) {
+                                                           int n, int64_t xs, int64_t ys,
+                                                           float n_f, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -100,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (FULL || gi < ng) raw[g] = ld16_stream(xr + 8 * gi);
+    if (FULL || gi < ng) raw[g] = ld_row_stream<TAIL>(xr, gi, n);
   }
 
   // Mean in two parts: mu0 is the binary32 mean; the mean r of the residuals
@@ -127,9 +152,10 @@ __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
     if (FULL || gi < ng) {
       float v[8];
       widen8<T>(raw[g], v);
+      const int cnt = granule_count<TAIL>(gi, n);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float d = v[k] - mu0;
+        const float d = k < cnt ? v[k] - mu0 : 0.0f;  // the padding is not centred
         acc1[k] += d;
         acc2[k] = fmaf(d, d, acc2[k]);
       }
@@ -147,20 +173,221 @@ __global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
       float v[8], gv[8], bv[8];
       widen8<T>(raw[g], v);
       if (gam) {
-        widen8<T>(ld16(gam + 8 * gi), gv);
+        widen8<T>(ld_row<TAIL>(gam, gi, n), gv);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) gv[k] = 1.0f;
       }
       if (bet) {
-        widen8<T>(ld16(bet + 8 * gi), bv);
+        widen8<T>(ld_row<TAIL>(bet, gi, n), bv);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = fmaf(((v[k] - mu0) - r) * rstd, gv[k], bv[k]);
-      st16_stream(yr + 8 * gi, narrow8<T>(v));
+      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
+    }
+  }
+}
+
+// ------------------------------------------------------ rows of many waves
+// Rows longer than one wave holds (8192 elements) stay register-resident in a
+// workgroup of W waves (s3.2.3's design with a wider tile): thread t owns
+// granules t, t + 64W, t + 128W, ...  Row statistics: each wave's DPP sum is
+// left in an LDS slot per wave, and after one barrier every lane adds the W
+// slots in a fixed pairwise order (s3.2's two-level reduction: in-thread, then
+// across threads, with a per-wave workspace).
+
+// Sum of v over the workgroup's W waves; every lane gets the same value.
+template <int W>
+__device__ __forceinline__ float block_sum(float v, float* slot) {
+  const float ws = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) slot[threadIdx.x >> 6] = ws;
+  __syncthreads();
+  float s[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) s[i] = slot[i];
+#pragma unroll
+  for (int h = W / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i) s[i] += s[i + h];
+  return s[0];
+}
+
+template <typename T, int W, int GPL, bool TAIL>
+__global__ __launch_bounds__(kWave* W) void rmsnorm_rowblock_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int ng, int n, int64_t xs,
+    int64_t ys, float n_f, float eps) {
+  __shared__ float slot[W];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * xs;
+  uint16_t* yr = y + row * ys;
+  u32x4 raw[GPL];
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    raw[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (gi < ng) raw[g] = ld_row<TAIL>(xr, gi, n);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    float v[8];
+    widen8<T>(raw[g], v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+  }
+  const float ss = block_sum<W>(tree8(acc), slot);
+  const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    if (gi < ng) {
+      float v[8];
+      widen8<T>(raw[g], v);
+      if (w) {
+        float wv[8];
+        widen8<T>(ld_row<TAIL>(w, gi, n), wv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
+      }
+      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
+    }
+  }
+}
+
+template <typename T, int W, int GPL, bool TAIL>
+__global__ __launch_bounds__(kWave* W) void layernorm_rowblock_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
+    uint16_t* y, int ng, int n, int64_t xs, int64_t ys, float n_f, float eps) {
+  __shared__ float slot0[W], slot1[W], slot2[W];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * xs;
+  uint16_t* yr = y + row * ys;
+  u32x4 raw[GPL];
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    raw[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (gi < ng) raw[g] = ld_row_stream<TAIL>(xr, gi, n);
+  }
+  // the same two-part mean as the one-wave kernel
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    float v[8];
+    widen8<T>(raw[g], v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += v[k];
+  }
+  const float mu0 = block_sum<W>(tree8(acc), slot0) / n_f;
+  float acc1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    if (gi < ng) {
+      float v[8];
+      widen8<T>(raw[g], v);
+      const int cnt = granule_count<TAIL>(gi, n);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float d = k < cnt ? v[k] - mu0 : 0.0f;
+        acc1[k] += d;
+        acc2[k] = fmaf(d, d, acc2[k]);
+      }
+    }
+  }
+  const float r = block_sum<W>(tree8(acc1), slot1) / n_f;
+  const float m2 = block_sum<W>(tree8(acc2), slot2) / n_f;
+  const float var = fmaxf(fmaf(-r, r, m2), 0.0f);
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    if (gi < ng) {
+      float v[8], gv[8], bv[8];
+      widen8<T>(raw[g], v);
+      if (gam) {
+        widen8<T>(ld_row<TAIL>(gam, gi, n), gv);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) gv[k] = 1.0f;
+      }
+      if (bet) {
+        widen8<T>(ld_row<TAIL>(bet, gi, n), bv);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fmaf(((v[k] - mu0) - r) * rstd, gv[k], bv[k]);
+      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
+    }
+  }
+}
+
+// ------------------------------------------------- split-K, two passes
+// Rows beyond what a workgroup's registers hold (s3.2.4): the first pass only
+// accumulates the sum of squares, chunk by chunk; the second pass walks the
+// chunks in reverse order, so the chunks read last in the first pass are the
+// first re-read (still in cache), and writes y.  x is read twice; the ledger
+// counts that.  One 1024-thread workgroup per row; a chunk is one granule per
+// thread, and the first pass keeps kSplitUnroll chunks of loads in flight.
+constexpr int kSplitWaves = 16;
+constexpr int kSplitThreads = kWave * kSplitWaves;
+constexpr int kSplitUnroll = 4;
+
+template <typename T, bool TAIL>
+__global__ __launch_bounds__(kSplitThreads) void rmsnorm_splitk_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int ng, int n, int64_t xs,
+    int64_t ys, float n_f, float eps) {
+  __shared__ float slot[kSplitWaves];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * xs;
+  uint16_t* yr = y + row * ys;
+  const int chunks = (ng + kSplitThreads - 1) / kSplitThreads;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < chunks; c0 += kSplitUnroll) {
+    u32x4 raw[kSplitUnroll];
+#pragma unroll
+    for (int u = 0; u < kSplitUnroll; ++u) {
+      const int gi = (c0 + u) * kSplitThreads + t;
+      raw[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (gi < ng) raw[u] = ld_row<TAIL>(xr, gi, n);
+    }
+#pragma unroll
+    for (int u = 0; u < kSplitUnroll; ++u) {
+      float v[8];
+      widen8<T>(raw[u], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+    }
+  }
+  const float ss = block_sum<kSplitWaves>(tree8(acc), slot);
+  const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+  for (int c = chunks - 1; c >= 0; --c) {  // reverse order: the last chunks are still cached
+    const int gi = c * kSplitThreads + t;
+    if (gi < ng) {
+      float v[8];
+      widen8<T>(ld_row<TAIL>(xr, gi, n), v);
+      if (w) {
+        float wv[8];
+        widen8<T>(ld_row<TAIL>(w, gi, n), wv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
+      }
+      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
     }
   }
 }
@@ -172,49 +399,102 @@ int granules_per_lane(int ng) {
   return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16;
 }
 
+// Waves per row for kOneWaveGranules < ng <= kResidentGranules: the smallest
+// power of two in [2, 16] whose threads hold the row at 8 granules each (8
+// granules = 32 VGPRs of row data, which keeps a 1024-thread workgroup within
+// its 128 VGPRs per lane without spilling).
+int block_waves(int ng) {
+  int w = 2;
+  while (w < 16 && w * kWave * 8 < ng) w *= 2;
+  return w;
+}
+
 }  // namespace
 
-#define QRW_NORM_DISPATCH(KERNEL, T, gpl, full, grid, stream, ...)                       \
-  do {                                                                                   \
-    switch (gpl) {                                                                       \
-      case 1:                                                                            \
-        if (full) KERNEL<T, 1, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);          \
-        else KERNEL<T, 1, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);             \
-        break;                                                                           \
-      case 2:                                                                            \
-        if (full) KERNEL<T, 2, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);          \
-        else KERNEL<T, 2, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);             \
-        break;                                                                           \
-      case 4:                                                                            \
-        if (full) KERNEL<T, 4, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);          \
-        else KERNEL<T, 4, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);             \
-        break;                                                                           \
-      case 8:                                                                            \
-        if (full) KERNEL<T, 8, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);          \
-        else KERNEL<T, 8, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);             \
-        break;                                                                           \
-      default:                                                                           \
-        if (full) KERNEL<T, 16, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);         \
-        else KERNEL<T, 16, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);            \
-        break;                                                                           \
-    }                                                                                    \
+#define QRW_NORM_DISPATCH(KERNEL, T, gpl, full, tail, grid, stream, ...)                      \
+  do {                                                                                        \
+    switch (gpl) {                                                                            \
+      case 1:                                                                                 \
+        if (tail) KERNEL<T, 1, false, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);        \
+        else if (full) KERNEL<T, 1, true, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);   \
+        else KERNEL<T, 1, false, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);           \
+        break;                                                                                \
+      case 2:                                                                                 \
+        if (tail) KERNEL<T, 2, false, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);        \
+        else if (full) KERNEL<T, 2, true, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);   \
+        else KERNEL<T, 2, false, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);           \
+        break;                                                                                \
+      case 4:                                                                                 \
+        if (tail) KERNEL<T, 4, false, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);        \
+        else if (full) KERNEL<T, 4, true, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);   \
+        else KERNEL<T, 4, false, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);           \
+        break;                                                                                \
+      case 8:                                                                                 \
+        if (tail) KERNEL<T, 8, false, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);        \
+        else if (full) KERNEL<T, 8, true, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);   \
+        else KERNEL<T, 8, false, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);           \
+        break;                                                                                \
+      default:                                                                                \
+        if (tail) KERNEL<T, 16, false, true><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);       \
+        else if (full) KERNEL<T, 16, true, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);  \
+        else KERNEL<T, 16, false, false><<<grid, kBlock, 0, stream>>>(__VA_ARGS__);          \
+        break;                                                                                \
+    }                                                                                         \
+  } while (0)
+
+// One launch of a row-block kernel: W waves per workgroup, one row per workgroup.
+#define QRW_ROWBLOCK_GO(KERNEL, T, W, GPL, tail, rows, stream, ...)                           \
+  do {                                                                                        \
+    if (tail) KERNEL<T, W, GPL, true><<<dim3((unsigned)(rows)), kWave * W, 0, stream>>>(__VA_ARGS__); \
+    else KERNEL<T, W, GPL, false><<<dim3((unsigned)(rows)), kWave * W, 0, stream>>>(__VA_ARGS__);     \
+  } while (0)
+
+#define QRW_ROWBLOCK_DISPATCH(KERNEL, T, waves, tail, rows, stream, ...)                      \
+  do {                                                                                        \
+    switch (waves) {                                                                          \
+      case 2: QRW_ROWBLOCK_GO(KERNEL, T, 2, 8, tail, rows, stream, __VA_ARGS__); break;       \
+      case 4: QRW_ROWBLOCK_GO(KERNEL, T, 4, 8, tail, rows, stream, __VA_ARGS__); break;       \
+      case 8: QRW_ROWBLOCK_GO(KERNEL, T, 8, 8, tail, rows, stream, __VA_ARGS__); break;       \
+      default: QRW_ROWBLOCK_GO(KERNEL, T, 16, 8, tail, rows, stream, __VA_ARGS__); break;     \
+    }                                                                                         \
   } while (0)
 
 hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t n,
                           int64_t xs, int64_t ys, int dtype, float eps, hipStream_t stream) {
-  const int ng = (int)(n / 8);
-  const int gpl = granules_per_lane(ng);
-  const bool full = ng == gpl * kWave;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int ng = (int)((n + 7) / 8);
+  const bool tail = n % 8 != 0;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
   auto* yp = static_cast<uint16_t*>(y);
-  if (dtype == 1) {
-    QRW_NORM_DISPATCH(rmsnorm_kernel, F16, gpl, full, grid, stream, xp, wp, yp, rows, ng, xs, ys,
-                      (float)n, eps);
+  const int ni = (int)n;
+  const float nf = (float)n;
+  if (ng <= kOneWaveGranules) {
+    const int gpl = granules_per_lane(ng);
+    const bool full = !tail && ng == gpl * kWave;
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    if (dtype == 1)
+      QRW_NORM_DISPATCH(rmsnorm_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp, rows, ng,
+                        ni, xs, ys, nf, eps);
+    else
+      QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, ng,
+                        ni, xs, ys, nf, eps);
+  } else if (ng <= kResidentGranules) {
+    const int wv = block_waves(ng);
+    if (dtype == 1)
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, wp, yp, ng,
+                            ni, xs, ys, nf, eps);
+    else
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, wp, yp, ng,
+                            ni, xs, ys, nf, eps);
   } else {
-    QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, grid, stream, xp, wp, yp, rows, ng, xs,
-                      ys, (float)n, eps);
+    const dim3 grid((unsigned)rows);
+    if (dtype == 1) {
+      if (tail) rmsnorm_splitk_kernel<F16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+      else rmsnorm_splitk_kernel<F16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+    } else {
+      if (tail) rmsnorm_splitk_kernel<BF16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+      else rmsnorm_splitk_kernel<BF16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+    }
   }
   return hipGetLastError();
 }
@@ -222,20 +502,32 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
 hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y, int64_t rows,
                             int64_t n, int64_t xs, int64_t ys, int dtype, float eps,
                             hipStream_t stream) {
-  const int ng = (int)(n / 8);
-  const int gpl = granules_per_lane(ng);
-  const bool full = ng == gpl * kWave;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int ng = (int)((n + 7) / 8);
+  const bool tail = n % 8 != 0;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* gp = static_cast<const uint16_t*>(g);
   const auto* bp = static_cast<const uint16_t*>(b);
   auto* yp = static_cast<uint16_t*>(y);
-  if (dtype == 1) {
-    QRW_NORM_DISPATCH(layernorm_kernel, F16, gpl, full, grid, stream, xp, gp, bp, yp, rows, ng,
-                      xs, ys, (float)n, eps);
+  const int ni = (int)n;
+  const float nf = (float)n;
+  if (ng <= kOneWaveGranules) {
+    const int gpl = granules_per_lane(ng);
+    const bool full = !tail && ng == gpl * kWave;
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    if (dtype == 1)
+      QRW_NORM_DISPATCH(layernorm_kernel, F16, gpl, full, tail, grid, stream, xp, gp, bp, yp, rows,
+                        ng, ni, xs, ys, nf, eps);
+    else
+      QRW_NORM_DISPATCH(layernorm_kernel, BF16, gpl, full, tail, grid, stream, xp, gp, bp, yp,
+                        rows, ng, ni, xs, ys, nf, eps);
   } else {
-    QRW_NORM_DISPATCH(layernorm_kernel, BF16, gpl, full, grid, stream, xp, gp, bp, yp, rows, ng,
-                      xs, ys, (float)n, eps);
+    const int wv = block_waves(ng);
+    if (dtype == 1)
+      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, gp, bp, yp,
+                            ng, ni, xs, ys, nf, eps);
+    else
+      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, gp, bp,
+                            yp, ng, ni, xs, ys, nf, eps);
   }
   return hipGetLastError();
 }

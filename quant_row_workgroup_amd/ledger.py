@@ -54,6 +54,13 @@ def rmsnorm(rows: int, n: int, elt: int = 2, stat: int = 4):
     return sum(steps), fused, 4 * rows * n
 
 
+def rmsnorm_split(rows: int, n: int, elt: int = 2):
+    """The split-K RMSNorm of s3.2.4: x is read twice (sum of squares, then the
+    output pass), so the ledger counts one more read of x than the fused kernel."""
+    E = rows * n * elt
+    return rmsnorm(rows, n, elt)[0], _kernel([E, E, n * elt], [E]), 4 * rows * n
+
+
 def layernorm(rows: int, n: int, elt: int = 2):
     """LayerNorm.  The pages give only the total (20E + O(rows)); the chain is a
     reading: sum(x), sum(x^2) (statistics stored at the tensor dtype), x - mu,
@@ -176,6 +183,8 @@ def counted_bytes(cfg: dict) -> int:
     """Algorithmic bytes of one launch of a workload (see ``synth.WORKLOADS``)."""
     op = cfg["op"]
     if op == "rmsnorm":
+        if cfg.get("x_passes", 1) == 2:
+            return rmsnorm_split(cfg["rows"], cfg["n"], ELT[cfg["dtype"]])[1]
         return rmsnorm(cfg["rows"], cfg["n"], ELT[cfg["dtype"]])[1]
     if op == "layernorm":
         return layernorm(cfg["rows"], cfg["n"], ELT[cfg["dtype"]])[1]

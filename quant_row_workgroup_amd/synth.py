@@ -91,6 +91,14 @@ WORKLOADS = {
                                       y_dtype="f16", alpha=0.5, seed=12),
     "rmsnorm_256x1024_f16": dict(op="rmsnorm", rows=256, n=1024, dtype="f16", eps=1e-6, seed=1),
     "rmsnorm_4096x4096_f16": dict(op="rmsnorm", rows=4096, n=4096, dtype="f16", eps=1e-6, seed=2),
+    "rmsnorm_1024x32768_bf16": dict(op="rmsnorm", rows=1024, n=32768, dtype="bf16", eps=1e-6,
+                                    seed=13),
+    "rmsnorm_256x131072_bf16_splitk": dict(op="rmsnorm", rows=256, n=131072, dtype="bf16",
+                                           eps=1e-6, x_passes=2, seed=14),
+    "rmsnorm_4096x4095_bf16_ragged": dict(op="rmsnorm", rows=4096, n=4095, dtype="bf16", eps=1e-6,
+                                          seed=16),
+    "layernorm_1024x32768_bf16": dict(op="layernorm", rows=1024, n=32768, dtype="bf16", eps=1e-5,
+                                      seed=15),
     "layernorm_4096x4096_bf16": dict(op="layernorm", rows=4096, n=4096, dtype="bf16", eps=1e-5,
                                      seed=3),
     "rope_4096x32x128_f16": dict(op="rope", tokens=4096, heads=32, head_dim=128, rope_dim=128,

@@ -65,7 +65,9 @@ def rms(**kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), NULL), (dict(y=None), NULL),
     (dict(dtype=F32), DTYPE), (dict(dtype=0), DTYPE), (dict(dtype=7), DTYPE),
-    (dict(n=60), SHAPE), (dict(n=0), SHAPE), (dict(n=8200), SHAPE), (dict(rows=-1), SHAPE),
+    (dict(n=0), SHAPE), (dict(n=(1 << 26) + 1, xs=(1 << 26) + 8, ys=(1 << 26) + 8), SHAPE),
+    (dict(rows=-1), SHAPE), (dict(n=8200), STRIDE),
+    (dict(rows=1 << 31, n=8200, xs=8200, ys=8200), SHAPE),   # one workgroup per long row
     (dict(xs=56), STRIDE), (dict(ys=60, n=56), STRIDE), (dict(xs=68), STRIDE),
     (dict(x=ctypes.c_void_p((1 << 32) + 8)), ALIGN), (dict(y=ctypes.c_void_p((2 << 32) + 4)), ALIGN),
     (dict(w=ctypes.c_void_p((3 << 32) + 2)), ALIGN),
@@ -89,7 +91,9 @@ def ln(**kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(x=None), NULL), (dict(dtype=F32), DTYPE), (dict(n=12), SHAPE), (dict(xs=32), STRIDE),
+    (dict(x=None), NULL), (dict(dtype=F32), DTYPE), (dict(n=0), SHAPE),
+    (dict(n=65537, xs=65544, ys=65544), SHAPE),                 # no two-pass LayerNorm
+    (dict(xs=32), STRIDE), (dict(n=13, xs=13, ys=16), STRIDE),
     (dict(b=ctypes.c_void_p((4 << 32) + 8)), ALIGN), (dict(eps=-1.0), VALUE),
     (dict(y=ctypes.c_void_p((1 << 32) + 16)), ALIAS), (dict(rows=0), OK),
 ])

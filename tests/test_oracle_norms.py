@@ -145,3 +145,29 @@ def test_layernorm_standardises(fmt):
     tol = 2.0 ** -8 if fmt == "bf16" else 2.0 ** -11
     assert np.all(np.abs(y.mean(axis=1)) < tol)
     assert np.all(np.abs(y.var(axis=1) - 1.0) < 4 * tol)
+
+
+# ------------------------------------------------------------- ragged lengths
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 3, 13, 21])
+def test_lengths_not_a_multiple_of_8_against_brute_force(fmt, n):
+    # s5.4: a row of n columns, any n; the divisor is n
+    x = _rand(600 + n, (3, n), 0.5, 1.5, fmt)
+    w = _rand(700 + n, (n,), 1.0, 0.2, fmt)
+    b = _rand(800 + n, (n,), 0.0, 0.2, fmt)
+    y = oracle.rmsnorm(x, w, fmt, 1e-6)
+    z = oracle.layernorm(x, w, b, fmt, 1e-5)
+    for r in range(3):
+        assert [int(v) for v in y[r]] == exact.rmsnorm_ref(x[r], w, fmt, 1e-6), r
+        assert [int(v) for v in z[r]] == exact.layernorm_ref(x[r], w, b, fmt, 1e-5), r
+
+
+def test_single_element_rows():
+    # n = 1: RMSNorm gives sign(x) * w / sqrt(1 + eps/x^2); LayerNorm gives beta
+    x = synth.to_storage(np.array([[3.0], [-0.5]]), "bf16")
+    w = synth.to_storage(np.array([2.0]), "bf16")
+    b = synth.to_storage(np.array([0.25]), "bf16")
+    y = _f64(oracle.rmsnorm(x, w, "bf16", 1e-6), "bf16")
+    assert list(y[:, 0]) == [2.0, -2.0]
+    z = _f64(oracle.layernorm(x, w, b, "bf16", 1e-5), "bf16")
+    assert list(z[:, 0]) == [0.25, 0.25]
