@@ -283,3 +283,16 @@ def ew_scale_add(x, b, alpha: float, x_dtype: str, y_dtype: str | None = None):
     L.oracle_ew_scale_add(_ptr(x), _ptr(b), _ptr(y), x.size, alpha, DTYPE_CODE[x_dtype],
                           DTYPE_CODE[yd])
     return y
+
+
+def rmsnorm_rope_fp8_rounded(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int,
+                             dtype: str, cs_dtype: str, neox: bool, eps: float):
+    """The staged form of the fused operator ("TileLang tutorial, ch. 13", s3.3.4:
+    the normalised row is written back in x's dtype and rotated there): RMSNorm
+    rounded once to ``dtype``, RoPE of those values rounded once to ``dtype``, then
+    the per-token cast (s3.1.5) of the result.  That is the composition of the
+    three operators above; returns (codes [tokens, n], scales [tokens])."""
+    u = rmsnorm(x, w, dtype, eps)
+    z = rope(u, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox)
+    q, scales = act_quant_fp8(z, dtype, None)
+    return q, scales[:, 0].copy()
