@@ -184,11 +184,11 @@ class Workload:
         st = ctypes.c_void_p(stream_ptr)
         if self.op == "fused":
             T, H, D, R = c["tokens"], c["heads"], c["head_dim"], c["rope_dim"]
-            rc = self.lib.rmsnorm_rope_fp8_fwd(p(s["x"]), p(s["w"]), p(s["cos"]), p(s["sin"]),
-                                               p(s["q"]), p(s["scales"]), T, H, D, R, H * D,
-                                               H * D, self.code[c["dtype"]],
-                                               self.code[c["cs_dtype"]], int(c["neox"]),
-                                               c["eps"], st)
+            fn = (self.lib.rmsnorm_rope_fp8_rounded_fwd if c.get("staged")
+                  else self.lib.rmsnorm_rope_fp8_fwd)
+            rc = fn(p(s["x"]), p(s["w"]), p(s["cos"]), p(s["sin"]), p(s["q"]), p(s["scales"]),
+                    T, H, D, R, H * D, H * D, self.code[c["dtype"]], self.code[c["cs_dtype"]],
+                    int(c["neox"]), c["eps"], st)
         elif self.op == "qk_norm_rope":
             T, D = c["tokens"], c["head_dim"]
             n = (c["q_heads"] + 2 * c["kv_heads"]) * D
@@ -329,9 +329,9 @@ def cpu_baseline(name: str, seconds: float):
 
     def call():
         if op == "fused":
-            oracle.rmsnorm_rope_fp8(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg["heads"],
-                                    cfg["head_dim"], cfg["rope_dim"], cfg["dtype"],
-                                    cfg["cs_dtype"], cfg["neox"], cfg["eps"])
+            fn = oracle.rmsnorm_rope_fp8_rounded if cfg.get("staged") else oracle.rmsnorm_rope_fp8
+            fn(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg["heads"], cfg["head_dim"],
+               cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "act_quant":
             oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
         elif op == "ew":

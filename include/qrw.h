@@ -150,6 +150,22 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
                          void* stream);
 
 /*
+ * The staged form of the same operator, as s3.3.4's dataflow runs it: the
+ * normalised row is written back in x's dtype and rotated there, so
+ *   u = round_T( x[t,:] * rstd_t * weight )       (T = dtype, nearest-even)
+ *   z = round_T( RoPE(u) )                        (unrotated channels: z = u)
+ * and scales / codes are formed from z as in rmsnorm_rope_fp8_fwd.  The
+ * result equals rmsnorm_fwd, then rope_apply_*, then act_quant_fp8_fwd with
+ * one group per row.  Same arguments, layout, limits and errors as
+ * rmsnorm_rope_fp8_fwd.
+ */
+int rmsnorm_rope_fp8_rounded_fwd(const void* x, const void* weight, const void* cos,
+                                 const void* sin, uint8_t* q, float* scales, int64_t tokens,
+                                 int64_t heads, int64_t head_dim, int64_t rope_dim,
+                                 int64_t x_token_stride, int64_t q_token_stride, int dtype,
+                                 int cs_dtype, int neox, float eps, void* stream);
+
+/*
  * Activation quantisation to OCP E4M3FN (s3.1.5), one scale per group of
  * `group` consecutive channels of a row, or per row (group == n):
  *   amax_{r,k}   = max |x[r,j]| over group k of row r

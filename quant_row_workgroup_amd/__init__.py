@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     ew_scale_cast_fwd,
     load,
     qk_norm_rope_fp8_kv_fwd,
+    rmsnorm_rope_fp8_rounded_fwd,
     qk_norm_rope_fwd,
     rmsnorm_fwd,
     rmsnorm_rope_fp8_fwd,

@@ -28,7 +28,8 @@ STATUS = {
 
 EXPORTS = ("rmsnorm_fwd", "layernorm_fwd", "rope_apply_interleaved", "rope_apply_neox",
            "rmsnorm_rope_fp8_fwd", "act_quant_fp8_fwd", "qk_norm_rope_fwd",
-           "qk_norm_rope_fp8_kv_fwd", "ew_add_fwd", "ew_scale_cast_fwd", "ew_scale_add_fwd",
+           "qk_norm_rope_fp8_kv_fwd", "rmsnorm_rope_fp8_rounded_fwd", "ew_add_fwd",
+           "ew_scale_cast_fwd", "ew_scale_add_fwd",
            "qrw_status_string")
 
 
@@ -58,6 +59,7 @@ def load():
     L.rope_apply_neox.argtypes = rope_args
     L.rmsnorm_rope_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                        i32, i32, i32, f32, vp]
+    L.rmsnorm_rope_fp8_rounded_fwd.argtypes = L.rmsnorm_rope_fp8_fwd.argtypes
     L.act_quant_fp8_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     L.qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32,
                                    i32, f32, vp]
@@ -165,10 +167,7 @@ def rope_apply_neox(x, cos, sin, heads: int, head_dim: int, rope_dim: int | None
                  head_dim if rope_dim is None else rope_dim, out)
 
 
-def rmsnorm_rope_fp8_fwd(x, weight, cos, sin, heads: int, head_dim: int,
-                         rope_dim: int | None = None, neox: bool = True, eps: float = 1e-6,
-                         q=None, scales=None):
-    """Returns (codes uint8 [tokens, n], scales float32 [tokens])."""
+def _fused(fname, x, weight, cos, sin, heads, head_dim, rope_dim, neox, eps, q, scales):
     tokens, n, xs = _rows(x, "x")
     if heads * head_dim != n:
         raise ValueError("heads * head_dim must equal the row length")
@@ -181,12 +180,27 @@ def rmsnorm_rope_fp8_fwd(x, weight, cos, sin, heads: int, head_dim: int,
     for t, nm in ((cos, "cos"), (sin, "sin")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
-    st = load().rmsnorm_rope_fp8_fwd(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(cos),
-                                     _ptr(sin), _ptr(q), _ptr(scales), tokens, heads, head_dim,
-                                     rd, xs, qs, _dtype(x), _dtype(cos), int(bool(neox)), eps,
-                                     _stream(x))
-    _check("rmsnorm_rope_fp8_fwd", st)
+    st = getattr(load(), fname)(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(cos), _ptr(sin),
+                                _ptr(q), _ptr(scales), tokens, heads, head_dim, rd, xs, qs,
+                                _dtype(x), _dtype(cos), int(bool(neox)), eps, _stream(x))
+    _check(fname, st)
     return q, scales
+
+
+def rmsnorm_rope_fp8_fwd(x, weight, cos, sin, heads: int, head_dim: int,
+                         rope_dim: int | None = None, neox: bool = True, eps: float = 1e-6,
+                         q=None, scales=None):
+    """Returns (codes uint8 [tokens, n], scales float32 [tokens])."""
+    return _fused("rmsnorm_rope_fp8_fwd", x, weight, cos, sin, heads, head_dim, rope_dim, neox,
+                  eps, q, scales)
+
+
+def rmsnorm_rope_fp8_rounded_fwd(x, weight, cos, sin, heads: int, head_dim: int,
+                                 rope_dim: int | None = None, neox: bool = True,
+                                 eps: float = 1e-6, q=None, scales=None):
+    """The staged form (normalised and rotated values rounded to x's dtype)."""
+    return _fused("rmsnorm_rope_fp8_rounded_fwd", x, weight, cos, sin, heads, head_dim,
+                  rope_dim, neox, eps, q, scales)
 
 
 def act_quant_fp8_fwd(x, group: int | None = None, q=None, scales=None):

@@ -174,11 +174,11 @@ int rope_apply_neox(const void* x, const void* cos, const void* sin, void* y, in
                      y_token_stride, dtype, cs_dtype, true, stream);
 }
 
-int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, const void* sin,
-                         uint8_t* q, float* scales, int64_t tokens, int64_t heads,
-                         int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
-                         int64_t q_token_stride, int dtype, int cs_dtype, int neox, float eps,
-                         void* stream) {
+static int fused_entry(const void* x, const void* weight, const void* cos, const void* sin,
+                       uint8_t* q, float* scales, int64_t tokens, int64_t heads,
+                       int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
+                       int64_t q_token_stride, int dtype, int cs_dtype, int neox, float eps,
+                       bool round_mid, void* stream) {
   if (!is_16bit(dtype) || !cs_ok(dtype, cs_dtype)) return QRW_ERR_DTYPE;
   int st = check_heads(tokens, heads, head_dim, rope_dim);
   if (st != QRW_OK) return st;
@@ -208,7 +208,25 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
   return finish(qrw::launch_rmsnorm_rope_fp8(x, weight, cos, sin, q, scales, tokens, heads,
                                              head_dim, rope_dim, x_token_stride,
                                              q_token_stride, dtype, cs_dtype, neox == 1, eps,
-                                             static_cast<hipStream_t>(stream)));
+                                             round_mid, static_cast<hipStream_t>(stream)));
+}
+
+int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, const void* sin,
+                         uint8_t* q, float* scales, int64_t tokens, int64_t heads,
+                         int64_t head_dim, int64_t rope_dim, int64_t x_token_stride,
+                         int64_t q_token_stride, int dtype, int cs_dtype, int neox, float eps,
+                         void* stream) {
+  return fused_entry(x, weight, cos, sin, q, scales, tokens, heads, head_dim, rope_dim,
+                     x_token_stride, q_token_stride, dtype, cs_dtype, neox, eps, false, stream);
+}
+
+int rmsnorm_rope_fp8_rounded_fwd(const void* x, const void* weight, const void* cos,
+                                 const void* sin, uint8_t* q, float* scales, int64_t tokens,
+                                 int64_t heads, int64_t head_dim, int64_t rope_dim,
+                                 int64_t x_token_stride, int64_t q_token_stride, int dtype,
+                                 int cs_dtype, int neox, float eps, void* stream) {
+  return fused_entry(x, weight, cos, sin, q, scales, tokens, heads, head_dim, rope_dim,
+                     x_token_stride, q_token_stride, dtype, cs_dtype, neox, eps, true, stream);
 }
 
 int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,

@@ -33,7 +33,7 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    const void* sin, uint8_t* q, float* scales, int64_t tokens,
                                    int64_t heads, int64_t head_dim, int64_t rope_dim,
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
-                                   float eps, hipStream_t stream);
+                                   float eps, bool round_mid, hipStream_t stream);
 
 hipError_t launch_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows,
                                 int64_t n, int64_t group, int64_t xs, int64_t qs, int dtype,

@@ -130,7 +130,19 @@ __global__ __launch_bounds__(kBlock) void rope_kernel(const uint16_t* x, const v
 }
 
 // ------------------------------------------------------------------ fused
-template <typename T, typename CS, bool NEOX, int K>
+// Round eight binary32 values to the 16-bit format T (nearest-even) and back.
+template <typename T>
+__device__ __forceinline__ void round8(float (&v)[8]) {
+  widen8<T>(narrow8<T>(v), v);
+}
+
+// MID: the staged form of the page's fused dataflow, which writes the
+// normalised row back to shared memory in x's dtype and rotates it there: the
+// normalised values x * rstd * w and the rotated values are each rounded to
+// T, and the codes quantise those stored values (the same results as the
+// three operators run one after another).  Without MID the row stays in
+// binary32 from the load to the codes.
+template <typename T, typename CS, bool NEOX, int K, bool MID>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, RowPlan pl, float n_f,
@@ -199,6 +211,15 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
         vb[i][e] *= wb[e];
       }
     }
+    if (MID) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        va[i][e] *= rstd;
+        vb[i][e] *= rstd;
+      }
+      round8<T>(va[i]);
+      round8<T>(vb[i]);
+    }
     if (kind[i] == kItemRope) {
       float c[8], s[8];
       if (pl.lane_hoist) {
@@ -212,15 +233,21 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
         Table8<CS>::load(srow, si[i], s);
       }
       rotate<NEOX>(va[i], vb[i], c, s);
+      if (MID) {
+        round8<T>(va[i]);
+        round8<T>(vb[i]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(va[i][e]), fabsf(vb[i][e])));
   }
 
   // 4. per-token scale (s3.1.5): scale = max(amax_z, 1e-4) / 448, amax_z = amax * rstd
-  const float amax_z = wave_max(amax) * rstd;
+  //    (MID: the stored values already carry rstd)
+  const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
   const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
   const float k = rstd / scale;
+  const float inv = 1.0f / scale;
   if (lane == 0) scales[t] = scale;
 
   // 5. quantise and store the codes
@@ -230,8 +257,10 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
       float a[8], b[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        a[e] = va[i][e] * k;
-        b[e] = vb[i][e] * k;
+        // MID: the correctly rounded quotient of the stored value, as the
+        // standalone per-token cast forms it
+        a[e] = MID ? div_rn(va[i][e], scale, inv) : va[i][e] * k;
+        b[e] = MID ? div_rn(vb[i][e], scale, inv) : vb[i][e] * k;
       }
       st8(qr + oa[i], fp8x8(a));
       if (ob[i] >= 0) st8(qr + ob[i], fp8x8(b));
@@ -592,7 +621,16 @@ int contig_blocks(const RowPlan& pl) {
 template <typename T, typename CS, bool NEOX>
 void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w,
               const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
-              int64_t qs, const RowPlan& pl, float n_f, float eps) {
+              int64_t qs, const RowPlan& pl, float n_f, float eps, bool mid) {
+  if (mid) {  // the staged form: the item kernel, any shape
+    switch (kk) {
+      case 1: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 1, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+      case 2: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 2, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+      case 4: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 4, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+      default: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 8, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    }
+    return;
+  }
   switch (contig_blocks(pl)) {
     case 1: contig_go_xd<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
     case 2: contig_go_xd<T, CS, NEOX, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
@@ -609,10 +647,10 @@ void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16
     }
   }
   switch (kk) {
-    case 1: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 1><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    case 2: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 2><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    case 4: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 4><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    default: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 8><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 1: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 1, false><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 2: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 2, false><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 4: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 4, false><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    default: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 8, false><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
   }
 }
 
@@ -620,9 +658,9 @@ template <typename T, typename CS>
 void fused_go2(bool neox, int kk, dim3 grid, hipStream_t st, const uint16_t* x,
                const uint16_t* w, const void* c, const void* s, uint8_t* q, float* sc,
                int64_t tokens, int64_t xs, int64_t qs, const RowPlan& pl, float n_f,
-               float eps) {
-  if (neox) fused_go<T, CS, true>(kk, grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps);
-  else fused_go<T, CS, false>(kk, grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps);
+               float eps, bool mid) {
+  if (neox) fused_go<T, CS, true>(kk, grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid);
+  else fused_go<T, CS, false>(kk, grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid);
 }
 
 int items_per_lane(int n_items, int kmax) {
@@ -656,7 +694,7 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    const void* sin, uint8_t* q, float* scales, int64_t tokens,
                                    int64_t heads, int64_t head_dim, int64_t rope_dim,
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
-                                   float eps, hipStream_t stream) {
+                                   float eps, bool round_mid, hipStream_t stream) {
   const RowPlan pl = make_plan(heads, head_dim, rope_dim);
   const int kk = items_per_lane(pl.n_items, 8);
   const dim3 grid((unsigned)((tokens + kRowsPerBlock - 1) / kRowsPerBlock));
@@ -664,11 +702,11 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
   const auto* wp = static_cast<const uint16_t*>(w);
   const float n_f = (float)pl.n;
   if (dtype == 1) {
-    if (cs_dtype == 3) fused_go2<F16, float>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps);
-    else fused_go2<F16, F16>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps);
+    if (cs_dtype == 3) fused_go2<F16, float>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps, round_mid);
+    else fused_go2<F16, F16>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps, round_mid);
   } else {
-    if (cs_dtype == 3) fused_go2<BF16, float>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps);
-    else fused_go2<BF16, BF16>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps);
+    if (cs_dtype == 3) fused_go2<BF16, float>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps, round_mid);
+    else fused_go2<BF16, BF16>(neox, kk, grid, stream, xp, wp, cos, sin, q, scales, tokens, xs, qs, pl, n_f, eps, round_mid);
   }
   return hipGetLastError();
 }

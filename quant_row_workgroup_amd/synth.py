@@ -115,6 +115,10 @@ WORKLOADS = {
                                                        kv_heads=8, head_dim=128, rope_dim=128,
                                                        dtype="bf16", cs_dtype="bf16", eps=1e-6,
                                                        neox=True, num_slots=16384, seed=9),
+    "rmsnorm_rope_fp8_4096x4096_bf16_staged": dict(op="fused", tokens=4096, heads=32,
+                                                   head_dim=128, rope_dim=128, dtype="bf16",
+                                                   cs_dtype="bf16", eps=1e-6, neox=True,
+                                                   staged=True, seed=5),
     "rmsnorm_rope_fp8_4096x4096_bf16": dict(op="fused", tokens=4096, heads=32, head_dim=128,
                                             rope_dim=128, dtype="bf16", cs_dtype="bf16",
                                             eps=1e-6, neox=True, seed=5),

@@ -252,3 +252,13 @@ def test_qk_kv_cache_validation(kw, want):
 ])
 def test_elementwise_validation(call, want):
     assert call(qrw.load()) == want
+
+
+def test_staged_fused_validates_like_the_exact_one():
+    L = qrw.load()
+    args = [X, W, C, S, Q, SC, 4, 32, 128, 128, 4096, 4096, BF16, BF16, 1, 1e-6, None]
+    for i, bad, want in [(0, None, NULL), (12, F32, DTYPE), (8, 100, SHAPE), (10, 4000, STRIDE),
+                         (14, 2, VALUE), (4, ctypes.c_void_p((1 << 32) + 4096), ALIAS), (6, 0, OK)]:
+        a = list(args)
+        a[i] = bad
+        assert L.rmsnorm_rope_fp8_rounded_fwd(*a) == want == L.rmsnorm_rope_fp8_fwd(*a), i
