@@ -41,10 +41,42 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-I", INCLUDE, "-o", LIB + ".tmp"] + sources()
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-Wall"]
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile each source to an object in parallel (bounded by ``jobs``, default
+    the CPU count, at most 16), then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(f)[:-4] + ".o") for f in srcs]
+
+    def compile_one(pair):
+        src, obj = pair
+        cmd = [hipcc(), f"--offload-arch={ARCH}"] + FLAGS + ["-I", INCLUDE, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    n = jobs or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        results = list(ex.map(compile_one, zip(srcs, objs)))
+    failed = False
+    for src, r in zip(srcs, results):
+        out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                        if "packed-fp32-ops' is not a recognized feature" not in line)
+        if out.strip():
+            print(out, file=sys.stderr)
+        if r.returncode != 0:
+            print(f"compiling {os.path.basename(src)} failed", file=sys.stderr)
+            failed = True
+    if failed:
+        raise subprocess.CalledProcessError(1, "hipcc")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
     tl = torch_lib_dir()
     if tl:
         cmd += [f"-Wl,-rpath,{tl}"]

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
 // in the same granule.  Each lane needs a single table granule per token.
 // The arithmetic is that of rotate(): first of a pair x_a c - x_b s as
 // fma(x_a, c, x_b * (-s)), second x_b c + x_a s as fma(x_b, c, x_a * s).
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD>
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_contig_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, float n_f,
@@ -340,6 +340,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_contig_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[g][e] *= f[e];
     }
+    if (MID) {  // the staged form (see rmsnorm_rope_fp8_kernel): store x*w*rstd in T
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[g][e] *= rstd;
+      round8<T>(v[g]);
+    }
     if (NEOX) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[g][e] = fmaf(v[g][e], c[e], lane_xor<XD>(v[g][e]) * sn[e]);
@@ -351,21 +356,23 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_contig_kernel(
         v[g][2 * k + 1] = fmaf(x1, c[k], x0 * sn[k]);
       }
     }
+    if (MID) round8<T>(v[g]);
 #pragma unroll
     for (int e = 0; e < 8; e += 2)
       m[(e >> 1) & 3] = fmaxf(m[(e >> 1) & 3], fmaxf(fabsf(v[g][e]), fabsf(v[g][e + 1])));
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-  const float amax_z = wave_max(amax) * rstd;
+  const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
   const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
   const float kq = rstd / scale;
+  const float inv = 1.0f / scale;
   if (lane == 0) scales[t] = scale;
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float a[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = v[g][e] * kq;
+    for (int e = 0; e < 8; ++e) a[e] = MID ? div_rn(v[g][e], scale, inv) : v[g][e] * kq;
     st8(qr + 8 * (kWave * g + lane), fp8x8(a));
   }
 }
@@ -585,25 +592,34 @@ bool dense_ok(const RowPlan& pl, int kk) {
 template <typename T, typename CS, bool NEOX, int G, int XD>
 void contig_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
                const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-               const RowPlan& pl, float n_f, float eps) {
+               const RowPlan& pl, float n_f, float eps, bool mid) {
+  if (mid) {
+    if (w)
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, true><<<grid, kBlock, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+    else
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, true><<<grid, kBlock, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+    return;
+  }
   if (w)
-    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD><<<grid, kBlock, 0, st>>>(
+    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false><<<grid, kBlock, 0, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
   else
-    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD><<<grid, kBlock, 0, st>>>(
+    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, false><<<grid, kBlock, 0, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
 }
 
 template <typename T, typename CS, bool NEOX, int G>
 void contig_go_xd(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
                   const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-                  const RowPlan& pl, float n_f, float eps) {
+                  const RowPlan& pl, float n_f, float eps, bool mid) {
   switch (pl.head_dim / 16) {
-    case 1: contig_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    case 2: contig_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    case 4: contig_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    case 8: contig_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
-    default: contig_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
+    case 1: contig_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
+    case 2: contig_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
+    case 4: contig_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
+    case 8: contig_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
+    default: contig_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
   }
 }
 
@@ -622,7 +638,14 @@ template <typename T, typename CS, bool NEOX>
 void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w,
               const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
               int64_t qs, const RowPlan& pl, float n_f, float eps, bool mid) {
-  if (mid) {  // the staged form: the item kernel, any shape
+  switch (contig_blocks(pl)) {
+    case 1: contig_go_xd<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
+    case 2: contig_go_xd<T, CS, NEOX, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
+    case 4: contig_go_xd<T, CS, NEOX, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
+    case 8: contig_go_xd<T, CS, NEOX, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
+    default: break;
+  }
+  if (mid) {  // the staged form on any other shape: the item kernel
     switch (kk) {
       case 1: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 1, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
       case 2: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 2, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
@@ -630,13 +653,6 @@ void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16
       default: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 8, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
     }
     return;
-  }
-  switch (contig_blocks(pl)) {
-    case 1: contig_go_xd<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
-    case 2: contig_go_xd<T, CS, NEOX, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
-    case 4: contig_go_xd<T, CS, NEOX, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
-    case 8: contig_go_xd<T, CS, NEOX, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); return;
-    default: break;
   }
   if (dense_ok(pl, kk)) {
     switch (kk) {
