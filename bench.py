@@ -53,8 +53,10 @@ KERNEL_SOURCES = {
     "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
     "fused": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
-    "qk_norm_rope": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
-    "qk_kv": ("qrw_qknorm.hip", "qrw_device.h", "qrw_launch.h"),
+    "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
+                     "qrw_qknorm_gc_b.hip", "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),
+    "qk_kv": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip", "qrw_qknorm_gc_b.hip",
+              "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),
     "ew": ("qrw_ew.hip", "qrw_device.h", "qrw_launch.h"),
 }
 

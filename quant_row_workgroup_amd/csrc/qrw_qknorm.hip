@@ -1,261 +1,40 @@
-// qrw_qknorm.hip -- per-head QK RMSNorm + RoPE, in place on a packed QKV row
-// (gfx950).
-//
-// Definition: "TileLang tutorial, ch. 13", s2.4 (cross-module fusion: each
-// q/k value gets a weighted RMSNorm and then RoPE; the q/k columns are read
-// and written back and the v columns are not touched), with RMSNorm as in
-// s3.2.1 taken over each head's head_dim channels and RoPE as in s3.3.1 on
-// the head's tail span.
-//
-// Layout: a token row holds q_heads query heads, kv_heads key heads and
-// kv_heads value heads of head_dim channels.  Only the first
-// (q_heads + kv_heads) * head_dim channels are read and written.
-//
-// Mapping: the q/k part of a row is cut into chunks of 64*GC granules; one
-// wave64 handles one chunk of one token, lane l taking granules
-// chunk*64*GC + l + 64*g (g < GC), so every load and store instruction
-// covers 1 KiB contiguous.  A head is HG = head_dim/8 consecutive lanes and
-// chunks hold whole heads, so chunks are independent.  Per head: the sum of
-// squares is reduced with DPP inside the head's HG lanes; the rotation pairs
-// are in-lane (interleaved) or lane l and lane l ^ XR (NeoX, XR =
-// rope_dim/16) inside the head's rotated span.  A lane's position in its
-// head, hence its weight and table granule, is the same for all its granules.
-//
-// Arithmetic (binary32, one rounding at the output): u = x * w (exact for
-// 16-bit operands), the rotation as one fma per output, then * rstd.
-//
-// With the KV-cache write (the same section's fusion table: Q/K RMSNorm +
-// RoPE + quantised KV-cache write), the chunks cover the whole row: q heads
-// are written back in place as above, while k heads (after norm and
-// rotation) and v heads (as stored) are cast to E4M3FN with one scale per
-// (token, head), the per-token cast of s3.1.5 applied to a head: scale =
-// max(amax, 1e-4) / 448 from a DPP max inside the head's lanes, codes of the
-// correctly rounded binary32 quotient, written to cache row slots[t].
-#include <type_traits>
-
-#include "qrw_device.h"
-#include "qrw_launch.h"
+// qrw_qknorm.hip -- launchers of the per-head QK RMSNorm + RoPE kernels (and
+// the variant with the FP8 KV-cache write); the kernel is in qrw_qknorm.h.
+#include "qrw_qknorm.h"
 
 namespace qrw {
-
-// Destination of the quantised k and v heads (unused without the KV write).
-struct KvDest {
-  uint8_t* kc;             // [num_slots] rows of cache_stride bytes
-  uint8_t* vc;
-  float* ks;               // [num_slots, kv_heads]
-  float* vs;
-  const int64_t* slots;    // [tokens] or NULL (token t -> row t)
-  int64_t num_slots;
-  int64_t cache_stride;
-  int k_end;               // first v granule of a row
-  int kv_heads;
-};
-
-template <typename CS>
-__device__ __forceinline__ const char* qk_table_row(const void* base, int64_t t, int half) {
-  constexpr int bytes = std::is_same<CS, float>::value ? 4 : 2;
-  return static_cast<const char*>(base) + t * (int64_t)half * bytes;
-}
-
-template <typename T, typename CS, bool NEOX, int HG, int XR, int GC, bool KV>
-__global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
-    uint16_t* qkv, const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
-    const void* cosv, const void* sinv, int64_t tokens, int64_t stride, int ng, int q_gran,
-    int chunks, int s0, int half, float n_f, float eps, KvDest kv) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  const int64_t t = wave / chunks;
-  if (t >= tokens) return;  // wave-uniform
-  const int gb = (int)(wave - t * chunks) * kWave * GC;
-  uint16_t* row = qkv + t * stride;
-  const int j = lane & (HG - 1);        // granule position inside the head
-  const int js = j - s0;                // position inside the rotated span (< 0: outside)
-  const bool span = js >= 0;
-  int64_t slot = t;
-  bool cached = true;
-  if constexpr (KV) {
-    if (kv.slots) slot = kv.slots[t];
-    cached = slot >= 0 && slot < kv.num_slots;
-  }
-
-  u32x4 raw[GC];
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const int gi = gb + kWave * g + lane;
-    raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (gi < ng) raw[g] = ld16_stream(row + 8 * gi);
-  }
-  float fq[8], fk[8];
-  if (wq) {
-    widen8<T>(ld16(wq + 8 * j), fq);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) fq[e] = 1.0f;
-  }
-  if (wk) {
-    widen8<T>(ld16(wk + 8 * j), fk);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) fk[e] = 1.0f;
-  }
-  float c[8], sn[8];
-  const char* crow = qk_table_row<CS>(cosv, t, half);
-  const char* srow = qk_table_row<CS>(sinv, t, half);
-  if (NEOX) {
-    const int tg = span ? (js & (XR - 1)) : 0;
-    Table8<CS>::load(crow, tg, c);
-    Table8<CS>::load(srow, tg, sn);
-    if (js < XR) {  // first half of the span (or outside it): x c - x_partner s
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sn[e] = -sn[e];
-    }
-  } else {
-    float c4[4], s4[4];
-    Table4<CS>::load(crow, span ? js : 0, c4);
-    Table4<CS>::load(srow, span ? js : 0, s4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      c[k] = c4[k];
-      sn[k] = s4[k];
-    }
-  }
-
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const int gi = gb + kWave * g + lane;
-    float acc0 = 0.f, acc1 = 0.f;
-    acc0 = sumsq2(T{}, raw[g][0], acc0);
-    acc1 = sumsq2(T{}, raw[g][1], acc1);
-    acc0 = sumsq2(T{}, raw[g][2], acc0);
-    acc1 = sumsq2(T{}, raw[g][3], acc1);
-    const float ss = group_sum<HG>(acc0 + acc1);
-    const bool is_q = gi < q_gran;
-    const bool is_v = KV && gi >= kv.k_end;
-    const float rstd = is_v ? 1.0f : 1.0f / sqrtf(ss / n_f + eps);
-    float v[8];
-    widen8<T>(raw[g], v);
-    if (!is_v) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= is_q ? fq[e] : fk[e];
-    }
-    const bool rot = span && !is_v;
-    if (NEOX) {
-      float r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = fmaf(v[e], c[e], lane_xor<XR>(v[e]) * sn[e]);
-      if (rot) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = r[e];
-      }
-    } else if (rot) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = v[2 * k], x1 = v[2 * k + 1];
-        v[2 * k] = fmaf(x0, c[k], -(x1 * sn[k]));
-        v[2 * k + 1] = fmaf(x1, c[k], x0 * sn[k]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= rstd;
-    if constexpr (KV) {
-      float m = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-      const float am = fmaxf(group_max<HG>(m), 1e-4f);
-      if (gi < ng) {
-        if (is_q) {
-          st16_stream(row + 8 * gi, narrow8<T>(v));
-        } else if (cached) {
-          const float scale = am / 448.0f;
-          const float y = 1.0f / scale;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
-          const int hg = is_v ? gi - kv.k_end : gi - q_gran;  // granule inside the k (v) part
-          st8_stream((is_v ? kv.vc : kv.kc) + slot * kv.cache_stride + 8 * hg, fp8x8(v));
-          if (j == 0) (is_v ? kv.vs : kv.ks)[slot * kv.kv_heads + hg / HG] = scale;
-        }
-      }
-    } else {
-      if (gi < ng) st16_stream(row + 8 * gi, narrow8<T>(v));
-    }
-  }
-}
-
-// ------------------------------------------------------------------ launch
 namespace {
 
-constexpr int kQkChunk = 2;  // granules per lane per wave
-
-// Everything a launch needs besides the template arguments.
-struct QkArgs {
-  dim3 grid;
-  hipStream_t st;
-  uint16_t* x;
-  const uint16_t* wq;
-  const uint16_t* wk;
-  const void* c;
-  const void* s;
-  int64_t tokens, stride;
-  int ng, qg, chunks, s0, half;
-  float n_f, eps;
-  KvDest kv;
-};
-
-template <typename T, typename CS, bool NEOX, int HG, int XR>
-void qk_go(const QkArgs& a) {
-  if (a.kv.kc)
-    qk_norm_rope_kernel<T, CS, NEOX, HG, XR, kQkChunk, true><<<a.grid, kBlock, 0, a.st>>>(
-        a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
-        a.n_f, a.eps, a.kv);
-  else
-    qk_norm_rope_kernel<T, CS, NEOX, HG, XR, kQkChunk, false><<<a.grid, kBlock, 0, a.st>>>(
-        a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
-        a.n_f, a.eps, a.kv);
-}
-
-template <typename T, typename CS, bool NEOX, int HG>
-void qk_go_xr(int xr, const QkArgs& a) {
-  if constexpr (!NEOX) {
-    qk_go<T, CS, NEOX, HG, 1>(a);
-  } else {
-    switch (xr) {
-      case 1: qk_go<T, CS, NEOX, HG, 1>(a); break;
-      case 2: qk_go<T, CS, NEOX, HG, 2>(a); break;
-      case 4: qk_go<T, CS, NEOX, HG, 4>(a); break;
-      case 8:  // rope_dim <= head_dim keeps xr <= hg / 2
-        if constexpr (HG >= 16) qk_go<T, CS, NEOX, HG, 8>(a);
-        break;
-      default:
-        if constexpr (HG >= 32) qk_go<T, CS, NEOX, HG, 16>(a);
-        break;
-    }
+// Granules per lane per wave for a row of ng granules: one chunk for the
+// whole row when it has at most 12 * 64 granules (the smallest width that
+// holds it), else the widest width that splits the row into equal chunks,
+// else 8 (the last chunk of a row is then partly idle).  Measured on MI355X:
+// one wave per token, or equal chunks, are fastest; idle lane slots and
+// widths above 12 (register pressure) cost time.
+int pick_chunk(int ng) {
+  static const int kWidths[] = {1, 2, 3, 4, 5, 6, 8, 10, 12};
+  const int need = (ng + kWave - 1) / kWave;
+  if (need <= 12) {
+    for (int c : kWidths)
+      if (c >= need) return c;
   }
+  for (int i = 8; i >= 0; --i)
+    if (ng % (kWave * kWidths[i]) == 0) return kWidths[i];
+  return 8;
 }
-
-template <typename T, typename CS, bool NEOX>
-void qk_go_hg(int hg, int xr, const QkArgs& a) {
-  switch (hg) {
-    case 8: qk_go_xr<T, CS, NEOX, 8>(xr, a); break;
-    case 16: qk_go_xr<T, CS, NEOX, 16>(xr, a); break;
-    default: qk_go_xr<T, CS, NEOX, 32>(xr, a); break;
-  }
-}
-
-}  // namespace
-
-namespace {
 
 hipError_t qk_launch(void* qkv, const void* q_weight, const void* k_weight, const void* cos,
                      const void* sin, int64_t tokens, int64_t q_heads, int64_t kv_heads,
                      int64_t head_dim, int64_t rope_dim, int64_t stride, int dtype, int cs_dtype,
                      bool neox, float eps, KvDest kv, hipStream_t stream) {
-  const int hg = (int)(head_dim / 8);
-  const int xr = (int)(rope_dim / 16);
-  const int64_t heads = kv.kc ? q_heads + 2 * kv_heads : q_heads + kv_heads;
   QkArgs a;
-  a.ng = (int)(heads * hg);
-  a.qg = (int)(q_heads * hg);
-  const int per_wave = kWave * kQkChunk;
+  a.hg = (int)(head_dim / 8);
+  a.xr = (int)(rope_dim / 16);
+  const int64_t heads = kv.kc ? q_heads + 2 * kv_heads : q_heads + kv_heads;
+  a.ng = (int)(heads * a.hg);
+  a.qg = (int)(q_heads * a.hg);
+  const int gc = pick_chunk(a.ng);
+  const int per_wave = kWave * gc;
   a.chunks = (a.ng + per_wave - 1) / per_wave;
   a.s0 = (int)((head_dim - rope_dim) / 8);
   a.half = (int)(rope_dim / 2);
@@ -271,25 +50,22 @@ hipError_t qk_launch(void* qkv, const void* q_weight, const void* k_weight, cons
   a.stride = stride;
   a.n_f = (float)head_dim;
   a.eps = eps;
-  kv.k_end = (int)((q_heads + kv_heads) * hg);
+  kv.k_end = (int)((q_heads + kv_heads) * a.hg);
   kv.kv_heads = (int)kv_heads;
   a.kv = kv;
-  if (dtype == 1) {
-    if (cs_dtype == 3) {
-      if (neox) qk_go_hg<F16, float, true>(hg, xr, a);
-      else qk_go_hg<F16, float, false>(hg, xr, a);
-    } else {
-      if (neox) qk_go_hg<F16, F16, true>(hg, xr, a);
-      else qk_go_hg<F16, F16, false>(hg, xr, a);
-    }
-  } else {
-    if (cs_dtype == 3) {
-      if (neox) qk_go_hg<BF16, float, true>(hg, xr, a);
-      else qk_go_hg<BF16, float, false>(hg, xr, a);
-    } else {
-      if (neox) qk_go_hg<BF16, BF16, true>(hg, xr, a);
-      else qk_go_hg<BF16, BF16, false>(hg, xr, a);
-    }
+  a.dtype = dtype;
+  a.cs_dtype = cs_dtype;
+  a.neox = neox;
+  switch (gc) {
+    case 1: qk_run_gc1(a); break;
+    case 2: qk_run_gc2(a); break;
+    case 3: qk_run_gc3(a); break;
+    case 4: qk_run_gc4(a); break;
+    case 5: qk_run_gc5(a); break;
+    case 6: qk_run_gc6(a); break;
+    case 8: qk_run_gc8(a); break;
+    case 10: qk_run_gc10(a); break;
+    default: qk_run_gc12(a); break;
   }
   return hipGetLastError();
 }
