@@ -47,8 +47,17 @@ __device__ __forceinline__ void st_row_stream(uint16_t* p, int gi, int n, u32x4 
     st16_stream(p + 8 * gi, g);
 }
 
+// Occupancy floor (waves per SIMD) of the one-wave kernels: 4 (<= 128 VGPRs)
+// up to 8 granules per lane, 2 for 16 (the row alone is 64 VGPRs).  The
+// ragged 8-granule form runs at 3: measured faster than at 4 on 4096 x 4095
+// (15.3 vs 16.5 us).  Without a floor the compiler's choice swings between ~80
+// and ~250 VGPRs from one instance to the next.  The row-block kernels ask for
+// 4.
+template <int GPL, bool TAIL>
+constexpr int kNormWaves = GPL <= 4 ? 4 : GPL == 8 ? (TAIL ? 3 : 4) : 2;
+
 template <typename T, int GPL, bool FULL, bool TAIL>
-__global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWaves<GPL, TAIL>))) void rmsnorm_kernel(const uint16_t* x,
                                                          const uint16_t* __restrict__ w,
                                                          uint16_t* y, int64_t rows, int ng,
                                                          int n, int64_t xs, int64_t ys,
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const uint16_t* x,
 }
 
 template <typename T, int GPL, bool FULL, bool TAIL>
-__global__ __launch_bounds__(kBlock) void layernorm_kernel(const uint16_t* x,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWaves<GPL, TAIL>))) void layernorm_kernel(const uint16_t* x,
                                                            const uint16_t* __restrict__ gam,
                                                            const uint16_t* __restrict__ bet,
                                                            uint16_t* y, int64_t rows, int ng,
@@ -216,7 +225,7 @@ __device__ __forceinline__ float block_sum(float v, float* slot) {
 }
 
 template <typename T, int W, int GPL, bool TAIL>
-__global__ __launch_bounds__(kWave* W) void rmsnorm_rowblock_kernel(
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int ng, int n, int64_t xs,
     int64_t ys, float n_f, float eps) {
   __shared__ float slot[W];
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(kWave* W) void rmsnorm_rowblock_kernel(
 }
 
 template <typename T, int W, int GPL, bool TAIL>
-__global__ __launch_bounds__(kWave* W) void layernorm_rowblock_kernel(
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
     uint16_t* y, int ng, int n, int64_t xs, int64_t ys, float n_f, float eps) {
   __shared__ float slot0[W], slot1[W], slot2[W];
