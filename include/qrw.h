@@ -22,15 +22,18 @@
  * Layout.  Row-major.  A "row" (or a token) is `n` contiguous elements; rows
  *   are `*_row_stride` ELEMENTS apart.  Heads are packed inside a token:
  *   head h occupies elements [h*head_dim, (h+1)*head_dim).
- * Granules.  Rows are moved in 16-byte granules, so: `n` (or head_dim) is a
- *   multiple of 8, row strides are multiples of 8 elements, and every tensor
- *   base pointer is 16-byte aligned.  Weight vectors and tables are packed.
- *   With zero rows (tokens) nothing is read or written and pointers may be
- *   NULL.
+ * Granules.  Rows are moved in 16-byte granules, so row strides are
+ *   multiples of 8 elements and every tensor base pointer is 16-byte aligned;
+ *   row lengths are multiples of 8 except where an entry point says
+ *   otherwise (rmsnorm_fwd, layernorm_fwd and the elementwise family take any
+ *   length).  Weight vectors and tables are packed.  With zero rows (tokens,
+ *   elements) nothing is read or written and pointers may be NULL.
  * Dtypes.  `dtype` is QRW_F16 or QRW_BF16 and applies to x, y and the weight
- *   vectors.  RoPE tables have `cs_dtype`, either QRW_F32 or equal to dtype.
- * Numerics.  All arithmetic is binary32; every 16-bit or FP8 output is
- *   rounded once, to nearest-even, from the binary32 result.
+ *   vectors (the elementwise family also takes QRW_F32).  RoPE tables have
+ *   `cs_dtype`, either QRW_F32 or equal to dtype.
+ * Numerics.  Arithmetic is binary32 (binary64 for the elementwise family's
+ *   16-bit outputs); every 16-bit or FP8 output is rounded once, to
+ *   nearest-even.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *   asynchronous on it; argument errors are reported before anything is
  *   enqueued.
