@@ -23,6 +23,10 @@
 #include "qrw_device.h"
 #include "qrw_launch.h"
 
+#ifndef QRW_QUANT_GATHER
+#define QRW_QUANT_GATHER 1
+#endif
+
 namespace qrw {
 
 template <typename T, int GPL, bool FULL, int L>
@@ -30,6 +34,10 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
                                                                  float* scales, int64_t rows,
                                                                  int ng, int64_t xs, int64_t qs,
                                                                  int64_t groups) {
+  // When a whole row has at most 64 groups (GPL <= L), lane j collects the
+  // scale of group j (from any lane of that group, by a lane permute) and the
+  // row's scales leave in one contiguous store instead of one store per group.
+  constexpr bool kGather = FULL && GPL <= L && QRW_QUANT_GATHER;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -42,6 +50,7 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
     if (FULL || gi < ng) raw[g] = ld16_stream(xr + 8 * gi);
   }
+  float mine = 0.0f;
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
@@ -51,14 +60,26 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
 #pragma unroll
     for (int e = 0; e < 8; e += 2) m = fmaxf(m, fmaxf(fabsf(v[e]), fabsf(v[e + 1])));
     const float am = fmaxf(group_max<L>(m), 1e-4f);  // groups never straddle the row end
+    const float scale = am / 448.0f;
+    if constexpr (kGather) {
+      // groups g*(64/L) .. of this step sit in lane blocks of L; lane j takes
+      // group j = g*(64/L) + q from lane q*L
+      constexpr int kPer = kWave / L;
+      const int src = (lane % kPer) * L;
+      const float got = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, scale)));
+      if (lane / kPer == g) mine = got;
+    }
     if (FULL || gi < ng) {
-      const float scale = am / 448.0f;
       const float y = 1.0f / scale;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
       st8_stream(qr + 8 * gi, fp8x8(v));
-      if ((lane & (L - 1)) == 0) scales[row * groups + gi / L] = scale;
+      if (!kGather && (lane & (L - 1)) == 0) scales[row * groups + gi / L] = scale;
     }
+  }
+  if constexpr (kGather) {
+    if (lane < GPL * (kWave / L)) scales[row * groups + lane] = mine;
   }
 }
 
