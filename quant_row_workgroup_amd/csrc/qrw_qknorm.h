@@ -67,7 +67,7 @@ template <typename T, typename CS, bool NEOX, int HG, int XR, int GC, bool KV>
 __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
     uint16_t* qkv, const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
     const void* cosv, const void* sinv, int64_t tokens, int64_t stride, int ng, int q_gran,
-    int chunks, int s0, int half, float n_f, float eps, KvDest kv) {
+    int chunks, int s0, int half, float inv_n, float eps, KvDest kv) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   const int64_t t = wave / chunks;
@@ -137,7 +137,16 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
     const float ss = group_sum<HG>(acc0 + acc1);
     const bool is_q = gi < q_gran;
     const bool is_v = KV && gi >= kv.k_end;
-    const float rstd = is_v ? 1.0f : 1.0f / sqrtf(ss / n_f + eps);
+    // inv_n = 1 / head_dim, exact (head_dim is a power of two): ss * inv_n == ss / head_dim
+    // 1/sqrt(mean + eps) once per head and granule (GC times per lane): the
+    // hardware reciprocal square root refined by one Newton-Raphson step,
+    // y <- y (3/2 - (v/2) y^2), good to about one binary32 ulp.  A correctly
+    // rounded 1.0f / sqrtf() costs a division sequence per head, which measured
+    // 7% slower on the 4096 x (32+8+8) x 128 workload.
+    const float mv = ss * inv_n + eps;
+    float yr = __builtin_amdgcn_rsqf(mv);
+    yr = yr * fmaf(-0.5f * mv * yr, yr, 1.5f);
+    const float rstd = is_v ? 1.0f : yr;
     float v[8];
     widen8<T>(raw[g], v);
     if (!is_v) {
@@ -199,7 +208,7 @@ struct QkArgs {
   const void* s;
   int64_t tokens, stride;
   int ng, qg, chunks, s0, half;
-  float n_f, eps;
+  float inv_n, eps;
   KvDest kv;
   int dtype, cs_dtype, hg, xr;
   bool neox;
@@ -210,11 +219,11 @@ void qk_go(const QkArgs& a) {
   if (a.kv.kc)
     qk_norm_rope_kernel<T, CS, NEOX, HG, XR, GC, true><<<a.grid, kBlock, 0, a.st>>>(
         a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
-        a.n_f, a.eps, a.kv);
+        a.inv_n, a.eps, a.kv);
   else
     qk_norm_rope_kernel<T, CS, NEOX, HG, XR, GC, false><<<a.grid, kBlock, 0, a.st>>>(
         a.x, a.wq, a.wk, a.c, a.s, a.tokens, a.stride, a.ng, a.qg, a.chunks, a.s0, a.half,
-        a.n_f, a.eps, a.kv);
+        a.inv_n, a.eps, a.kv);
 }
 
 template <typename T, typename CS, bool NEOX, int HG, int GC>

@@ -48,7 +48,7 @@ hipError_t qk_launch(void* qkv, const void* q_weight, const void* k_weight, cons
   a.s = sin;
   a.tokens = tokens;
   a.stride = stride;
-  a.n_f = (float)head_dim;
+  a.inv_n = 1.0f / (float)head_dim;  // exact: head_dim is 64, 128 or 256
   a.eps = eps;
   kv.k_end = (int)((q_heads + kv_heads) * a.hg);
   kv.kv_heads = (int)kv_heads;
