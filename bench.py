@@ -51,7 +51,8 @@ KERNEL_SOURCES = {
     "rmsnorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "layernorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
-    "fused": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
+    "fused": ("qrw_rope.hip", "qrw_fused_tail.hip", "qrw_plan.h", "qrw_device.h",
+              "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
                      "qrw_qknorm_gc_b.hip", "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),

@@ -13,6 +13,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace qrw {
@@ -164,6 +165,19 @@ struct Table8<BF16> {
     widen8<BF16>(ld16(reinterpret_cast<const uint16_t*>(row) + 8 * s), v);
   }
 };
+
+// Start of token t's row of a packed [tokens, half] cos or sin table.
+template <typename CS>
+__device__ __forceinline__ const char* table_row(const void* base, int64_t t, int half) {
+  constexpr int bytes = std::is_same<CS, float>::value ? 4 : 2;
+  return static_cast<const char*>(base) + t * (int64_t)half * bytes;
+}
+
+// Round eight binary32 values to the 16-bit format T (nearest-even) and back.
+template <typename T>
+__device__ __forceinline__ void round8(float (&v)[8]) {
+  widen8<T>(narrow8<T>(v), v);
+}
 
 // ----------------------------------------------------------- wave64 reductions
 template <int CTRL>

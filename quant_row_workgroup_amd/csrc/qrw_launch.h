@@ -35,6 +35,18 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
                                    float eps, bool round_mid, hipStream_t stream);
 
+// The fused operator when heads rotate only their tail span, in the
+// contiguous layout (qrw_fused_tail.hip): applies when rope_dim < head_dim,
+// both powers of two, 16 <= rope_dim <= 256, and the row is 1, 2, 4 or 8
+// blocks of 512 channels.
+bool fused_tail_ok(int64_t heads, int64_t head_dim, int64_t rope_dim);
+hipError_t launch_rmsnorm_rope_fp8_tail(const void* x, const void* w, const void* cos,
+                                        const void* sin, uint8_t* q, float* scales,
+                                        int64_t tokens, int64_t heads, int64_t head_dim,
+                                        int64_t rope_dim, int64_t xs, int64_t qs, int dtype,
+                                        int cs_dtype, bool neox, float eps, bool round_mid,
+                                        hipStream_t stream);
+
 hipError_t launch_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows,
                                 int64_t n, int64_t group, int64_t xs, int64_t qs, int dtype,
                                 hipStream_t stream);

@@ -35,12 +35,6 @@
 
 namespace qrw {
 
-template <typename CS>
-__device__ __forceinline__ const char* table_row(const void* base, int64_t t, int half) {
-  constexpr int bytes = std::is_same<CS, float>::value ? 4 : 2;
-  return static_cast<const char*>(base) + t * (int64_t)half * bytes;
-}
-
 // Rotate one item in place.  NeoX: channel e of A pairs with channel e of B,
 // using table entry e.  Interleaved: channels (2k, 2k+1) of A use entry k and
 // those of B use entry 4 + k.  First of a pair: x_a c - x_b s; second:
@@ -130,12 +124,6 @@ __global__ __launch_bounds__(kBlock) void rope_kernel(const uint16_t* x, const v
 }
 
 // ------------------------------------------------------------------ fused
-// Round eight binary32 values to the 16-bit format T (nearest-even) and back.
-template <typename T>
-__device__ __forceinline__ void round8(float (&v)[8]) {
-  widen8<T>(narrow8<T>(v), v);
-}
-
 // MID: the staged form of the page's fused dataflow, which writes the
 // normalised row back to shared memory in x's dtype and rotates it there: the
 // normalised values x * rstd * w and the rotated values are each rounded to
@@ -712,6 +700,10 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
                                    float eps, bool round_mid, hipStream_t stream) {
   const RowPlan pl = make_plan(heads, head_dim, rope_dim);
+  if (contig_blocks(pl) == 0 && fused_tail_ok(heads, head_dim, rope_dim))
+    return launch_rmsnorm_rope_fp8_tail(x, w, cos, sin, q, scales, tokens, heads, head_dim,
+                                        rope_dim, xs, qs, dtype, cs_dtype, neox, eps, round_mid,
+                                        stream);
   const int kk = items_per_lane(pl.n_items, 8);
   const dim3 grid((unsigned)((tokens + kRowsPerBlock - 1) / kRowsPerBlock));
   const auto* xp = static_cast<const uint16_t*>(x);

@@ -119,6 +119,9 @@ WORKLOADS = {
                                                    head_dim=128, rope_dim=128, dtype="bf16",
                                                    cs_dtype="bf16", eps=1e-6, neox=True,
                                                    staged=True, seed=5),
+    "rmsnorm_rope_fp8_4096x4096_bf16_onehead": dict(op="fused", tokens=4096, heads=1,
+                                                    head_dim=4096, rope_dim=128, dtype="bf16",
+                                                    cs_dtype="bf16", eps=1e-6, neox=True, seed=5),
     "rmsnorm_rope_fp8_4096x4096_bf16": dict(op="fused", tokens=4096, heads=32, head_dim=128,
                                             rope_dim=128, dtype="bf16", cs_dtype="bf16",
                                             eps=1e-6, neox=True, seed=5),

@@ -151,3 +151,32 @@ def assert_scales(got, want, rtol=1e-6, what=""):
     rel = np.abs(got - want) / np.abs(want)
     assert rel.max() <= rtol, f"{what}: scale rel err {rel.max():.3e}"
     return float(rel.max())
+
+
+def e4m3_boundaries():
+    """Decision boundaries of round-to-nearest into E4M3FN: the midpoints between
+    consecutive non-negative finite values (float64)."""
+    v = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    v = np.unique(v.numpy())
+    return (v[1:] + v[:-1]) / 2
+
+
+def assert_codes_away_from_ties(got, want, quotient, rel=2.0 ** -20, what=""):
+    """FP8 codes equal wherever the exact quotient z / scale lies farther than
+    ``rel`` (relative) from an E4M3 rounding boundary; within that distance of a
+    boundary either neighbour is a correct rounding at the precision the binary32
+    row statistics resolve.  Never more than one step apart."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    d = np.abs(ord8(got) - ord8(want))
+    assert d.max() <= 1 if d.size else True, f"{what}: codes {int(d.max())} steps apart"
+    b = e4m3_boundaries()
+    q = np.abs(np.asarray(quotient, dtype=np.float64))
+    i = np.clip(np.searchsorted(b, q), 1, len(b) - 1)
+    gap = np.minimum(np.abs(q - b[i - 1]), np.abs(q - b[i]))
+    near = gap <= rel * np.maximum(q, 2.0 ** -9)
+    bad = (d != 0) & ~near
+    assert not bad.any(), (f"{what}: {int(bad.sum())} codes differ away from a rounding "
+                           f"boundary, e.g. at {np.argwhere(bad)[0]}")
+    return {"exact_frac": float((d == 0).mean()), "near_tie_frac": float(near.mean()),
+            "max_step": int(d.max()) if d.size else 0}
