@@ -7,8 +7,10 @@
 // Mapping: one wave64 per row, four rows per 256-thread workgroup.  Lane l
 // owns granules l, l+64, l+128, ... (GPL of them), so each load instruction
 // of a wave covers 1 KiB of contiguous row.  Row statistics: eight per-lane
-// partial sums (one per element slot of a granule, a shallow serial chain),
-// a fixed pairwise tree, then the wave64 DPP reduction.
+// partial sums (a shallow serial chain each), a fixed pairwise tree, then the
+// wave64 DPP reduction.  The one-wave RMSNorm forms its sum of squares on the
+// packed 16-bit pairs with v_dot2 (the products are exact in binary32); the
+// other kernels widen and use fma.
 //
 // Cache hints (measured on MI355X at 4096 x 4096): the rows are touched once
 // per launch, so outputs are written with non-temporal stores; LayerNorm also
@@ -22,44 +24,42 @@
 
 namespace qrw {
 
-// The valid elements of granule gi of a row of n elements: 8, except in the
-// partial last granule of a row whose length is not a multiple of 8 (TAIL).
-template <bool TAIL>
-__device__ __forceinline__ int granule_count(int gi, int n) {
-  if constexpr (TAIL) return min(max(n - 8 * gi, 0), 8);
-  return 8;
+// A row whose length is not a multiple of 8 ends in one partial granule,
+// index nfull = n >> 3 (TAIL).  Every other granule is whole and takes a full
+// 16-byte access under a plain `gi < nfull` mask; the partial one is held in
+// a register pair of its own by the thread whose granule sequence it ends, so
+// that thread's accumulation order is the same as if it sat in the array.
+// Whole granule gi of a row, or zeros where gi >= nfull (requires nfull >= 1).
+// Branch-free: a masked lane re-reads the row's last whole granule, which its
+// neighbours load anyway, and drops it.  (A branch per granule makes the
+// compiler copy every live register at each join.)
+template <bool STREAM>
+__device__ __forceinline__ u32x4 ld_masked(const uint16_t* p, int gi, int nfull) {
+  const bool in = gi < nfull;
+  const uint16_t* q = p + 8 * (in ? gi : nfull - 1);
+  const u32x4 v = STREAM ? ld16_stream(q) : ld16(q);
+  return in ? v : (u32x4){0u, 0u, 0u, 0u};
 }
+
 template <bool TAIL>
-__device__ __forceinline__ u32x4 ld_row(const uint16_t* p, int gi, int n) {
-  if (TAIL && 8 * gi + 8 > n) return ld_partial(p + 8 * gi, n - 8 * gi);
-  return ld16(p + 8 * gi);
-}
-template <bool TAIL>
-__device__ __forceinline__ u32x4 ld_row_stream(const uint16_t* p, int gi, int n) {
-  if (TAIL && 8 * gi + 8 > n) return ld_partial(p + 8 * gi, n - 8 * gi);
-  return ld16_stream(p + 8 * gi);
-}
-template <bool TAIL>
-__device__ __forceinline__ void st_row_stream(uint16_t* p, int gi, int n, u32x4 g) {
-  if (TAIL && 8 * gi + 8 > n)
-    st_partial(p + 8 * gi, g, n - 8 * gi);
-  else
-    st16_stream(p + 8 * gi, g);
+__device__ __forceinline__ u32x4 ld_tail(const uint16_t* p, bool mine, int nfull, int n) {
+  if (TAIL && mine) return ld_partial(p + 8 * nfull, n & 7);
+  return (u32x4){0u, 0u, 0u, 0u};
 }
 
 // Occupancy floor (waves per SIMD) of the one-wave kernels: 4 (<= 128 VGPRs)
-// up to 8 granules per lane, 2 for 16 (the row alone is 64 VGPRs).  The
-// ragged 8-granule form runs at 3: measured faster than at 4 on 4096 x 4095
-// (15.3 vs 16.5 us).  Without a floor the compiler's choice swings between ~80
+// up to 8 granules per lane, 2 for 16 (the row alone is 64 VGPRs).  A launch
+// of 4096 rows is 4 waves per SIMD, so below 4 a quarter of the rows wait for
+// a second round.  Without a floor the compiler's choice swings between ~80
 // and ~250 VGPRs from one instance to the next.  The row-block kernels ask for
 // 4.
 template <int GPL, bool TAIL>
-constexpr int kNormWaves = GPL <= 4 ? 4 : GPL == 8 ? (TAIL ? 3 : 4) : 2;
+constexpr int kNormWaves = GPL <= 8 ? 4 : 2;
 
 template <typename T, int GPL, bool FULL, bool TAIL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWaves<GPL, TAIL>))) void rmsnorm_kernel(const uint16_t* x,
                                                          const uint16_t* __restrict__ w,
-                                                         uint16_t* y, int64_t rows, int ng,
+                                                         uint16_t* y, int64_t rows, int nfull,
                                                          int n, int64_t xs, int64_t ys,
                                                          float n_f, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -67,60 +67,101 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   if (row >= rows) return;  // wave-uniform
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
+  const bool mine = TAIL && lane == (nfull & (kWave - 1));
 
   u32x4 raw[GPL];
   u32x4 wr[GPL];
+  const bool any = FULL || nfull > 0;  // wave-uniform
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (FULL || gi < ng) raw[g] = ld_row<TAIL>(xr, gi, n);
+    if (any) raw[g] = FULL ? ld16(xr + 8 * gi) : ld_masked<false>(xr, gi, nfull);
   }
-  if (w) {
+  const u32x4 xt = ld_tail<TAIL>(xr, mine, nfull, n);
+  // The weights are loaded with x, except in the ragged form, which reads
+  // them at output time (measured faster there: 12.9 against 14.4 us on
+  // 4096 x 4095 bf16; the other way round costs on whole rows).
+  constexpr bool kPreW = !TAIL;
+  if (kPreW && w) {
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave + lane;
       wr[g] = (u32x4){0u, 0u, 0u, 0u};
-      if (FULL || gi < ng) wr[g] = ld_row<TAIL>(w, gi, n);
+      if (any) wr[g] = FULL ? ld16(w + 8 * gi) : ld_masked<false>(w, gi, nfull);
     }
   }
 
+  // sum of squares on the packed pairs (v_dot2: the 16-bit products are exact)
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
-    float v[8];
-    widen8<T>(raw[g], v);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+    for (int k = 0; k < 4; ++k) acc[(4 * g + k) & 7] = sumsq2(T{}, raw[g][k], acc[(4 * g + k) & 7]);
+  }
+  if (TAIL) {  // the partial granule ends its lane's sequence
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[(4 * GPL + k) & 7] = sumsq2(T{}, xt[k], acc[(4 * GPL + k) & 7]);
   }
   const float ss = wave_sum(tree8(acc));
   const float rstd = 1.0f / sqrtf(ss / n_f + eps);
 
+  auto finish = [&](u32x4 xg, u32x4 wg) {
+    float v[8];
+    widen8<T>(xg, v);
+    if (w) {
+      float wv[8];
+      widen8<T>(wg, wv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
+    }
+    return narrow8<T>(v);
+  };
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
-    if (FULL || gi < ng) {
-      float v[8];
-      widen8<T>(raw[g], v);
-      if (w) {
-        float wv[8];
-        widen8<T>(wr[g], wv);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
-      }
-      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
-    }
+    if (FULL || gi < nfull)
+      st16_stream(yr + 8 * gi,
+                  finish(raw[g], !w ? (u32x4){0u, 0u, 0u, 0u} : kPreW ? wr[g] : ld16(w + 8 * gi)));
   }
+  if (mine) st_partial(yr + 8 * nfull, finish(xt, ld_tail<TAIL>(w, w != nullptr, nfull, n)), n & 7);
+}
+
+// LayerNorm's centred pass over one granule: the first cnt elements are
+// centred on mu0 and accumulated; padding elements are not centred.
+__device__ __forceinline__ void centred_moments(const float (&v)[8], int cnt, float mu0,
+                                                float (&acc1)[8], float (&acc2)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float d = k < cnt ? v[k] - mu0 : 0.0f;
+    acc1[k] += d;
+    acc2[k] = fmaf(d, d, acc2[k]);
+  }
+}
+
+// y = ((x - mu0) - r) * rstd * gamma + beta for one granule; absent gamma is
+// 1, absent beta 0.
+template <typename T>
+__device__ __forceinline__ u32x4 layernorm_out(u32x4 xg, u32x4 gg, u32x4 bg, bool has_g,
+                                               bool has_b, float mu0, float r, float rstd) {
+  float v[8], gv[8], bv[8];
+  widen8<T>(xg, v);
+  widen8<T>(gg, gv);
+  widen8<T>(bg, bv);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    v[k] = fmaf(((v[k] - mu0) - r) * rstd, has_g ? gv[k] : 1.0f, has_b ? bv[k] : 0.0f);
+  return narrow8<T>(v);
 }
 
 template <typename T, int GPL, bool FULL, bool TAIL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWaves<GPL, TAIL>))) void layernorm_kernel(const uint16_t* x,
                                                            const uint16_t* __restrict__ gam,
                                                            const uint16_t* __restrict__ bet,
-                                                           uint16_t* y, int64_t rows, int ng,
+                                                           uint16_t* y, int64_t rows, int nfull,
                                                            int n, int64_t xs, int64_t ys,
                                                            float n_f, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -128,14 +169,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   if (row >= rows) return;
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
+  const bool mine = TAIL && lane == (nfull & (kWave - 1));
 
   u32x4 raw[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (FULL || gi < ng) raw[g] = ld_row_stream<TAIL>(xr, gi, n);
+    if (FULL || gi < nfull) raw[g] = ld16_stream(xr + 8 * gi);
   }
+  const u32x4 xt = ld_tail<TAIL>(xr, mine, nfull, n);
 
   // Mean in two parts: mu0 is the binary32 mean; the mean r of the residuals
   // x - mu0 comes out of the same register pass as the centred second moment,
@@ -144,9 +187,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   // their accuracy.
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
+  for (int g = 0; g < GPL + (TAIL ? 1 : 0); ++g) {
     float v[8];
-    widen8<T>(raw[g], v);
+    widen8<T>(g < GPL ? raw[g] : xt, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] += v[k];
   }
@@ -158,46 +201,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
-    if (FULL || gi < ng) {
-      float v[8];
-      widen8<T>(raw[g], v);
-      const int cnt = granule_count<TAIL>(gi, n);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float d = k < cnt ? v[k] - mu0 : 0.0f;  // the padding is not centred
-        acc1[k] += d;
-        acc2[k] = fmaf(d, d, acc2[k]);
-      }
-    }
+    float v[8];
+    widen8<T>(raw[g], v);
+    centred_moments(v, FULL || gi < nfull ? 8 : 0, mu0, acc1, acc2);
+  }
+  if (mine) {
+    float v[8];
+    widen8<T>(xt, v);
+    centred_moments(v, n & 7, mu0, acc1, acc2);
   }
   const float r = wave_sum(tree8(acc1)) / n_f;
   const float m2 = wave_sum(tree8(acc2)) / n_f;
   const float var = fmaxf(fmaf(-r, r, m2), 0.0f);  // mean((x - mu0 - r)^2)
   const float rstd = 1.0f / sqrtf(var + eps);
 
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
-    if (FULL || gi < ng) {
-      float v[8], gv[8], bv[8];
-      widen8<T>(raw[g], v);
-      if (gam) {
-        widen8<T>(ld_row<TAIL>(gam, gi, n), gv);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) gv[k] = 1.0f;
-      }
-      if (bet) {
-        widen8<T>(ld_row<TAIL>(bet, gi, n), bv);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = fmaf(((v[k] - mu0) - r) * rstd, gv[k], bv[k]);
-      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
-    }
+    if (FULL || gi < nfull)
+      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
+                                                bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
+                                                bet != nullptr, mu0, r, rstd));
   }
+  if (mine)
+    st_partial(yr + 8 * nfull,
+               layernorm_out<T>(xt, ld_tail<TAIL>(gam, gam != nullptr, nfull, n),
+                                ld_tail<TAIL>(bet, bet != nullptr, nfull, n), gam != nullptr,
+                                bet != nullptr, mu0, r, rstd),
+               n & 7);
 }
 
 // ------------------------------------------------------ rows of many waves
@@ -224,74 +256,90 @@ __device__ __forceinline__ float block_sum(float v, float* slot) {
   return s[0];
 }
 
+// RMSNorm output of one granule: (x * w) * rstd, or x * rstd without weights.
+template <typename T>
+__device__ __forceinline__ u32x4 rmsnorm_granule(u32x4 xg, u32x4 wg, bool has_w, float rstd) {
+  float v[8];
+  widen8<T>(xg, v);
+  if (has_w) {
+    float wv[8];
+    widen8<T>(wg, wv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
+  }
+  return narrow8<T>(v);
+}
+
 template <typename T, int W, int GPL, bool TAIL>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_rowblock_kernel(
-    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int ng, int n, int64_t xs,
+    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int nfull, int n, int64_t xs,
     int64_t ys, float n_f, float eps) {
   __shared__ float slot[W];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
+  const bool mine = TAIL && t == nfull % (kWave * W);
   u32x4 raw[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave * W + t;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (gi < ng) raw[g] = ld_row<TAIL>(xr, gi, n);
+    if (gi < nfull) raw[g] = ld16(xr + 8 * gi);
   }
+  const u32x4 xt = ld_tail<TAIL>(xr, mine, nfull, n);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
+  for (int g = 0; g < GPL + (TAIL ? 1 : 0); ++g) {
     float v[8];
-    widen8<T>(raw[g], v);
+    widen8<T>(g < GPL ? raw[g] : xt, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
   }
   const float ss = block_sum<W>(tree8(acc), slot);
   const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave * W + t;
-    if (gi < ng) {
-      float v[8];
-      widen8<T>(raw[g], v);
-      if (w) {
-        float wv[8];
-        widen8<T>(ld_row<TAIL>(w, gi, n), wv);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
-      }
-      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
-    }
+    if (gi < nfull)
+      st16_stream(yr + 8 * gi,
+                  rmsnorm_granule<T>(raw[g], w ? ld16(w + 8 * gi) : zero, w != nullptr, rstd));
   }
+  if (mine)
+    st_partial(yr + 8 * nfull,
+               rmsnorm_granule<T>(xt, w ? ld_partial(w + 8 * nfull, n & 7) : zero,
+                                  w != nullptr, rstd),
+               n & 7);
 }
 
 template <typename T, int W, int GPL, bool TAIL>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
-    uint16_t* y, int ng, int n, int64_t xs, int64_t ys, float n_f, float eps) {
+    uint16_t* y, int nfull, int n, int64_t xs, int64_t ys, float n_f, float eps) {
   __shared__ float slot0[W], slot1[W], slot2[W];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
+  const bool mine = TAIL && t == nfull % (kWave * W);
   u32x4 raw[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave * W + t;
     raw[g] = (u32x4){0u, 0u, 0u, 0u};
-    if (gi < ng) raw[g] = ld_row_stream<TAIL>(xr, gi, n);
+    if (gi < nfull) raw[g] = ld16_stream(xr + 8 * gi);
   }
+  const u32x4 xt = ld_tail<TAIL>(xr, mine, nfull, n);
   // the same two-part mean as the one-wave kernel
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
+  for (int g = 0; g < GPL + (TAIL ? 1 : 0); ++g) {
     float v[8];
-    widen8<T>(raw[g], v);
+    widen8<T>(g < GPL ? raw[g] : xt, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] += v[k];
   }
@@ -301,45 +349,36 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave * W + t;
-    if (gi < ng) {
+    if (gi < nfull) {
       float v[8];
       widen8<T>(raw[g], v);
-      const int cnt = granule_count<TAIL>(gi, n);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float d = k < cnt ? v[k] - mu0 : 0.0f;
-        acc1[k] += d;
-        acc2[k] = fmaf(d, d, acc2[k]);
-      }
+      centred_moments(v, 8, mu0, acc1, acc2);
     }
+  }
+  if (mine) {
+    float v[8];
+    widen8<T>(xt, v);
+    centred_moments(v, n & 7, mu0, acc1, acc2);
   }
   const float r = block_sum<W>(tree8(acc1), slot1) / n_f;
   const float m2 = block_sum<W>(tree8(acc2), slot2) / n_f;
   const float var = fmaxf(fmaf(-r, r, m2), 0.0f);
   const float rstd = 1.0f / sqrtf(var + eps);
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave * W + t;
-    if (gi < ng) {
-      float v[8], gv[8], bv[8];
-      widen8<T>(raw[g], v);
-      if (gam) {
-        widen8<T>(ld_row<TAIL>(gam, gi, n), gv);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) gv[k] = 1.0f;
-      }
-      if (bet) {
-        widen8<T>(ld_row<TAIL>(bet, gi, n), bv);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = fmaf(((v[k] - mu0) - r) * rstd, gv[k], bv[k]);
-      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
-    }
+    if (gi < nfull)
+      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
+                                                bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
+                                                bet != nullptr, mu0, r, rstd));
   }
+  if (mine)
+    st_partial(yr + 8 * nfull,
+               layernorm_out<T>(xt, ld_tail<TAIL>(gam, gam != nullptr, nfull, n),
+                                ld_tail<TAIL>(bet, bet != nullptr, nfull, n), gam != nullptr,
+                                bet != nullptr, mu0, r, rstd),
+               n & 7);
 }
 
 // ------------------------------------------------- split-K, two passes
@@ -355,14 +394,15 @@ constexpr int kSplitUnroll = 4;
 
 template <typename T, bool TAIL>
 __global__ __launch_bounds__(kSplitThreads) void rmsnorm_splitk_kernel(
-    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int ng, int n, int64_t xs,
+    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int nfull, int n, int64_t xs,
     int64_t ys, float n_f, float eps) {
   __shared__ float slot[kSplitWaves];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
-  const int chunks = (ng + kSplitThreads - 1) / kSplitThreads;
+  const bool mine = TAIL && t == nfull % kSplitThreads;
+  const int chunks = (nfull + kSplitThreads - 1) / kSplitThreads;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < chunks; c0 += kSplitUnroll) {
     u32x4 raw[kSplitUnroll];
@@ -370,7 +410,7 @@ __global__ __launch_bounds__(kSplitThreads) void rmsnorm_splitk_kernel(
     for (int u = 0; u < kSplitUnroll; ++u) {
       const int gi = (c0 + u) * kSplitThreads + t;
       raw[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (gi < ng) raw[u] = ld_row<TAIL>(xr, gi, n);
+      if (gi < nfull) raw[u] = ld16(xr + 8 * gi);
     }
 #pragma unroll
     for (int u = 0; u < kSplitUnroll; ++u) {
@@ -380,24 +420,27 @@ __global__ __launch_bounds__(kSplitThreads) void rmsnorm_splitk_kernel(
       for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
     }
   }
+  if (TAIL) {  // the partial granule ends its thread's sequence
+    float v[8];
+    widen8<T>(ld_tail<TAIL>(xr, mine, nfull, n), v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+  }
   const float ss = block_sum<kSplitWaves>(tree8(acc), slot);
   const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  if (mine)  // the last granule of the row comes first in the reversed pass
+    st_partial(yr + 8 * nfull,
+               rmsnorm_granule<T>(ld_partial(xr + 8 * nfull, n & 7),
+                                  w ? ld_partial(w + 8 * nfull, n & 7) : zero, w != nullptr,
+                                  rstd),
+               n & 7);
   for (int c = chunks - 1; c >= 0; --c) {  // reverse order: the last chunks are still cached
     const int gi = c * kSplitThreads + t;
-    if (gi < ng) {
-      float v[8];
-      widen8<T>(ld_row<TAIL>(xr, gi, n), v);
-      if (w) {
-        float wv[8];
-        widen8<T>(ld_row<TAIL>(w, gi, n), wv);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (v[k] * wv[k]) * rstd;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = v[k] * rstd;
-      }
-      st_row_stream<TAIL>(yr, gi, n, narrow8<T>(v));
-    }
+    if (gi < nfull)
+      st16_stream(yr + 8 * gi, rmsnorm_granule<T>(ld16(xr + 8 * gi),
+                                                  w ? ld16(w + 8 * gi) : zero, w != nullptr,
+                                                  rstd));
   }
 }
 
@@ -476,33 +519,34 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
   const auto* wp = static_cast<const uint16_t*>(w);
   auto* yp = static_cast<uint16_t*>(y);
   const int ni = (int)n;
+  const int nfull = (int)(n >> 3);  // whole granules; the kernels take the partial one apart
   const float nf = (float)n;
   if (ng <= kOneWaveGranules) {
     const int gpl = granules_per_lane(ng);
     const bool full = !tail && ng == gpl * kWave;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (dtype == 1)
-      QRW_NORM_DISPATCH(rmsnorm_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp, rows, ng,
+      QRW_NORM_DISPATCH(rmsnorm_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
                         ni, xs, ys, nf, eps);
     else
-      QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, ng,
+      QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
                         ni, xs, ys, nf, eps);
   } else if (ng <= kResidentGranules) {
     const int wv = block_waves(ng);
     if (dtype == 1)
-      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, wp, yp, ng,
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, wp, yp, nfull,
                             ni, xs, ys, nf, eps);
     else
-      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, wp, yp, ng,
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, wp, yp, nfull,
                             ni, xs, ys, nf, eps);
   } else {
     const dim3 grid((unsigned)rows);
     if (dtype == 1) {
-      if (tail) rmsnorm_splitk_kernel<F16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
-      else rmsnorm_splitk_kernel<F16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+      if (tail) rmsnorm_splitk_kernel<F16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, nfull, ni, xs, ys, nf, eps);
+      else rmsnorm_splitk_kernel<F16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, nfull, ni, xs, ys, nf, eps);
     } else {
-      if (tail) rmsnorm_splitk_kernel<BF16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
-      else rmsnorm_splitk_kernel<BF16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, ng, ni, xs, ys, nf, eps);
+      if (tail) rmsnorm_splitk_kernel<BF16, true><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, nfull, ni, xs, ys, nf, eps);
+      else rmsnorm_splitk_kernel<BF16, false><<<grid, kSplitThreads, 0, stream>>>(xp, wp, yp, nfull, ni, xs, ys, nf, eps);
     }
   }
   return hipGetLastError();
@@ -518,6 +562,7 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
   const auto* bp = static_cast<const uint16_t*>(b);
   auto* yp = static_cast<uint16_t*>(y);
   const int ni = (int)n;
+  const int nfull = (int)(n >> 3);  // whole granules; the kernels take the partial one apart
   const float nf = (float)n;
   if (ng <= kOneWaveGranules) {
     const int gpl = granules_per_lane(ng);
@@ -525,18 +570,18 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (dtype == 1)
       QRW_NORM_DISPATCH(layernorm_kernel, F16, gpl, full, tail, grid, stream, xp, gp, bp, yp, rows,
-                        ng, ni, xs, ys, nf, eps);
+                        nfull, ni, xs, ys, nf, eps);
     else
       QRW_NORM_DISPATCH(layernorm_kernel, BF16, gpl, full, tail, grid, stream, xp, gp, bp, yp,
-                        rows, ng, ni, xs, ys, nf, eps);
+                        rows, nfull, ni, xs, ys, nf, eps);
   } else {
     const int wv = block_waves(ng);
     if (dtype == 1)
       QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, gp, bp, yp,
-                            ng, ni, xs, ys, nf, eps);
+                            nfull, ni, xs, ys, nf, eps);
     else
       QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, gp, bp,
-                            yp, ng, ni, xs, ys, nf, eps);
+                            yp, nfull, ni, xs, ys, nf, eps);
   }
   return hipGetLastError();
 }

@@ -60,7 +60,7 @@ def _ln(rows, n, dt, seed, affine=True, in_place=False):
     return st
 
 
-RAGGED = [1, 3, 7, 13, 100, 513, 1001, 4099, 8191]
+RAGGED = [1, 3, 7, 13, 100, 513, 1001, 4095, 4099, 8191]
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
