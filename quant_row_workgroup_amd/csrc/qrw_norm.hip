@@ -52,7 +52,8 @@ __device__ __forceinline__ u32x4 ld_tail(const uint16_t* p, bool mine, int nfull
 // of 4096 rows is 4 waves per SIMD, so below 4 a quarter of the rows wait for
 // a second round.  Without a floor the compiler's choice swings between ~80
 // and ~250 VGPRs from one instance to the next.  The row-block kernels ask for
-// 4.
+// 8 at 4 granules per thread (7 for ragged LayerNorm, which spills at 8) and
+// 4 at 8 granules.
 template <int GPL, bool TAIL>
 constexpr int kNormWaves = GPL <= 8 ? 4 : 2;
 
@@ -274,7 +275,7 @@ __device__ __forceinline__ u32x4 rmsnorm_granule(u32x4 xg, u32x4 wg, bool has_w,
 }
 
 template <typename T, int W, int GPL, bool TAIL>
-__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_rowblock_kernel(
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <= 4 ? 8 : 4))) void rmsnorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int nfull, int n, int64_t xs,
     int64_t ys, float n_f, float eps) {
   __shared__ float slot[W];
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 template <typename T, int W, int GPL, bool TAIL>
-__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_rowblock_kernel(
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <= 4 ? (TAIL ? 7 : 8) : 4))) void layernorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
     uint16_t* y, int nfull, int n, int64_t xs, int64_t ys, float n_f, float eps) {
   __shared__ float slot0[W], slot1[W], slot2[W];
@@ -451,14 +452,23 @@ int granules_per_lane(int ng) {
   return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16;
 }
 
-// Waves per row for kOneWaveGranules < ng <= kResidentGranules: the smallest
-// power of two in [2, 16] whose threads hold the row at 8 granules each (8
-// granules = 32 VGPRs of row data, which keeps a 1024-thread workgroup within
-// its 128 VGPRs per lane without spilling).
-int block_waves(int ng) {
+// Row-block shape for kOneWaveGranules < ng <= kResidentGranules: gpt granules
+// per thread (4, or 8 for rows beyond 4 granules x max_waves waves), and the
+// smallest power of two in [2, 16] of waves whose threads hold the row.  At 4
+// granules (16 VGPRs of row data) the kernels run at up to 8 waves per SIMD;
+// at 8 (32 VGPRs) a 1024-thread workgroup stays within 128 VGPRs per lane.
+// Measured on MI355X (bf16): RMSNorm 2048 x 16384 25.3 against 27.3 us and
+// 1024 x 32768 26.6 against 27.3 us at 4; LayerNorm, whose three block sums
+// cost more at 16 waves, takes 4 only up to 8 waves (2048 x 16384: 27.7
+// against 28.2 us; 1024 x 32768 at 16 waves x 4: 29.5 against 28.2 us).
+struct BlockShape {
+  int waves, gpt;
+};
+BlockShape block_shape(int ng, int max_waves_at_4) {
+  const int gpt = ng <= max_waves_at_4 * kWave * 4 ? 4 : 8;
   int w = 2;
-  while (w < 16 && w * kWave * 8 < ng) w *= 2;
-  return w;
+  while (w < 16 && w * kWave * gpt < ng) w *= 2;
+  return {w, gpt};
 }
 
 }  // namespace
@@ -501,8 +511,13 @@ int block_waves(int ng) {
     else KERNEL<T, W, GPL, false><<<dim3((unsigned)(rows)), kWave * W, 0, stream>>>(__VA_ARGS__);     \
   } while (0)
 
-#define QRW_ROWBLOCK_DISPATCH(KERNEL, T, waves, tail, rows, stream, ...)                      \
+#define QRW_ROWBLOCK_DISPATCH(KERNEL, T, waves, gpt, tail, rows, stream, ...)                 \
   do {                                                                                        \
+    if (gpt == 4) {                                                                           \
+      if (waves <= 8) QRW_ROWBLOCK_GO(KERNEL, T, 8, 4, tail, rows, stream, __VA_ARGS__);      \
+      else QRW_ROWBLOCK_GO(KERNEL, T, 16, 4, tail, rows, stream, __VA_ARGS__);                \
+      break;                                                                                  \
+    }                                                                                         \
     switch (waves) {                                                                          \
       case 2: QRW_ROWBLOCK_GO(KERNEL, T, 2, 8, tail, rows, stream, __VA_ARGS__); break;       \
       case 4: QRW_ROWBLOCK_GO(KERNEL, T, 4, 8, tail, rows, stream, __VA_ARGS__); break;       \
@@ -532,12 +547,12 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
       QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
                         ni, xs, ys, nf, eps);
   } else if (ng <= kResidentGranules) {
-    const int wv = block_waves(ng);
+    const BlockShape b = block_shape(ng, 16);
     if (dtype == 1)
-      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, wp, yp, nfull,
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, b.waves, b.gpt, tail, rows, stream, xp, wp, yp, nfull,
                             ni, xs, ys, nf, eps);
     else
-      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, wp, yp, nfull,
+      QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, BF16, b.waves, b.gpt, tail, rows, stream, xp, wp, yp, nfull,
                             ni, xs, ys, nf, eps);
   } else {
     const dim3 grid((unsigned)rows);
@@ -575,12 +590,12 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
       QRW_NORM_DISPATCH(layernorm_kernel, BF16, gpl, full, tail, grid, stream, xp, gp, bp, yp,
                         rows, nfull, ni, xs, ys, nf, eps);
   } else {
-    const int wv = block_waves(ng);
+    const BlockShape b = block_shape(ng, 8);
     if (dtype == 1)
-      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, F16, wv, tail, rows, stream, xp, gp, bp, yp,
+      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, F16, b.waves, b.gpt, tail, rows, stream, xp, gp, bp, yp,
                             nfull, ni, xs, ys, nf, eps);
     else
-      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, BF16, wv, tail, rows, stream, xp, gp, bp,
+      QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, BF16, b.waves, b.gpt, tail, rows, stream, xp, gp, bp,
                             yp, nfull, ni, xs, ys, nf, eps);
   }
   return hipGetLastError();

@@ -83,7 +83,7 @@ def test_ragged_without_weights_and_in_place():
 
 
 # one workgroup of several waves per row (8192 < n <= 65536)
-ROWBLOCK = [8200, 12288, 16391, 32768, 40000, 65533, 65536]
+ROWBLOCK = [8200, 12288, 12289, 16391, 32768, 40000, 65533, 65536]
 # the two-pass kernel (n > 65536, RMSNorm only)
 SPLITK = [65537, 131072, 262147, 1 << 20]
 
