@@ -253,13 +253,14 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // RN(x / s) given y = RN(1 / s), without a division (Markstein's correction:
-// q = RN(x*y), r = x - q*s exactly by one fma, RN(q + r*y) is the correctly
-// rounded quotient for the |x| <= 448*s range of a quantiser); the sign of a
-// zero x is kept.
+// q = RN(x*y), the remainder q*s - x is exact by one fma, and RN(q - r*y) is
+// the correctly rounded quotient for the |x| <= 448*s range of a quantiser).
+// Taking the remainder with this sign keeps the sign of a zero x with no
+// extra instruction: for x = -0 both fma results are -0, for x = +0 both +0.
 __device__ __forceinline__ float div_rn(float x, float s, float y) {
   const float q = x * y;
-  const float r = fmaf(-q, s, x);
-  return __builtin_copysignf(fmaf(r, y, q), x);
+  const float r = fmaf(q, s, -x);
+  return fmaf(-r, y, q);
 }
 
 // Sum of squares of the two 16-bit elements of a packed pair, added to acc,
