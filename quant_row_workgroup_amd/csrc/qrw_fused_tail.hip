@@ -110,9 +110,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_tail_kernel(
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
-  const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
+  const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float kq = rstd / scale;
-  const float inv = 1.0f / scale;
+  const float inv = recip_rn(scale);
   if (lane == 0) scales[t] = scale;
 #pragma unroll
   for (int g = 0; g < G; ++g) {

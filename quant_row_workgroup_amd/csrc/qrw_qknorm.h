@@ -187,8 +187,8 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
           for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
           const float am = fmaxf(group_max<HG>(m), 1e-4f);
           if (gi < ng && cached) {
-            const float scale = am / 448.0f;
-            const float y = 1.0f / scale;
+            const float scale = scale_e4m3(am);
+            const float y = recip_rn(scale);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
             const int hg = is_v ? gi - kv.k_end : gi - q_gran;  // granule inside the k (v) part
@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
       }
     }
   } else {
+    // in place: every granule of the chunk is a q or k granule
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
       const int gi = gb + kWave * g + lane;
@@ -212,33 +213,23 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
       acc1 = sumsq2(T{}, raw[g][3], acc1);
       const float ss = group_sum<HG>(acc0 + acc1);
       const bool is_q = gi < q_gran;
-      const bool is_v = KV && gi >= kv.k_end;
-      // inv_n = 1 / head_dim, exact (head_dim is a power of two): ss * inv_n == ss / head_dim
-      // 1/sqrt(mean + eps) once per head and granule (GC times per lane): the
-      // hardware reciprocal square root refined by one Newton-Raphson step,
-      // y <- y (3/2 - (v/2) y^2), good to about one binary32 ulp.  A correctly
-      // rounded 1.0f / sqrtf() costs a division sequence per head, which measured
-      // 7% slower on the 4096 x (32+8+8) x 128 workload.
+      // rstd as in the KV form's norm_rotate
       const float mv = ss * inv_n + eps;
-      float yr = __builtin_amdgcn_rsqf(mv);
-      yr = yr * fmaf(-0.5f * mv * yr, yr, 1.5f);
-      const float rstd = is_v ? 1.0f : yr;
+      float rstd = __builtin_amdgcn_rsqf(mv);
+      rstd = rstd * fmaf(-0.5f * mv * rstd, rstd, 1.5f);
       float v[8];
       widen8<T>(raw[g], v);
-      if (!is_v) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= is_q ? fq[e] : fk[e];
-      }
-      const bool rot = span && !is_v;
+      for (int e = 0; e < 8; ++e) v[e] *= is_q ? fq[e] : fk[e];
       if (NEOX) {
         float r[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[e] = fmaf(v[e], c[e], lane_xor<XR>(v[e]) * sn[e]);
-        if (rot) {
+        if (span) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = r[e];
         }
-      } else if (rot) {
+      } else if (span) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float x0 = v[2 * k], x1 = v[2 * k + 1];
@@ -248,27 +239,7 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] *= rstd;
-      if constexpr (KV) {
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-        const float am = fmaxf(group_max<HG>(m), 1e-4f);
-        if (gi < ng) {
-          if (is_q) {
-            st16_stream(row + 8 * gi, narrow8<T>(v));
-          } else if (cached) {
-            const float scale = am / 448.0f;
-            const float y = 1.0f / scale;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
-            const int hg = is_v ? gi - kv.k_end : gi - q_gran;  // granule inside the k (v) part
-            st8_stream((is_v ? kv.vc : kv.kc) + slot * kv.cache_stride + 8 * hg, fp8x8(v));
-            if (j == 0) (is_v ? kv.vs : kv.ks)[slot * kv.kv_heads + hg / HG] = scale;
-          }
-        }
-      } else {
-        if (gi < ng) st16_stream(row + 8 * gi, narrow8<T>(v));
-      }
+      if (gi < ng) st16_stream(row + 8 * gi, narrow8<T>(v));
     }
   }
 }

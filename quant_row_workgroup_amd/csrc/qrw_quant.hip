@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
 #pragma unroll
     for (int e = 0; e < 8; e += 2) m = fmaxf(m, fmaxf(fabsf(v[e]), fabsf(v[e + 1])));
     const float am = fmaxf(group_max<L>(m), 1e-4f);  // groups never straddle the row end
-    const float scale = am / 448.0f;
+    const float scale = scale_e4m3(am);
     if constexpr (kGather) {
       // groups g*(64/L) .. of this step sit in lane blocks of L; lane j takes
       // group j = g*(64/L) + q from lane q*L
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
       if (lane / kPer == g) mine = got;
     }
     if (FULL || gi < ng) {
-      const float y = 1.0f / scale;
+      const float y = recip_rn(scale);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
       st8_stream(qr + 8 * gi, fp8x8(v));
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kBlock) void act_quant_token_kernel(const uint16_t*
       m[e >> 1] = fmaxf(m[e >> 1], fmaxf(fabsf(v[e]), fabsf(v[e + 1])));
   }
   const float am = fmaxf(wave_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))), 1e-4f);
-  const float scale = am / 448.0f;
-  const float y = 1.0f / scale;
+  const float scale = scale_e4m3(am);
+  const float y = recip_rn(scale);
   if (lane == 0) scales[row] = scale;
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {

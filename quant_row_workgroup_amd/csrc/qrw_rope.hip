@@ -233,9 +233,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
   // 4. per-token scale (s3.1.5): scale = max(amax_z, 1e-4) / 448, amax_z = amax * rstd
   //    (MID: the stored values already carry rstd)
   const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
-  const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
+  const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float k = rstd / scale;
-  const float inv = 1.0f / scale;
+  const float inv = recip_rn(scale);
   if (lane == 0) scales[t] = scale;
 
   // 5. quantise and store the codes
@@ -351,9 +351,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_contig_kernel(
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
-  const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
+  const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float kq = rstd / scale;
-  const float inv = 1.0f / scale;
+  const float inv = recip_rn(scale);
   if (lane == 0) scales[t] = scale;
 
 #pragma unroll
@@ -419,7 +419,7 @@ __device__ __forceinline__ void dense_token(const u32x4 (&ra)[K], const u32x4 (&
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   const float amax_z = wave_max(amax) * rstd;
-  const float scale = fmaxf(amax_z, 1e-4f) / 448.0f;
+  const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float kq = rstd / scale;
   if (lane == 0) *scale_out = scale;
 
