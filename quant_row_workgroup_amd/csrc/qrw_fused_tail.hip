@@ -26,13 +26,18 @@
 
 namespace qrw {
 
+// Rows (waves) per workgroup: 16, measured faster than 4 or 8 on one 4096-wide
+// head rotating its last 128 channels, 4096 tokens bf16 (11.06 against 11.6
+// us).
+constexpr int kTailRows = 16;
+
 template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XR, bool MID>
-__global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_tail_kernel(
+__global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, int hg_mask,
     int s0, float n_f, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kTailRows + (threadIdx.x >> 6);
   if (t >= tokens) return;  // wave-uniform
   const uint16_t* xr = x + t * xs;
   uint8_t* qr = q + t * qs;
@@ -135,7 +140,7 @@ void tail_go(dim3 grid, hipStream_t st, const void* x, const void* w, const void
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
 #define QRW_TAIL_LAUNCH(HW, M)                                                                  \
-  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M><<<grid, kBlock, 0, st>>>(             \
+  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M><<<grid, kWave * kTailRows, 0, st>>>( \
       xp, wp, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps)
   if (mid) {
     if (wp) QRW_TAIL_LAUNCH(true, true);
@@ -191,7 +196,7 @@ hipError_t launch_rmsnorm_rope_fp8_tail(const void* x, const void* w, const void
                                         int64_t rope_dim, int64_t xs, int64_t qs, int dtype,
                                         int cs_dtype, bool neox, float eps, bool round_mid,
                                         hipStream_t stream) {
-  const dim3 grid((unsigned)((tokens + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 grid((unsigned)((tokens + kTailRows - 1) / kTailRows));
   const int gg = (int)(heads * head_dim / 512);
   const int xr = (int)(rope_dim / 16);
   const int half = (int)(rope_dim / 2);
