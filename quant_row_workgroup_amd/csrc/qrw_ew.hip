@@ -11,7 +11,8 @@
 //   two or more extra bits rounds like the value itself (Boldo and Melquiond,
 //   IEEE TC 2008), so the output is the rounding of the binary64 result rather
 //   than a double rounding through binary32.  The HBM-bound kernel hides the
-//   few extra binary64 operations.
+//   few extra binary64 operations.  A plain sum of two 16-bit values (alpha
+//   == 1) skips binary64: its binary32 sum rounds correctly (see combine).
 //
 // Mapping: lane l of wave w takes E consecutive elements at
 // ((w * U + u) * 64 + l) * E for u < U, so every memory instruction of a wave
@@ -112,9 +113,16 @@ __device__ __forceinline__ float round_odd_f32(double d) {
 }
 
 // x * alpha (+ b) for an output of type YT, in the form the YT store expects.
-template <typename YT, bool HAS_B>
+// ADD: x + b of two values of the 16-bit output format (alpha == 1).  Their
+// binary32 sum rounds once more to that format exactly as the exact sum does:
+// it is exact when the exponents differ by at most 15 (bf16) or 13 (f16), and
+// otherwise the smaller operand is below a quarter of the larger one's half
+// ulp, so that both the exact and the binary32 sums round to the larger.
+template <typename YT, bool HAS_B, bool ADD = false>
 __device__ __forceinline__ float combine(float x, float alpha, float b) {
-  if constexpr (std::is_same<YT, float>::value) {
+  if constexpr (ADD) {
+    return x + b;
+  } else if constexpr (std::is_same<YT, float>::value) {
     return HAS_B ? fmaf(x, alpha, b) : x * alpha;
   } else {
     const double v = HAS_B ? fma((double)x, (double)alpha, (double)b) : (double)x * (double)alpha;
@@ -122,7 +130,7 @@ __device__ __forceinline__ float combine(float x, float alpha, float b) {
   }
 }
 
-template <typename XT, typename YT, bool HAS_B, int E, int U>
+template <typename XT, typename YT, bool HAS_B, int E, int U, bool ADD>
 __global__ __launch_bounds__(kBlock) void ew_kernel(const void* __restrict__ x,
                                                     const void* __restrict__ b, void* y,
                                                     int64_t n, float alpha) {
@@ -146,12 +154,12 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const void* __restrict__ x,
       V::widen(xr[u], xv);
       if (HAS_B) V::widen(br[u], bv);
 #pragma unroll
-      for (int e = 0; e < E; ++e) yv[e] = combine<YT, HAS_B>(xv[e], alpha, HAS_B ? bv[e] : 0.0f);
+      for (int e = 0; e < E; ++e) yv[e] = combine<YT, HAS_B, ADD>(xv[e], alpha, HAS_B ? bv[e] : 0.0f);
       Vec<YT, E>::st(y, i, yv);
     } else if (i < n) {  // the unit that straddles the end
       for (int64_t k = i; k < n; ++k) {
         const float xs = Scalar<XT>::ld(x, k);
-        Scalar<YT>::st(y, k, combine<YT, HAS_B>(xs, alpha, HAS_B ? Scalar<XT>::ld(b, k) : 0.0f));
+        Scalar<YT>::st(y, k, combine<YT, HAS_B, ADD>(xs, alpha, HAS_B ? Scalar<XT>::ld(b, k) : 0.0f));
       }
     }
   }
@@ -162,18 +170,18 @@ namespace {
 
 constexpr int64_t kEwBigUnits = (int64_t)1 << 20;  // above this, 4 units per lane
 
-template <typename XT, typename YT, bool HAS_B, int E>
+template <typename XT, typename YT, bool HAS_B, int E, bool ADD = false>
 void ew_go(const void* x, const void* b, void* y, int64_t n, float alpha, hipStream_t st) {
   const int64_t units = (n + E - 1) / E;
   if (units > kEwBigUnits) {
     constexpr int U = 4;
     const int64_t waves = (units + kWave * U - 1) / (kWave * U);
     const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
-    ew_kernel<XT, YT, HAS_B, E, U><<<grid, kBlock, 0, st>>>(x, b, y, n, alpha);
+    ew_kernel<XT, YT, HAS_B, E, U, ADD><<<grid, kBlock, 0, st>>>(x, b, y, n, alpha);
   } else {
     const int64_t waves = (units + kWave - 1) / kWave;
     const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
-    ew_kernel<XT, YT, HAS_B, E, 1><<<grid, kBlock, 0, st>>>(x, b, y, n, alpha);
+    ew_kernel<XT, YT, HAS_B, E, 1, ADD><<<grid, kBlock, 0, st>>>(x, b, y, n, alpha);
   }
 }
 
@@ -184,7 +192,10 @@ void ew_b(bool has_b, const void* x, const void* b, void* y, int64_t n, float al
   constexpr int E = kWide ? 4 : 8;
   if constexpr (std::is_same<XT, YT>::value) {  // an addend only comes with one dtype
     if (has_b) {
-      ew_go<XT, YT, true, E>(x, b, y, n, alpha, st);
+      if (!kWide && alpha == 1.0f)  // a plain 16-bit sum: binary32 is enough
+        ew_go<XT, YT, true, E, true>(x, b, y, n, alpha, st);
+      else
+        ew_go<XT, YT, true, E>(x, b, y, n, alpha, st);
       return;
     }
   }

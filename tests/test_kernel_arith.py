@@ -9,8 +9,12 @@ quotient without a division instruction:
   page's float32 cast ("TileLang tutorial, ch. 13", s3.1.5) and the oracle
   compute.
 
-(The third identity, hardware reciprocal plus one Newton step == IEEE 1/s,
-depends on the GPU's reciprocal instruction and cannot be emulated here.)"""
+and the elementwise add: the binary32 sum of two 16-bit values, rounded once
+to their format, is the correctly rounded sum (s3.1.1's a + b).
+
+(The remaining identity, hardware reciprocal plus one Newton step == IEEE
+1/s, depends on the GPU's reciprocal instruction and cannot be emulated
+here.)"""
 from fractions import Fraction
 
 import numpy as np
@@ -112,3 +116,52 @@ def test_scale_over_whole_binades(e):
         exact = Fraction(float(q)) - Fraction(float(r)) * Fraction(float(F32(1.0) / F32(448.0)))
         assert _rn32(exact) == want[i], a[i]
     assert len(bad) <= 20
+
+
+def _bf16_rne_from_f32(f: np.ndarray) -> np.ndarray:
+    u = f.astype(F32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _round_odd_f32(d: np.ndarray) -> np.ndarray:
+    f = d.astype(F32)
+    u = f.view(np.uint32).copy()
+    inexact = f.astype(np.float64) != d
+    up = np.abs(d) > np.abs(f.astype(np.float64))
+    fix = inexact & ((u & 1) == 0)
+    u[fix & up] += 1
+    u[fix & ~up] -= 1
+    return u.view(F32)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # sums that overflow to inf
+def test_sum_of_two_16bit_values_rounds_once_through_binary32(fmt):
+    # the elementwise add of two 16-bit tensors forms x + b in binary32 and
+    # rounds that once to the 16-bit format; it must equal the rounding of the
+    # exact sum (formed in binary64, exact up to a 45-bit exponent gap, beyond
+    # which the smaller operand cannot move the result), rounded to odd at
+    # binary32 and then to the format (a single rounding, Boldo-Melquiond)
+    rng = np.random.default_rng(11)
+    n = 400_000
+    if fmt == "bf16":
+        bits = rng.integers(0, 0x7F80, size=(2, n), dtype=np.uint32)
+        sign = rng.integers(0, 2, size=(2, n), dtype=np.uint32) << 15
+        v = ((bits | sign) << 16).view(F32)
+        a, b = v[0], v[1]
+        # near-cancellation pairs and small exponent gaps
+        b[: n // 4] = -a[: n // 4] * F32(1.0078125)
+        b[n // 4: n // 2] = (a[n // 4: n // 2].view(np.uint32) ^ 0x80010000).view(F32)
+        b = ((_bf16_rne_from_f32(b).astype(np.uint32)) << 16).view(F32)
+        got = _bf16_rne_from_f32((a + b).astype(F32))
+        want = _bf16_rne_from_f32(_round_odd_f32(a.astype(np.float64) + b.astype(np.float64)))
+    else:
+        bits = rng.integers(0, 0x7C00, size=(2, n), dtype=np.uint16)
+        sign = rng.integers(0, 2, size=(2, n), dtype=np.uint16) << 15
+        v = (bits | sign).view(np.float16).astype(F32)
+        a, b = v[0], v[1]
+        b[: n // 4] = (-a[: n // 4] * F32(1.0009765625)).astype(np.float16).astype(F32)
+        got = (a + b).astype(F32).astype(np.float16).view(np.uint16)
+        want = _round_odd_f32(a.astype(np.float64) + b.astype(np.float64)).astype(
+            np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
