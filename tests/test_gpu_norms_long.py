@@ -106,6 +106,13 @@ def test_long_rows_in_place_and_without_weights():
     _ln(4, 16391, "f16", seed=9, in_place=True, affine=False)
 
 
+@pytest.mark.parametrize("n,dt,with_w", [(1 << 26, "bf16", True), ((1 << 26) - 3, "f16", False)])
+def test_longest_rmsnorm_rows(n, dt, with_w):
+    # the longest row the split-K kernel accepts (QRW_MAX_ROW_SPLIT = 2^26
+    # elements, 128 MiB of bf16), whole and ragged
+    _rms(1, n, dt, seed=13, with_w=with_w)
+
+
 @pytest.mark.parametrize("n", [16391, 262147])
 def test_long_rows_are_batch_invariant(n):
     # a row's output does not depend on which other rows share the launch
