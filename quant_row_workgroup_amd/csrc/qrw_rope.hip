@@ -367,7 +367,13 @@ __global__ __launch_bounds__(kWave * kContigRows<MID>) void rmsnorm_rope_fp8_con
     float a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = MID ? div_rn(v[g][e], scale, inv) : v[g][e] * kq;
-    st8(qr + 8 * (kWave * g + lane), fp8x8(a));
+    // codes: plain stores for the exact form, non-temporal for the staged one
+    // (each measured faster on 4096 x 4096 bf16: 10.97 against 11.45 us, and
+    // 12.29 against 12.71 us)
+    if (MID)
+      st8_stream(qr + 8 * (kWave * g + lane), fp8x8(a));
+    else
+      st8(qr + 8 * (kWave * g + lane), fp8x8(a));
   }
 }
 
