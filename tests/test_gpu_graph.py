@@ -3,8 +3,12 @@ the library's own elementwise kernel), the in-place QK-norm + RoPE, RMSNorm,
 the fused RMSNorm + RoPE + FP8, the per-group FP8 cast and an elementwise
 add is replayed several times, with unrelated eager work and
 synchronisations between the replays; every replay must reproduce the eager
-results bit for bit.  (No memset node is recorded: the graph contains only
-the library's kernels.)"""
+results bit for bit.  A second graph holds every other entry point (the KV-cache
+write, LayerNorm, both RoPE conventions, the staged fused form, scale-add) and
+the ragged, row-block, split-K and tail-rotation paths; there, bytes the
+operators do not own (cache rows no token maps to, row padding) must keep
+their fill.  (No memset node is recorded: the graphs contain only the
+library's kernels.)"""
 import numpy as np
 import pytest
 import torch
@@ -80,4 +84,85 @@ def test_graph_replays_match_eager():
         # unrelated eager work between replays
         _run(i, other)
         torch.matmul(i["x"][:, :128].float(), i["x"][:, :128].float().t())
+        torch.cuda.synchronize()
+
+
+def _inputs_rest():
+    T, Hq, Hk, D = 16, 8, 2, 128
+    n = (Hq + 2 * Hk) * D
+    g = lambda seed, shape, m=0.0, s=1.0: dev(synth.normal(seed, shape, m, s, "bf16"), "bf16")
+    ns = 2 * T + 3
+    return dict(
+        T=T, Hq=Hq, Hk=Hk, D=D, ns=ns,
+        qkv0=g(11, (T, n)), qw=g(12, (D,), 1.0, 0.1), kw=g(13, (D,), 1.0, 0.1),
+        c=dev(synth.rope_table(T, D, "bf16")[0], "bf16"),
+        s=dev(synth.rope_table(T, D, "bf16")[1], "bf16"),
+        slots=torch.from_numpy(synth.cache_slots(14, T, ns)).cuda(),
+        x=g(15, (T, 4096), 0.0, 3.0), w=g(16, (4096,), 1.0, 0.1), b=g(17, (4096,), 0.0, 0.1),
+        xr=g(18, (T, 4096))[:, :4095],                      # ragged rows, stride 4096
+        xl=g(19, (3, 40000)), wl=g(20, (40000,), 1.0, 0.1),  # one workgroup per row
+        xs=g(21, (2, 131072)), ws=g(22, (131072,), 1.0, 0.1))  # two-pass split-K
+
+
+def _outputs_rest(i):
+    T, e8 = i["T"], lambda shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
+    f32 = lambda shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    like = torch.empty_like
+    return dict(qkv=like(i["qkv0"]), kc=e8((i["ns"], i["Hk"] * i["D"])),
+                vc=e8((i["ns"], i["Hk"] * i["D"])), ks=f32((i["ns"], i["Hk"])),
+                vs=f32((i["ns"], i["Hk"])), ln=like(i["x"]), ri=like(i["x"]), rn=like(i["x"]),
+                qs=e8((T, 4096)), ss=f32((T,)), qt=e8((T, 4096)), st=f32((T,)),
+                sa=like(i["x"]), yr=torch.empty((T, 4096), dtype=torch.bfloat16, device="cuda"),
+                yl=like(i["xl"]), ys=like(i["xs"]), lnl=like(i["xl"]))
+
+
+def _run_rest(i, o):
+    """Every entry point the first graph test does not hold, and the ragged,
+    row-block, split-K and tail-rotation paths."""
+    qrw.ew_scale_cast_fwd(i["qkv0"], 1.0, out=o["qkv"])          # exact copy
+    qrw.qk_norm_rope_fp8_kv_fwd(o["qkv"], i["qw"], i["kw"], i["c"], i["s"], o["kc"], o["vc"],
+                                o["ks"], o["vs"], i["Hq"], i["Hk"], i["D"], slots=i["slots"])
+    qrw.layernorm_fwd(i["x"], i["w"], i["b"], 1e-5, out=o["ln"])
+    qrw.rope_apply_interleaved(i["x"], i["c"], i["s"], 32, 128, out=o["ri"])
+    qrw.rope_apply_neox(i["x"], i["c"], i["s"], 32, 128, out=o["rn"])
+    qrw.rmsnorm_rope_fp8_rounded_fwd(i["x"], i["w"], i["c"], i["s"], 32, 128, q=o["qs"],
+                                     scales=o["ss"])
+    qrw.rmsnorm_rope_fp8_fwd(i["x"], i["w"], i["c"], i["s"], 1, 4096, 128, q=o["qt"],
+                             scales=o["st"])                      # one head, tail rotation
+    qrw.ew_scale_add_fwd(i["x"], i["x"], 0.5, out=o["sa"])
+    qrw.rmsnorm_fwd(i["xr"], i["w"][:4095], 1e-6, out=o["yr"][:, :4095])
+    qrw.rmsnorm_fwd(i["xl"], i["wl"], 1e-6, out=o["yl"])
+    qrw.rmsnorm_fwd(i["xs"], i["ws"], 1e-6, out=o["ys"])
+    qrw.layernorm_fwd(i["xl"], i["wl"], None, 1e-5, out=o["lnl"])
+
+
+def test_graph_replays_match_eager_all_entry_points():
+    i = _inputs_rest()
+
+    def fill(o):
+        for v in o.values():
+            v.view(torch.uint8).fill_(0x5C)
+
+    ref = _outputs_rest(i)
+    fill(ref)
+    _run_rest(i, ref)
+    torch.cuda.synchronize()
+    o = _outputs_rest(i)
+    _run_rest(i, o)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        _run_rest(i, o)
+    torch.cuda.synchronize()
+    other = _outputs_rest(i)
+    for rep in range(4):
+        fill(o)  # bytes the replay does not own must stay as filled
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(o[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+        _run_rest(i, other)  # unrelated eager work between replays
         torch.cuda.synchronize()
