@@ -39,7 +39,8 @@ def _check(x, w, c, s, H, D, R, dt, cs, neox, what, eps=1e-6):
 
 
 def test_rounded_workload_shape():
-    name = "rmsnorm_rope_fp8_4096x4096_bf16"
+    # the benchmark's staged workload, at full size and in bench.py's launch form
+    name = "rmsnorm_rope_fp8_4096x4096_bf16_staged"
     inp = synth.make_inputs(name)
     st = _check(inp["x"], inp["w"], inp["cos"], inp["sin"], inp["heads"], inp["head_dim"],
                 inp["rope_dim"], inp["dtype"], inp["cs_dtype"], inp["neox"], name, inp["eps"])
