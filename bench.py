@@ -398,8 +398,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the row operators shard by tokens "
-              "with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the row operators shard by tokens with no "
+              "exchange between GPUs, so one GPU's throughput is the figure. Use --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch

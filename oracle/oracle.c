@@ -19,7 +19,7 @@
  * 8-bit floating point spec for E4M3FN).  There is no fusion, blocking or
  * reordering: one row at a time, one element at a time, single thread.
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *  - FP8 is OCP E4M3FN (bias 7, max finite 448 = 0x7E, S.1111.111 is NaN, no
  *    infinities); the quantisation divides by the scale and clamps to +-448
  *    before encoding, as the per-token cast in [EW] s3.1.5 does.  That cast
