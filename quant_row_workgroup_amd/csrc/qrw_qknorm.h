@@ -75,8 +75,11 @@ __global__ __launch_bounds__(kBlock) void qk_norm_rope_kernel(
   const int gb = (int)(wave - t * chunks) * kWave * GC;
   uint16_t* row = qkv + t * stride;
   const int j = lane & (HG - 1);        // granule position inside the head
-  const int js = j - s0;                // position inside the rotated span (< 0: outside)
-  const bool span = js >= 0;
+  // NeoX with 2*XR == HG rotates the whole head (rope_dim == head_dim, s0 == 0):
+  // every lane is in the span, known at compile time
+  constexpr bool kWhole = NEOX && 2 * XR == HG;
+  const int js = kWhole ? j : j - s0;   // position inside the rotated span (< 0: outside)
+  const bool span = kWhole || js >= 0;
   int64_t slot = t;
   bool cached = true;
   if constexpr (KV) {
