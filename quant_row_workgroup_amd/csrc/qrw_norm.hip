@@ -217,13 +217,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   const float rstd = 1.0f / sqrtf(var + eps);
 
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  if (gam && bet) {
+    // the affine case without a test per granule, so that the gamma/beta
+    // loads of later granules can be issued ahead of earlier granules' math
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
-    const int gi = g * kWave + lane;
-    if (FULL || gi < nfull)
-      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
-                                                bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
-                                                bet != nullptr, mu0, r, rstd));
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave + lane;
+      if (FULL || gi < nfull)
+        st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], ld16(gam + 8 * gi),
+                                                  ld16(bet + 8 * gi), true, true, mu0, r, rstd));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave + lane;
+      if (FULL || gi < nfull)
+        st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
+                                                  bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
+                                                  bet != nullptr, mu0, r, rstd));
+    }
   }
   if (mine)
     st_partial(yr + 8 * nfull,
@@ -303,12 +315,18 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
   const float ss = block_sum<W>(tree8(acc), slot);
   const float rstd = 1.0f / sqrtf(ss / n_f + eps);
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  if (w) {  // no test per granule, so later weight loads run ahead of the math
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
-    const int gi = g * kWave * W + t;
-    if (gi < nfull)
-      st16_stream(yr + 8 * gi,
-                  rmsnorm_granule<T>(raw[g], w ? ld16(w + 8 * gi) : zero, w != nullptr, rstd));
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      if (gi < nfull) st16_stream(yr + 8 * gi, rmsnorm_granule<T>(raw[g], ld16(w + 8 * gi), true, rstd));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      if (gi < nfull) st16_stream(yr + 8 * gi, rmsnorm_granule<T>(raw[g], zero, false, rstd));
+    }
   }
   if (mine)
     st_partial(yr + 8 * nfull,
@@ -366,13 +384,23 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
   const float var = fmaxf(fmaf(-r, r, m2), 0.0f);
   const float rstd = 1.0f / sqrtf(var + eps);
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  if (gam && bet) {  // as in the one-wave kernel
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
-    const int gi = g * kWave * W + t;
-    if (gi < nfull)
-      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
-                                                bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
-                                                bet != nullptr, mu0, r, rstd));
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      if (gi < nfull)
+        st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], ld16(gam + 8 * gi),
+                                                  ld16(bet + 8 * gi), true, true, mu0, r, rstd));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      if (gi < nfull)
+        st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
+                                                  bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
+                                                  bet != nullptr, mu0, r, rstd));
+    }
   }
   if (mine)
     st_partial(yr + 8 * nfull,
