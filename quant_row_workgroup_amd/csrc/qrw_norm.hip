@@ -121,12 +121,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
     }
     return narrow8<T>(v);
   };
+  if (!kPreW && w) {  // late weights: the test stays outside the loop
 #pragma unroll
-  for (int g = 0; g < GPL; ++g) {
-    const int gi = g * kWave + lane;
-    if (FULL || gi < nfull)
-      st16_stream(yr + 8 * gi,
-                  finish(raw[g], !w ? (u32x4){0u, 0u, 0u, 0u} : kPreW ? wr[g] : ld16(w + 8 * gi)));
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave + lane;
+      if (FULL || gi < nfull) st16_stream(yr + 8 * gi, finish(raw[g], ld16(w + 8 * gi)));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave + lane;
+      if (FULL || gi < nfull)
+        st16_stream(yr + 8 * gi, finish(raw[g], w ? wr[g] : (u32x4){0u, 0u, 0u, 0u}));
+    }
   }
   if (mine) st_partial(yr + 8 * nfull, finish(xt, ld_tail<TAIL>(w, w != nullptr, nfull, n)), n & 7);
 }
