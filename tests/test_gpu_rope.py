@@ -43,6 +43,13 @@ SHAPES = [
     (1, 1, 16, 16),
     (9, 2, 1000, 16),     # odd number of pass-through granules per token
     (3, 4, 512, 512),
+    # whole heads of head_dim/16 in {1, 2, 4, 8, 16} on rows of 1, 2, 4 or 8
+    # blocks of 512 channels
+    (3, 4, 128, 128),     # one block
+    (2, 16, 64, 64),      # two blocks, head of 8 lanes
+    (4, 64, 32, 32),      # four blocks, head of 4 lanes
+    (3, 256, 16, 16),     # eight blocks, head of 2 lanes
+    (2, 16, 256, 256),    # eight blocks, head of 32 lanes
 ]
 
 
