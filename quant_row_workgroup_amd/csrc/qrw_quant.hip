@@ -23,10 +23,6 @@
 #include "qrw_device.h"
 #include "qrw_launch.h"
 
-#ifndef QRW_QUANT_GATHER
-#define QRW_QUANT_GATHER 1
-#endif
-
 namespace qrw {
 
 template <typename T, int GPL, bool FULL, int L>
@@ -37,7 +33,7 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
   // When a whole row has at most 64 groups (GPL <= L), lane j collects the
   // scale of group j (from any lane of that group, by a lane permute) and the
   // row's scales leave in one contiguous store instead of one store per group.
-  constexpr bool kGather = FULL && GPL <= L && QRW_QUANT_GATHER;
+  constexpr bool kGather = FULL && GPL <= L;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;

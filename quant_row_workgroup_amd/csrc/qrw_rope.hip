@@ -384,8 +384,8 @@ __global__ __launch_bounds__(kWave * kContigRows<MID>) void rmsnorm_rope_fp8_con
 // K = 4).  Offsets are closed-form and nothing is predicated; the sum of
 // squares runs on the packed pairs with v_dot2c.
 //
-// Each wave handles RPW tokens, t = wave, wave + W, ... (W waves in the
-// grid), software-pipelined: the loads of token k+1 are issued as soon as
+// Each wave handles RPW tokens (kDenseRpw), t = wave, wave + W, ... (W waves
+// in the grid), software-pipelined when RPW > 1: the loads of token k+1 are issued as soon as
 // token k's data is in registers, before token k is computed and stored, so
 // reads of later tokens overlap the arithmetic and the stores of earlier ones
 // instead of every wave waiting for the last of all reads.  The weight
@@ -556,29 +556,25 @@ void rope_go2(bool neox, int kk, dim3 grid, hipStream_t st, const uint16_t* x, c
   else rope_go<T, CS, false>(kk, grid, st, x, c, s, y, tokens, xs, ys, pl, copy);
 }
 
-// Tokens per wave of the dense kernel (fixed at build time; 1 = no pipelining).
-#ifndef QRW_DENSE_RPW
-#define QRW_DENSE_RPW 1
-#endif
-#ifndef QRW_DENSE_LDS
-#define QRW_DENSE_LDS 0
-#endif
+// Tokens per wave of the dense kernel.  1: pipelining several tokens per wave
+// did not pay at these sizes on MI355X (the kernel keeps the capability).
+constexpr int kDenseRpw = 1;
 
 template <typename T, typename CS, bool NEOX, int K>
 void dense_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
               const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
               const RowPlan& pl, float n_f, float eps) {
-  constexpr int kRpw = QRW_DENSE_RPW;
+  constexpr int kRpw = kDenseRpw;
   int lg = 0;
   while ((1 << lg) < pl.gph) ++lg;
   const dim3 g((unsigned)((tokens + (int64_t)kRowsPerBlock * kRpw - 1) /
                           ((int64_t)kRowsPerBlock * kRpw)));
   (void)grid;
   if (w)
-    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, true, kRpw><<<g, kBlock, QRW_DENSE_LDS, st>>>(
+    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, true, kRpw><<<g, kBlock, 0, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.head_dim, pl.half, lg, n_f, eps);
   else
-    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, false, kRpw><<<g, kBlock, QRW_DENSE_LDS, st>>>(
+    rmsnorm_rope_fp8_dense_kernel<T, CS, NEOX, K, false, kRpw><<<g, kBlock, 0, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, pl.head_dim, pl.half, lg, n_f, eps);
 }
 
