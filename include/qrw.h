@@ -32,8 +32,8 @@
  *   vectors (the elementwise family also takes QRW_F32).  RoPE tables have
  *   `cs_dtype`, either QRW_F32 or equal to dtype.
  * Numerics.  Arithmetic is binary32 (binary64 for the elementwise family's
- *   16-bit outputs); every 16-bit or FP8 output is rounded once, to
- *   nearest-even.
+ *   16-bit outputs, except a plain 16-bit sum); every 16-bit or FP8 output is
+ *   rounded once, to nearest-even.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *   asynchronous on it; argument errors are reported before anything is
  *   enqueued.
@@ -234,7 +234,9 @@ int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weigh
  * (any n >= 0; no multiple-of-8 requirement), 16-byte aligned, F16, BF16 or
  * F32.  Each output is x * alpha + b rounded once, nearest-even, to y's
  * dtype (a float32 fma for float32 outputs; for 16-bit outputs a float64 fma
- * carried to the cast without a second rounding).  y may be exactly x (or b) when it
+ * carried to the cast without a second rounding, or, for a plain sum of two
+ * 16-bit values (alpha == 1), their float32 sum, which rounds the same way).
+ * y may be exactly x (or b) when it
  * has the same dtype (in place); any other overlap of y with an input is
  * QRW_ERR_ALIAS.
  *   ew_add_fwd:        y = a + b              (a, b, y: dtype)
