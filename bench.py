@@ -298,9 +298,12 @@ def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
 # ---------------------------------------------------------------- CPU side
 def compute_dtype(cfg: dict) -> str:
     """The arithmetic type of the kernel: binary32, except the elementwise family's
-    16-bit outputs, which are formed in binary64."""
+    16-bit outputs, which are formed in binary64 (a plain sum of two 16-bit
+    values, alpha == 1, stays binary32)."""
     if cfg["op"] == "ew" and cfg.get("y_dtype", cfg["dtype"]) != "f32":
-        return "f64"
+        plain_sum = cfg.get("kind") == "add" or (cfg.get("kind") == "scale_add"
+                                                 and cfg.get("alpha") == 1.0)
+        return "f32" if plain_sum and cfg["dtype"] != "f32" else "f64"
     return "f32"
 
 
