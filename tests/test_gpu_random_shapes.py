@@ -1,0 +1,201 @@
+"""Seeded random shapes for every operator, against the fp64 oracle through the
+C ABI: row lengths, head sizes, rotation spans, group sizes, dtypes, table
+dtypes, pair conventions and optional weights are drawn within what each
+entry point accepts, so that every dispatch path (one wave or a workgroup per
+row, split-K, ragged tails, the contiguous, tail-rotation, dense and item
+fused kernels, every QK chunk width, each elementwise unroll) meets shapes
+nobody picked by hand.  Bars, per operator: 16-bit outputs within 2 ulp (with
+the cancellation allowance of the hand-written tests); act-quant codes and
+scales bit-exact; fused codes exact wherever the quotient is clear of an
+E4M3 rounding boundary and never more than one step off, scales to 1e-6."""
+import numpy as np
+import pytest
+
+import oracle
+import quant_row_workgroup_amd as qrw
+from quant_row_workgroup_amd import synth
+from tests import test_gpu_ew, test_gpu_fused, test_gpu_qk_kv, test_gpu_qk_norm_rope
+from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_terms
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 32
+
+
+def _rng(op, i):
+    return np.random.default_rng(1000 * (1 + ["norm", "rope", "fused", "aq", "qk", "kv",
+                                              "ew"].index(op)) + i)
+
+
+def _row_len(r, lo, hi):
+    """Log-uniform in [lo, hi], with a fair share of multiples of 8 and 512."""
+    n = int(np.exp(r.uniform(np.log(lo), np.log(hi))))
+    pick = r.integers(0, 4)
+    if pick == 1:
+        n = max(8, n // 8 * 8)
+    elif pick == 2:
+        n = max(512, n // 512 * 512)
+    return min(max(n, lo), hi)
+
+
+def _stride(n, r):
+    return (n + 7) // 8 * 8 + 8 * int(r.integers(0, 3))
+
+
+def _padded(x, dt, stride, seed):
+    """x as a row-strided device view; the padding holds large values, so a
+    kernel that reads past a row's end changes its result."""
+    rows, n = x.shape
+    wide = dev(synth.normal(seed, (rows, stride), 0.0, 300.0, dt), dt)
+    wide[:, :n] = dev(x, dt)
+    return wide[:, :n]
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_norms(i):
+    r = _rng("norm", i)
+    dt = ["f16", "bf16"][int(r.integers(0, 2))]
+    # RMSNorm up to the split-K range, LayerNorm up to one workgroup per row
+    n = _row_len(r, 1, 140000)
+    rows = _tokens(r, n)
+    x = synth.normal(i, (rows, n), 0.0, 1.5, dt, outlier_frac=0.01, outlier_mul=8.0)
+    w = synth.normal(i + 1, (n,), 1.0, 0.1, dt) if r.integers(0, 4) else None
+    xs = _padded(x, dt, _stride(n, r), i + 7)
+    got = host(qrw.rmsnorm_fwd(xs, None if w is None else dev(w, dt), 1e-6))
+    assert_close16(got, oracle.rmsnorm(x, w, dt, 1e-6), dt, what=f"rmsnorm {rows}x{n} {dt}")
+    n2 = min(n, 65536)
+    x2 = np.ascontiguousarray(x[:, :n2])
+    g = synth.normal(i + 2, (n2,), 1.0, 0.1, dt) if r.integers(0, 3) else None
+    b = synth.normal(i + 3, (n2,), 0.0, 0.1, dt) if r.integers(0, 3) else None
+    got = host(qrw.layernorm_fwd(_padded(x2, dt, _stride(n2, r), i + 8),
+                                 None if g is None else dev(g, dt),
+                                 None if b is None else dev(b, dt), 1e-5))
+    assert_close16(got, oracle.layernorm(x2, g, b, dt, 1e-5), dt,
+                   term_scale=layernorm_terms(x2, g, b, dt, 1e-5), what=f"layernorm {rows}x{n2}")
+
+
+def _tokens(r, n):
+    """Mostly a few rows; now and then enough for several whole workgroups and
+    a partial last one."""
+    return int(r.integers(7, 140)) if n <= 4096 and r.integers(0, 4) == 0 else int(r.integers(1, 7))
+
+
+def _heads(r, max_n=8192):
+    if r.integers(0, 6) == 0:                         # one or two long heads
+        D = 8 * int(r.integers(64, max_n // 16 + 1))  # 512 .. max_n / 2
+        R = 16 * int(r.integers(1, min(D // 16, 32) + 1))
+        return int(r.integers(1, 3)), D, R
+    D = 8 * int(r.integers(2, 65))                    # 16 .. 512, a multiple of 8
+    R = 16 * int(r.integers(1, D // 16 + 1))          # 16 .. D, a multiple of 16
+    if r.integers(0, 3) == 0 and (D & (D - 1)) == 0:  # whole-head and tail-only cases
+        R = D if r.integers(0, 2) else max(16, D // 4)
+    H = int(r.integers(1, max(1, min(32, max_n // D)) + 1))
+    return H, D, R
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_rope(i):
+    r = _rng("rope", i)
+    dt = ["f16", "bf16"][int(r.integers(0, 2))]
+    cs = ["f32", dt][int(r.integers(0, 2))]
+    neox = bool(r.integers(0, 2))
+    H, D, R = _heads(r)
+    T = _tokens(r, H * D)
+    x = synth.normal(i, (T, H * D), 0.0, 1.0, dt)
+    c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 4 else 7.0)
+    fn = qrw.rope_apply_neox if neox else qrw.rope_apply_interleaved
+    got = host(fn(dev(x, dt), dev(c, cs), dev(s, cs), H, D, R))
+    assert_close16(got, oracle.rope(x, c, s, H, D, R, dt, cs, neox), dt,
+                   term_scale=rope_terms(x, c, s, H, D, R, dt, cs, neox),
+                   what=f"rope {T}x{H}x{D}/{R} {dt}/{cs} {'neox' if neox else 'interleaved'}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_fused(i):
+    r = _rng("fused", i)
+    dt = ["f16", "bf16"][int(r.integers(0, 2))]
+    cs = ["f32", dt][int(r.integers(0, 2))]
+    neox = bool(r.integers(0, 2))
+    H, D, R = _heads(r)
+    T = _tokens(r, H * D)
+    x = synth.normal(i, (T, H * D), 0.0, 2.0, dt, outlier_frac=0.01, outlier_mul=10.0)
+    w = synth.normal(i + 1, (H * D,), 1.0, 0.1, dt) if r.integers(0, 3) else None
+    c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 4 else 7.0)
+    test_gpu_fused._check_ties(x, w, c, s, H, D, R, dt, cs, neox,
+                               what=f"fused {T}x{H}x{D}/{R} {dt}/{cs}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_act_quant(i):
+    r = _rng("aq", i)
+    dt = ["f16", "bf16"][int(r.integers(0, 2))]
+    group = [None, 8, 16, 32, 64, 128, 256, 512][int(r.integers(0, 8))]
+    unit = group or 8
+    n = max(unit, _row_len(r, 8, 8192) // unit * unit)
+    rows = _tokens(r, n)
+    x = synth.normal(i, (rows, n), 0.0, 1.0, dt, outlier_frac=0.01, outlier_mul=20.0)
+    q, sc = qrw.act_quant_fp8_fwd(dev(x, dt), group)
+    wq, wsc = oracle.act_quant_fp8(x, dt, group)
+    # both sides decide each code on the same correctly rounded binary32 quotient
+    assert np.array_equal(host(sc).view(np.uint32), wsc.view(np.uint32)), (rows, n, group)
+    assert np.array_equal(host(q), wq), (rows, n, group)
+
+
+def _qk_shape(r):
+    D = [64, 128, 256][int(r.integers(0, 3))]
+    R = [16, 32, 64, 128, 256][int(r.integers(0, 5))]
+    R = min(R, D)
+    T = int(r.integers(7, 70)) if r.integers(0, 4) == 0 else int(r.integers(1, 7))
+    return T, int(r.integers(1, 40)), int(r.integers(1, 9)), D, R
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_qk_norm_rope(i):
+    r = _rng("qk", i)
+    dt, cs = [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("f16", "f16")][int(r.integers(0, 4))]
+    neox = bool(r.integers(0, 2))
+    T, Hq, Hk, D, R = _qk_shape(r)
+    Hk = int(r.integers(0, Hk + 1))
+    x = synth.normal(i, (T, (Hq + 2 * Hk) * D), 0.0, 2.0, dt)
+    qw = synth.normal(i + 1, (D,), 1.0, 0.2, dt) if r.integers(0, 4) else None
+    kw = synth.normal(i + 2, (D,), 1.0, 0.2, dt) if r.integers(0, 4) else None
+    c, s = synth.rope_table(T, R, cs)
+    got, _ = test_gpu_qk_norm_rope._run(x, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, 1e-6)
+    test_gpu_qk_norm_rope._check(x, got, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, 1e-6,
+                                 what=f"qk {T}x({Hq}+{Hk}+{Hk})x{D}/{R} {dt}/{cs}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_qk_kv(i):
+    r = _rng("kv", i)
+    dt, cs = [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("f16", "f16")][int(r.integers(0, 4))]
+    neox = bool(r.integers(0, 2))
+    T, Hq, Hk, D, R = _qk_shape(r)
+    x = synth.normal(i, (T, (Hq + 2 * Hk) * D), 0.0, 2.0, dt, outlier_frac=0.02, outlier_mul=8.0)
+    qw = synth.normal(i + 1, (D,), 1.0, 0.2, dt)
+    kw = synth.normal(i + 2, (D,), 1.0, 0.2, dt)
+    c, s = synth.rope_table(T, R, cs)
+    ns = 2 * T + int(r.integers(0, 5))
+    test_gpu_qk_kv._check(x, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, 1e-6,
+                          slots=synth.cache_slots(i + 3, T, ns), ns=ns,
+                          pad=16 * int(r.integers(0, 3)), ties=True,
+                          what=f"qk_kv {T}x({Hq}+{Hk}+{Hk})x{D}/{R} {dt}/{cs}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_elementwise(i):
+    r = _rng("ew", i)
+    n = int(np.exp(r.uniform(0.0, np.log(3e6))))
+    kind = ["add", "scale_add", "scale_cast"][int(r.integers(0, 3))]
+    xf = ["f16", "bf16", "f32"][int(r.integers(0, 3))]
+    yf = ["f16", "bf16", "f32"][int(r.integers(0, 3))] if kind == "scale_cast" else xf
+    alpha = float(np.float32(r.choice([1.0, 0.5, -3.25, 1.0e-3, 7.0])))
+    x = synth.normal(i, (n,), 0.0, 4.0, xf)
+    b = synth.normal(i + 1, (n,), 0.0, 4.0, xf)
+    if kind == "add":
+        alpha = 1.0
+    if kind == "scale_cast":
+        b = None
+    got = test_gpu_ew._run(kind, x, b, alpha, xf, yf)
+    want = oracle.ew_scale_add(x, b, alpha, xf, yf)
+    test_gpu_ew._compare(got, want, yf, what=f"ew {kind} n={n} {xf}->{yf} alpha={alpha}")
