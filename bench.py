@@ -307,6 +307,22 @@ def compute_dtype(cfg: dict) -> str:
     return "f32"
 
 
+def resized_workload(name: str, rows: int) -> str:
+    """Register ``name`` with another row count as ``name@rows`` and return that
+    name (a paged-cache workload keeps at least four cache slots per token)."""
+    from quant_row_workgroup_amd import synth
+
+    cfg = dict(synth.WORKLOADS[name])
+    key = {"rope": "tokens", "fused": "tokens", "qk_norm_rope": "tokens", "qk_kv": "tokens",
+           "ew": "n"}.get(cfg["op"], "rows")
+    cfg[key] = rows
+    if cfg["op"] == "qk_kv":
+        cfg["num_slots"] = max(cfg["num_slots"], 4 * rows)
+    new = f"{name}@{rows}"
+    synth.WORKLOADS[new] = cfg
+    return new
+
+
 def op_of(name: str) -> str:
     from quant_row_workgroup_amd import synth
 
@@ -392,6 +408,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rows", type=int, default=0,
+                    help="run the workload with this many rows (tokens, or elements for the "
+                         "elementwise family) instead of its own count; every other size stays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -414,6 +433,8 @@ def main() -> int:
 
     from quant_row_workgroup_amd import synth
 
+    if args.rows:
+        args.workload = resized_workload(args.workload, args.rows)
     wl = Workload(args.workload, args.sets)
     print(f"[bench] {args.workload}: {args.sets} sets, warmup {args.warmup}, steps {args.steps}, "
           f"mode {args.mode}", file=sys.stderr, flush=True)

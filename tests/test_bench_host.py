@@ -1,0 +1,59 @@
+"""Host logic of bench.py on the CPU: the row-count override, the reported
+arithmetic type, and the refusal of more than one GPU."""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from quant_row_workgroup_amd import ledger, synth
+
+
+@pytest.fixture(autouse=True)
+def _restore_workloads():
+    saved = dict(synth.WORKLOADS)
+    yield
+    synth.WORKLOADS.clear()
+    synth.WORKLOADS.update(saved)
+
+
+ROW_KEY = {"rope": "tokens", "fused": "tokens", "qk_norm_rope": "tokens", "qk_kv": "tokens",
+           "ew": "n"}
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_resized_workload_changes_only_the_row_count(name):
+    base = dict(synth.WORKLOADS[name])
+    key = ROW_KEY.get(base["op"], "rows")
+    a, b = bench.resized_workload(name, 64), bench.resized_workload(name, 128)
+    ca, cb = synth.WORKLOADS[a], synth.WORKLOADS[b]
+    assert a == f"{name}@64" and ca[key] == 64 and cb[key] == 128
+    for k in base:
+        if k not in (key, "num_slots"):
+            assert ca[k] == base[k], k
+    if base["op"] == "qk_kv":
+        assert ca["num_slots"] >= 4 * 64 and cb["num_slots"] >= 4 * 128
+    # bytes grow by the same amount for each further 64 rows (the per-row cost);
+    # weights, tables of other rows and the like stay
+    c192 = synth.WORKLOADS[bench.resized_workload(name, 192)]
+    d1 = ledger.counted_bytes(cb) - ledger.counted_bytes(ca)
+    d2 = ledger.counted_bytes(c192) - ledger.counted_bytes(cb)
+    assert d1 == d2 > 0
+    inp = synth.make_inputs(a, rows=8)
+    assert inp["x"].shape[0] == 8
+    assert bench.full_rows(a) == 64
+
+
+def test_compute_dtype():
+    assert bench.compute_dtype(synth.WORKLOADS["rmsnorm_rope_fp8_4096x4096_bf16"]) == "f32"
+    assert bench.compute_dtype(synth.WORKLOADS["add_16M_bf16"]) == "f32"
+    assert bench.compute_dtype(synth.WORKLOADS["scale_cast_16M_f32_to_f16"]) == "f64"
+    assert bench.compute_dtype(synth.WORKLOADS["scale_add_1M_f32"]) == "f32"
+    assert bench.compute_dtype(dict(op="ew", kind="scale_add", alpha=0.5, dtype="bf16")) == "f64"
+    assert bench.compute_dtype(dict(op="ew", kind="scale_add", alpha=1.0, dtype="f16")) == "f32"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
