@@ -337,10 +337,16 @@ def full_rows(name: str) -> int:
 
 
 def cpu_baseline(name: str, seconds: float):
+    """The float64 C oracle on a bounded sample of the workload, on the host's
+    cores: first one thread, then one thread per core (at most 16) over
+    contiguous row blocks, each half of ``seconds``.  ctypes releases the
+    interpreter lock during each oracle call, so the threads run in parallel."""
+    import concurrent.futures
+
     import oracle
     from quant_row_workgroup_amd import ledger, synth
 
-    rows = 1 << 16 if op_of(name) == "ew" else 256
+    rows = 1 << 20 if op_of(name) == "ew" else 256
     inp = synth.make_inputs(name, rows=rows)
     cfg = dict(synth.WORKLOADS[name])
     op = cfg["op"]
@@ -349,54 +355,71 @@ def cpu_baseline(name: str, seconds: float):
     cfg[key] = rows
     bytes_per_call = ledger.counted_bytes(cfg)
 
-    def call():
+    def call(lo, hi):
+        x = inp["x"][lo:hi]
+        if op in ("fused", "rope", "qk_norm_rope", "qk_kv"):
+            cos, sin = inp["cos"][lo:hi], inp["sin"][lo:hi]
         if op == "fused":
             fn = oracle.rmsnorm_rope_fp8_rounded if cfg.get("staged") else oracle.rmsnorm_rope_fp8
-            fn(inp["x"], inp["w"], inp["cos"], inp["sin"], cfg["heads"], cfg["head_dim"],
-               cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], cfg["neox"], cfg["eps"])
+            fn(x, inp["w"], cos, sin, cfg["heads"], cfg["head_dim"], cfg["rope_dim"],
+               cfg["dtype"], cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "act_quant":
-            oracle.act_quant_fp8(inp["x"], cfg["dtype"], cfg.get("group"))
+            oracle.act_quant_fp8(x, cfg["dtype"], cfg.get("group"))
         elif op == "ew":
             alpha = 1.0 if cfg["kind"] == "add" else cfg["alpha"]
-            oracle.ew_scale_add(inp["x"], inp.get("b"), alpha, cfg["dtype"],
+            b = inp.get("b")
+            oracle.ew_scale_add(x, None if b is None else b[lo:hi], alpha, cfg["dtype"],
                                 cfg.get("y_dtype", cfg["dtype"]))
         elif op == "qk_kv":
-            oracle.qk_norm_rope_fp8_kv(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
-                                       inp["sin"], cfg["q_heads"], cfg["kv_heads"],
-                                       cfg["head_dim"], cfg["rope_dim"], cfg["dtype"],
-                                       cfg["cs_dtype"], cfg["neox"], cfg["eps"],
-                                       slots=inp["slots"], num_slots=cfg["num_slots"])
+            oracle.qk_norm_rope_fp8_kv(x, inp["q_weight"], inp["k_weight"], cos, sin,
+                                       cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                                       cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"],
+                                       cfg["neox"], cfg["eps"], slots=inp["slots"][lo:hi],
+                                       num_slots=cfg["num_slots"])
         elif op == "qk_norm_rope":
-            oracle.qk_norm_rope(inp["x"], inp["q_weight"], inp["k_weight"], inp["cos"],
-                                inp["sin"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
-                                cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], cfg["neox"],
-                                cfg["eps"])
+            oracle.qk_norm_rope(x, inp["q_weight"], inp["k_weight"], cos, sin, cfg["q_heads"],
+                                cfg["kv_heads"], cfg["head_dim"], cfg["rope_dim"],
+                                cfg["dtype"], cfg["cs_dtype"], cfg["neox"], cfg["eps"])
         elif op == "rmsnorm":
-            oracle.rmsnorm(inp["x"], inp["w"], cfg["dtype"], cfg["eps"])
+            oracle.rmsnorm(x, inp["w"], cfg["dtype"], cfg["eps"])
         elif op == "layernorm":
-            oracle.layernorm(inp["x"], inp["gamma"], inp["beta"], cfg["dtype"], cfg["eps"])
+            oracle.layernorm(x, inp["gamma"], inp["beta"], cfg["dtype"], cfg["eps"])
         else:
-            oracle.rope(inp["x"], inp["cos"], inp["sin"], cfg["heads"], cfg["head_dim"],
-                        cfg["rope_dim"], cfg["dtype"], cfg["cs_dtype"], True)
+            oracle.rope(x, cos, sin, cfg["heads"], cfg["head_dim"], cfg["rope_dim"],
+                        cfg["dtype"], cfg["cs_dtype"], True)
 
-    call()  # warm-up
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        call()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = bytes_per_call * reps / el / 1e9
+    def timed(step, budget):
+        step()  # warm-up
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            step()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    reps1, el1 = timed(lambda: call(0, rows), seconds / 2)
+    threads = max(1, min(16, os.cpu_count() or 1, rows))
+    cuts = [rows * i // threads for i in range(threads + 1)]
+    with concurrent.futures.ThreadPoolExecutor(threads) as pool:
+        def all_blocks():
+            for f in [pool.submit(call, cuts[i], cuts[i + 1]) for i in range(threads)]:
+                f.result()
+        repsn, eln = timed(all_blocks, seconds / 2)
+    gbs1 = bytes_per_call * reps1 / el1 / 1e9
+    gbsn = bytes_per_call * repsn / eln / 1e9
+    unit = "elements" if op == "ew" else "rows"
     return {
-        "value": round(gbs, 4),
+        "value": round(gbsn, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"{rows} of {full_rows(name)} "
-                   f"{'elements' if op == 'ew' else 'rows'} of the same workload, {reps} calls in {el:.1f} s, single-threaded "
-                   f"float64 C checker on {cpu_model()} ({os.cpu_count()} logical CPUs present)"),
+        "single_thread_value": round(gbs1, 4),
+        "sample": (f"{rows} of {full_rows(name)} {unit} of the same workload; float64 C "
+                   f"checker on {cpu_model()} ({os.cpu_count()} logical CPUs present): "
+                   f"{threads} threads over contiguous blocks of {unit}, {repsn} passes in "
+                   f"{eln:.1f} s; one thread, {reps1} passes in {el1:.1f} s"),
     }
 
 

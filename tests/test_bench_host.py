@@ -57,3 +57,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("name", ["rmsnorm_rope_fp8_4096x4096_bf16", "scale_add_1M_f32",
+                                  "qk_norm_rope_fp8_kv_4096_q32_kv8_d128_bf16"])
+def test_cpu_baseline_reports_both_thread_counts(name):
+    r = bench.cpu_baseline(name, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert 1 <= r["cores"] <= 16 and r["value"] > 0 and r["single_thread_value"] > 0
+    assert f"{r['cores']} threads" in r["sample"]
