@@ -60,7 +60,8 @@ enum qrw_status {
   QRW_ERR_NULL = -1,    /* a required pointer is NULL */
   QRW_ERR_DTYPE = -2,   /* unsupported dtype / cs_dtype code */
   QRW_ERR_SHAPE = -3,   /* a size is negative, not a multiple of its granule, or too large */
-  QRW_ERR_STRIDE = -4,  /* a row stride is shorter than the row or not a multiple of 8 */
+  QRW_ERR_STRIDE = -4,  /* a row stride is shorter than the row, not a multiple of 8, or
+                           the rows it spans exceed 2^56 bytes */
   QRW_ERR_ALIGN = -5,   /* a pointer is not 16-byte aligned */
   QRW_ERR_ALIAS = -6,   /* output overlaps an input other than as an exact in-place alias */
   QRW_ERR_LAUNCH = -7,  /* the kernel launch failed */

@@ -31,6 +31,15 @@ Span span_of(const void* p, int64_t rows, int64_t n, int64_t stride, int64_t elt
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// The bytes that `rows` rows of `n` elements `stride` apart span must fit the
+// address space (2^56 bytes here); nothing larger describes memory, and the
+// span arithmetic above could overflow.  Formed in 128 bits.
+constexpr int64_t kMaxExtent = (int64_t)1 << 56;
+bool extent_ok(int64_t rows, int64_t n, int64_t stride, int64_t elt) {
+  if (rows <= 0) return true;
+  return ((__int128)(rows - 1) * stride + n) * elt <= (__int128)kMaxExtent;
+}
+
 // y may equal x exactly (same base, same stride); any other overlap is refused.
 int check_alias(const void* x, int64_t xs, const void* y, int64_t ys, int64_t rows, int64_t n,
                 int64_t elt) {
@@ -58,6 +67,7 @@ int check_row_shape(int64_t rows, int64_t n, int64_t max_n, int64_t xs, int64_t 
   if (rows > (n > 8 * qrw::kOneWaveGranules ? (int64_t)0x7FFFFFFF : (int64_t)0x7FFFFFFF * 4))
     return QRW_ERR_SHAPE;
   if (xs < n || ys < n || xs % 8 != 0 || ys % 8 != 0) return QRW_ERR_STRIDE;
+  if (!extent_ok(rows, n, xs, 2) || !extent_ok(rows, n, ys, 2)) return QRW_ERR_STRIDE;
   if (!eps_ok(eps)) return QRW_ERR_VALUE;
   return QRW_OK;
 }
@@ -145,6 +155,7 @@ static int rope_common(const void* x, const void* cos, const void* sin, void* y,
   if (st != QRW_OK) return st;
   const int64_t n = heads * head_dim;
   if (xs < n || ys < n || xs % 8 != 0 || ys % 8 != 0) return QRW_ERR_STRIDE;
+  if (!extent_ok(tokens, n, xs, 2) || !extent_ok(tokens, n, ys, 2)) return QRW_ERR_STRIDE;
   if (tokens == 0) return QRW_OK;
   if (!x || !y || !cos || !sin) return QRW_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(cos) || !aligned16(sin))
@@ -185,6 +196,8 @@ static int fused_entry(const void* x, const void* weight, const void* cos, const
   const int64_t n = heads * head_dim;
   if (x_token_stride < n || x_token_stride % 8 != 0) return QRW_ERR_STRIDE;
   if (q_token_stride < n || q_token_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (!extent_ok(tokens, n, x_token_stride, 2) || !extent_ok(tokens, n, q_token_stride, 1))
+    return QRW_ERR_STRIDE;
   if (!eps_ok(eps)) return QRW_ERR_VALUE;
   if (neox != 0 && neox != 1) return QRW_ERR_VALUE;
   if (tokens == 0) return QRW_OK;
@@ -239,6 +252,8 @@ int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, in
   if (group != n && !(pow2_group && n % group == 0)) return QRW_ERR_SHAPE;
   if (x_row_stride < n || x_row_stride % 8 != 0) return QRW_ERR_STRIDE;
   if (q_row_stride < n || q_row_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (!extent_ok(rows, n, x_row_stride, 2) || !extent_ok(rows, n, q_row_stride, 1))
+    return QRW_ERR_STRIDE;
   if (rows == 0) return QRW_OK;
   if (!x || !q || !scales) return QRW_ERR_NULL;
   if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
@@ -265,6 +280,7 @@ int qk_norm_rope_fwd(void* qkv, const void* q_weight, const void* k_weight, cons
   const int64_t n = (q_heads + 2 * kv_heads) * head_dim;
   if (tokens > (int64_t)0x7FFFFFFF) return QRW_ERR_SHAPE;
   if (token_stride < n || token_stride % 8 != 0) return QRW_ERR_STRIDE;
+  if (!extent_ok(tokens, n, token_stride, 2)) return QRW_ERR_STRIDE;
   if (!eps_ok(eps)) return QRW_ERR_VALUE;
   if (neox != 0 && neox != 1) return QRW_ERR_VALUE;
   if (tokens == 0) return QRW_OK;
@@ -306,6 +322,10 @@ int qk_norm_rope_fp8_kv_fwd(void* qkv, const void* q_weight, const void* k_weigh
   const int64_t kvn = kv_heads * head_dim;
   if (token_stride < n || token_stride % 8 != 0) return QRW_ERR_STRIDE;
   if (cache_stride < kvn || cache_stride % 8 != 0) return QRW_ERR_STRIDE;
+  // (the cache extent also bounds the scale arrays: 4 * num_slots * kv_heads
+  // bytes is less than num_slots * kvn, since head_dim >= 64)
+  if (!extent_ok(tokens, n, token_stride, 2) || !extent_ok(num_slots, kvn, cache_stride, 1))
+    return QRW_ERR_STRIDE;
   if (!eps_ok(eps)) return QRW_ERR_VALUE;
   if (neox != 0 && neox != 1) return QRW_ERR_VALUE;
   if (tokens == 0) return QRW_OK;

@@ -78,6 +78,7 @@ def rms(**kw):
     (dict(rows=0), OK),                                         # empty: nothing launched
     (dict(rows=0, x=None, y=None, w=None), OK),                 # empty tensors may have no storage
     (dict(rows=0, dtype=F32), DTYPE),                           # but still a valid call
+    (dict(xs=1 << 54), STRIDE), (dict(ys=1 << 60), STRIDE),     # rows spanning > 2^56 bytes
 ])
 def test_rmsnorm_validation(kw, want):
     assert rms(**kw) == want
@@ -96,6 +97,7 @@ def ln(**kw):
     (dict(xs=32), STRIDE), (dict(n=13, xs=13, ys=16), STRIDE),
     (dict(b=ctypes.c_void_p((4 << 32) + 8)), ALIGN), (dict(eps=-1.0), VALUE),
     (dict(y=ctypes.c_void_p((1 << 32) + 16)), ALIAS), (dict(rows=0), OK),
+    (dict(xs=1 << 58), STRIDE),
 ])
 def test_layernorm_validation(kw, want):
     assert ln(**kw) == want
@@ -120,6 +122,7 @@ def rope(neox=True, **kw):
     (dict(y=ctypes.c_void_p((1 << 32) + 128)), ALIAS),
     (dict(c=ctypes.c_void_p((2 << 32) + 64)), ALIAS),
     (dict(T=0), OK), (dict(T=0, x=None, y=None, c=None, s=None), OK),
+    (dict(xs=1 << 58), STRIDE), (dict(ys=1 << 62), STRIDE),
 ])
 def test_rope_validation(neox, kw, want):
     assert rope(neox, **kw) == want
@@ -145,6 +148,7 @@ def fused(**kw):
     (dict(q=ctypes.c_void_p((1 << 32) + 4096)), ALIAS),  # codes inside x
     (dict(T=0), OK), (dict(T=0, x=None, q=None, sc=None, c=None, s=None), OK),
     (dict(T=0, R=24), SHAPE),
+    (dict(xs=1 << 58), STRIDE), (dict(qs=1 << 58), STRIDE),
 ])
 def test_fused_validation(kw, want):
     assert fused(**kw) == want
@@ -167,6 +171,7 @@ def aq(**kw):
     (dict(sc=ctypes.c_void_p(Q_ADDR + 64)), ALIAS),      # scales inside the codes
     (dict(q=ctypes.c_void_p((1 << 32) + 256)), ALIAS),   # codes inside x
     (dict(rows=0), OK), (dict(rows=0, x=None, q=None, sc=None), OK),
+    (dict(xs=1 << 58), STRIDE), (dict(qs=1 << 58), STRIDE),
 ])
 def test_act_quant_validation(kw, want):
     assert aq(**kw) == want
@@ -193,6 +198,7 @@ def qk(**kw):
     (dict(wq=ctypes.c_void_p((1 << 32) + 12288)), ALIAS),  # weight inside row 1
     (dict(T=0), OK), (dict(T=0, x=None, c=None, s=None), OK),
     (dict(T=0, R=24), SHAPE),
+    (dict(xs=1 << 58), STRIDE),
 ])
 def test_qk_norm_rope_validation(kw, want):
     assert qk(**kw) == want
@@ -227,6 +233,7 @@ def qkv_cache(**kw):
     (dict(c=ctypes.c_void_p((8 << 32) + 1024)), ALIAS),      # table inside the k cache
     (dict(T=0), OK), (dict(T=0, x=None, kc=None, vc=None, ks=None, vs=None, sl=None, ns=0), OK),
     (dict(T=0, R=24), SHAPE),
+    (dict(xs=1 << 58), STRIDE), (dict(cst=1 << 58), STRIDE), (dict(ns=1 << 50), STRIDE),
 ])
 def test_qk_kv_cache_validation(kw, want):
     assert qkv_cache(**kw) == want
