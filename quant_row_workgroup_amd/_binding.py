@@ -91,6 +91,37 @@ def _dtype(t):
     return _DTYPE[t.dtype]
 
 
+def _on_device(t, name):
+    """The tensor every other argument is checked against: on a ROCm device."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on a ROCm device")
+    return t
+
+
+def _same_device(t, like, name):
+    if not isinstance(t, torch.Tensor) or t.device != like.device:
+        raise ValueError(f"{name} must be a tensor on {like.device}")
+    return t
+
+
+def _exact(t, like, name, shape, dtype):
+    """An output (or a fixed-size input) the kernel reads or writes in full:
+    exactly this shape and dtype, on like's device."""
+    _same_device(t, like, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)}")
+    return t
+
+
+def _tables(cos, sin, tokens, rope_dim, like):
+    """cos and sin: packed [tokens, rope_dim/2], one dtype (float32 or like's)."""
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        _exact(t, like, nm, (tokens, rope_dim // 2), cos.dtype)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+
+
 def _rows(t, name):
     if t.dim() == 2 and t.shape[0] == 0:  # empty: strides carry no meaning
         return 0, t.shape[1], t.shape[1]
@@ -104,11 +135,12 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _vec(t, n, name):
+def _vec(t, n, name, like):
     if t is None:
         return None
-    if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
-        raise ValueError(f"{name} must be a packed vector of length {n}")
+    _same_device(t, like, name)
+    if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous() or t.dtype != like.dtype:
+        raise ValueError(f"{name} must be a packed {like.dtype} vector of length {n}")
     return t
 
 
@@ -120,35 +152,34 @@ def _new_rows(rows, n, like):
 
 def rmsnorm_fwd(x, weight=None, eps: float = 1e-6, out=None):
     """RMSNorm over the last dim of 2-D ``x``; returns ``out``."""
-    rows, n, xs = _rows(x, "x")
-    out = _new_rows(rows, n, x) if out is None else out
+    rows, n, xs = _rows(_on_device(x, "x"), "x")
+    out = _new_rows(rows, n, x) if out is None else _exact(out, x, "out", (rows, n), x.dtype)
     _, _, ys = _rows(out, "out")
-    st = load().rmsnorm_fwd(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(out), rows, n, xs,
+    st = load().rmsnorm_fwd(_ptr(x), _ptr(_vec(weight, n, "weight", x)), _ptr(out), rows, n, xs,
                             ys, _dtype(x), eps, _stream(x))
     _check("rmsnorm_fwd", st)
     return out
 
 
 def layernorm_fwd(x, gamma=None, beta=None, eps: float = 1e-5, out=None):
-    rows, n, xs = _rows(x, "x")
-    out = _new_rows(rows, n, x) if out is None else out
+    rows, n, xs = _rows(_on_device(x, "x"), "x")
+    out = _new_rows(rows, n, x) if out is None else _exact(out, x, "out", (rows, n), x.dtype)
     _, _, ys = _rows(out, "out")
-    st = load().layernorm_fwd(_ptr(x), _ptr(_vec(gamma, n, "gamma")),
-                              _ptr(_vec(beta, n, "beta")), _ptr(out), rows, n, xs, ys,
+    st = load().layernorm_fwd(_ptr(x), _ptr(_vec(gamma, n, "gamma", x)),
+                              _ptr(_vec(beta, n, "beta", x)), _ptr(out), rows, n, xs, ys,
                               _dtype(x), eps, _stream(x))
     _check("layernorm_fwd", st)
     return out
 
 
 def _rope(fn, x, cos, sin, heads, head_dim, rope_dim, out):
-    tokens, n, xs = _rows(x, "x")
+    tokens, n, xs = _rows(_on_device(x, "x"), "x")
     if heads * head_dim != n:
         raise ValueError("heads * head_dim must equal the row length")
-    out = torch.empty((tokens, n), dtype=x.dtype, device=x.device) if out is None else out
-    _, _, ys = _rows(out, "out")
-    for t, nm in ((cos, "cos"), (sin, "sin")):
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    if out is None:
+        out = torch.empty((tokens, n), dtype=x.dtype, device=x.device)
+    _, _, ys = _rows(_exact(out, x, "out", (tokens, n), x.dtype), "out")
+    _tables(cos, sin, tokens, rope_dim, x)
     st = getattr(load(), fn)(_ptr(x), _ptr(cos), _ptr(sin), _ptr(out), tokens, heads, head_dim,
                              rope_dim, xs, ys, _dtype(x), _dtype(cos), _stream(x))
     _check(fn, st)
@@ -168,7 +199,7 @@ def rope_apply_neox(x, cos, sin, heads: int, head_dim: int, rope_dim: int | None
 
 
 def _fused(fname, x, weight, cos, sin, heads, head_dim, rope_dim, neox, eps, q, scales):
-    tokens, n, xs = _rows(x, "x")
+    tokens, n, xs = _rows(_on_device(x, "x"), "x")
     if heads * head_dim != n:
         raise ValueError("heads * head_dim must equal the row length")
     rd = head_dim if rope_dim is None else rope_dim
@@ -176,11 +207,11 @@ def _fused(fname, x, weight, cos, sin, heads, head_dim, rope_dim, neox, eps, q, 
         q = torch.empty((tokens, n), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((tokens,), dtype=torch.float32, device=x.device)
-    _, _, qs = _rows(q, "q")
-    for t, nm in ((cos, "cos"), (sin, "sin")):
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
-    st = getattr(load(), fname)(_ptr(x), _ptr(_vec(weight, n, "weight")), _ptr(cos), _ptr(sin),
+    _, _, qs = _rows(_exact(q, x, "q", (tokens, n), torch.uint8), "q")
+    if not _exact(scales, x, "scales", (tokens,), torch.float32).is_contiguous():
+        raise ValueError("scales must be packed")
+    _tables(cos, sin, tokens, rd, x)
+    st = getattr(load(), fname)(_ptr(x), _ptr(_vec(weight, n, "weight", x)), _ptr(cos), _ptr(sin),
                                 _ptr(q), _ptr(scales), tokens, heads, head_dim, rd, xs, qs,
                                 _dtype(x), _dtype(cos), int(bool(neox)), eps, _stream(x))
     _check(fname, st)
@@ -206,14 +237,16 @@ def rmsnorm_rope_fp8_rounded_fwd(x, weight, cos, sin, heads: int, head_dim: int,
 def act_quant_fp8_fwd(x, group: int | None = None, q=None, scales=None):
     """E4M3FN codes of 2-D ``x`` with one scale per ``group`` channels (None: per
     row).  Returns (codes uint8 [rows, n], scales float32 [rows, n / group])."""
-    rows, n, xs = _rows(x, "x")
+    rows, n, xs = _rows(_on_device(x, "x"), "x")
     g = n if group is None else group
+    if g < 1:
+        raise ValueError("group must be positive")
     if q is None:
         q = torch.empty((rows, n), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, max(n // g, 1)), dtype=torch.float32, device=x.device)
-    _, _, qs = _rows(q, "q")
-    if not scales.is_contiguous():
+    _, _, qs = _rows(_exact(q, x, "q", (rows, n), torch.uint8), "q")
+    if not _exact(scales, x, "scales", (rows, max(n // g, 1)), torch.float32).is_contiguous():
         raise ValueError("scales must be packed")
     st = load().act_quant_fp8_fwd(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, _dtype(x),
                                   _stream(x))
@@ -225,15 +258,14 @@ def qk_norm_rope_fwd(qkv, q_weight, k_weight, cos, sin, q_heads: int, kv_heads: 
                      head_dim: int, rope_dim: int | None = None, neox: bool = True,
                      eps: float = 1e-6):
     """Per-head RMSNorm + RoPE on the q and k heads of 2-D ``qkv``, in place."""
-    tokens, n, xs = _rows(qkv, "qkv")
+    tokens, n, xs = _rows(_on_device(qkv, "qkv"), "qkv")
     if (q_heads + 2 * kv_heads) * head_dim != n:
         raise ValueError("(q_heads + 2 * kv_heads) * head_dim must equal the row length")
-    for t, nm in ((cos, "cos"), (sin, "sin")):
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
     rd = head_dim if rope_dim is None else rope_dim
-    st = load().qk_norm_rope_fwd(_ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight")),
-                                 _ptr(_vec(k_weight, head_dim, "k_weight")), _ptr(cos), _ptr(sin),
+    _tables(cos, sin, tokens, rd, qkv)
+    st = load().qk_norm_rope_fwd(_ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight", qkv)),
+                                 _ptr(_vec(k_weight, head_dim, "k_weight", qkv)), _ptr(cos),
+                                 _ptr(sin),
                                  tokens, q_heads, kv_heads, head_dim, rd, xs, _dtype(qkv),
                                  _dtype(cos), int(bool(neox)), eps, _stream(qkv))
     _check("qk_norm_rope_fwd", st)
@@ -246,27 +278,29 @@ def qk_norm_rope_fp8_kv_fwd(qkv, q_weight, k_weight, cos, sin, k_cache, v_cache,
                             eps: float = 1e-6):
     """QK RMSNorm + RoPE with q written back into 2-D ``qkv`` and k/v cast to
     E4M3 into the cache rows ``slots`` (int64 per token; None: row t)."""
-    tokens, n, xs = _rows(qkv, "qkv")
+    tokens, n, xs = _rows(_on_device(qkv, "qkv"), "qkv")
     if (q_heads + 2 * kv_heads) * head_dim != n:
         raise ValueError("(q_heads + 2 * kv_heads) * head_dim must equal the row length")
-    for t, nm in ((cos, "cos"), (sin, "sin")):
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be packed [tokens, rope_dim/2]")
+    rd = head_dim if rope_dim is None else rope_dim
+    _tables(cos, sin, tokens, rd, qkv)
+    _same_device(k_cache, qkv, "k_cache")
     num_slots, kvn, cs = _rows(k_cache, "k_cache")
-    if tuple(v_cache.shape) != (num_slots, kvn) or v_cache.stride() != k_cache.stride():
+    if kvn != kv_heads * head_dim:
+        raise ValueError("k_cache rows must hold kv_heads * head_dim codes")
+    _exact(v_cache, qkv, "v_cache", (num_slots, kvn), torch.uint8)
+    if v_cache.stride() != k_cache.stride():
         raise ValueError("v_cache must have k_cache's shape and strides")
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+    if k_cache.dtype != torch.uint8:
         raise ValueError("caches hold uint8 E4M3 codes")
     for t, nm in ((k_scales, "k_scales"), (v_scales, "v_scales")):
-        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (num_slots, kv_heads):
+        if not _exact(t, qkv, nm, (num_slots, kv_heads), torch.float32).is_contiguous():
             raise ValueError(f"{nm} must be packed float32 [num_slots, kv_heads]")
-    if slots is not None and (slots.dtype != torch.int64 or not slots.is_contiguous()
-                              or tuple(slots.shape) != (tokens,)):
+    if slots is not None and not _exact(slots, qkv, "slots", (tokens,),
+                                        torch.int64).is_contiguous():
         raise ValueError("slots must be packed int64 [tokens]")
-    rd = head_dim if rope_dim is None else rope_dim
     st = load().qk_norm_rope_fp8_kv_fwd(
-        _ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight")),
-        _ptr(_vec(k_weight, head_dim, "k_weight")), _ptr(cos), _ptr(sin), _ptr(k_cache),
+        _ptr(qkv), _ptr(_vec(q_weight, head_dim, "q_weight", qkv)),
+        _ptr(_vec(k_weight, head_dim, "k_weight", qkv)), _ptr(cos), _ptr(sin), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(slots), num_slots, tokens, q_heads,
         kv_heads, head_dim, rd, xs, cs, _dtype(qkv), _dtype(cos), int(bool(neox)), eps,
         _stream(qkv))
@@ -282,9 +316,8 @@ def _flat(t, name):
 
 def ew_add_fwd(a, b, out=None):
     """out = a + b (same shape and dtype), one rounding from fp32."""
-    if a.shape != b.shape or a.dtype != b.dtype:
-        raise ValueError("a and b must have the same shape and dtype")
-    y = torch.empty_like(a) if out is None else out
+    _exact(b, _on_device(a, "a"), "b", a.shape, a.dtype)
+    y = torch.empty_like(a) if out is None else _exact(out, a, "out", a.shape, a.dtype)
     st = load().ew_add_fwd(_ptr(_flat(a, "a")), _ptr(_flat(b, "b")), _ptr(_flat(y, "out")),
                            a.numel(), _dtype(a), _stream(a))
     _check("ew_add_fwd", st)
@@ -293,8 +326,10 @@ def ew_add_fwd(a, b, out=None):
 
 def ew_scale_cast_fwd(x, alpha: float, out_dtype=None, out=None):
     """out = (x * alpha) cast to ``out_dtype`` (default: x's dtype)."""
+    _on_device(x, "x")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _exact(out, x, "out", x.shape, out.dtype if out_dtype is None else out_dtype)
     st = load().ew_scale_cast_fwd(_ptr(_flat(x, "x")), _ptr(_flat(out, "out")), x.numel(), alpha,
                                   _dtype(x), _dtype(out), _stream(x))
     _check("ew_scale_cast_fwd", st)
@@ -303,9 +338,8 @@ def ew_scale_cast_fwd(x, alpha: float, out_dtype=None, out=None):
 
 def ew_scale_add_fwd(x, b, alpha: float, out=None):
     """out = x * alpha + b (same shape and dtype)."""
-    if x.shape != b.shape or x.dtype != b.dtype:
-        raise ValueError("x and b must have the same shape and dtype")
-    y = torch.empty_like(x) if out is None else out
+    _exact(b, _on_device(x, "x"), "b", x.shape, x.dtype)
+    y = torch.empty_like(x) if out is None else _exact(out, x, "out", x.shape, x.dtype)
     st = load().ew_scale_add_fwd(_ptr(_flat(x, "x")), _ptr(_flat(b, "b")), _ptr(_flat(y, "out")),
                                  x.numel(), alpha, _dtype(x), _stream(x))
     _check("ew_scale_add_fwd", st)
