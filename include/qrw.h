@@ -33,7 +33,9 @@
  *   `cs_dtype`, either QRW_F32 or equal to dtype.
  * Numerics.  Arithmetic is binary32 (binary64 for the elementwise family's
  *   16-bit outputs, except a plain 16-bit sum); every 16-bit or FP8 output is
- *   rounded once, to nearest-even.
+ *   rounded once, to nearest-even.  A NaN or infinite input leaves unspecified
+ *   the outputs computed from it (its row, its quantisation group or head,
+ *   its rotation pair, or its element) and nothing else.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *   asynchronous on it; argument errors are reported before anything is
  *   enqueued.
