@@ -307,6 +307,53 @@ def compute_dtype(cfg: dict) -> str:
     return "f32"
 
 
+def copy_ceiling(mib: int, sets: int, steps: int = 50):
+    """A plain device copy of ``mib`` MiB (f32, y = x * 1) through the library's
+    elementwise kernel, over ``sets`` rotating buffer pairs and graph-replayed:
+    what a bare 16-byte-per-lane copy of that size reaches on this GPU."""
+    import torch
+
+    lib = __import__("quant_row_workgroup_amd").load()
+    n = (mib << 20) // 4
+    xs = [torch.empty(n, dtype=torch.float32, device="cuda").uniform_() for _ in range(sets)]
+    ys = [torch.empty_like(x) for x in xs]
+
+    def go(i, sp):
+        rc = lib.ew_scale_cast_fwd(ctypes.c_void_p(xs[i % sets].data_ptr()),
+                                   ctypes.c_void_p(ys[i % sets].data_ptr()), n, 1.0, 3, 3,
+                                   ctypes.c_void_p(sp))
+        if rc != 0:
+            raise RuntimeError(f"ew_scale_cast_fwd failed: {rc}")
+
+    cur = torch.cuda.current_stream()
+    for i in range(3):
+        go(i, cur.cuda_stream)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(cur)
+    with torch.cuda.graph(g, stream=cap):
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            go(i, sp)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    end.synchronize()
+    if not torch.equal(ys[(steps - 1) % sets], xs[(steps - 1) % sets]):
+        raise RuntimeError("copy through the elementwise kernel is not exact")
+    us = start.elapsed_time(end) / steps * 1e3
+    moved = 2 * n * 4
+    print(f"[bench] copy ceiling: {mib} MiB in {us:.2f} us, {moved / us / 1e3:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    return {"mib": mib, "us_per_copy": round(us, 3), "GB/s": round(moved / us / 1e3, 1),
+            "frac": round(moved / us / 1e3 / PEAK_HBM_GBS, 4),
+            "kernel": "ew_scale_cast_fwd f32 -> f32, alpha 1 (16 B per lane)"}
+
+
 def resized_workload(name: str, rows: int) -> str:
     """Register ``name`` with another row count as ``name@rows`` and return that
     name (a paged-cache workload keeps at least four cache slots per token)."""
@@ -436,6 +483,10 @@ def main() -> int:
                          "elementwise family) instead of its own count; every other size stays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ceiling", type=int, default=0, metavar="MIB",
+                    help="also time a plain copy of MIB MiB through the library's 16-byte-per-lane "
+                         "elementwise kernel (f32, alpha 1), graph-replayed like the workload, and "
+                         "report it as copy_ceiling (context: what a bare copy of that size reaches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 5 plain device copies of MIB MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -464,6 +515,8 @@ def main() -> int:
     ms = time_gpu(wl, args.steps, args.warmup, args.mode)
     gbs = wl.counted / (ms * 1e-3) / 1e9
     print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+    ceiling = copy_ceiling(args.copy_ceiling, args.sets) if args.copy_ceiling else None
 
     if args.calibrate_copy:
         nb = args.calibrate_copy << 20
@@ -519,6 +572,8 @@ def main() -> int:
         "cpu_baseline": cpu,
         "kernel_src_hash": src_hash,
     }
+    if ceiling is not None:
+        line["copy_ceiling"] = ceiling
     print(json.dumps(line), flush=True)
     return 0
 
