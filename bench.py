@@ -313,7 +313,9 @@ def copy_ceiling(mib: int, sets: int, steps: int = 50):
     what a bare 16-byte-per-lane copy of that size reaches on this GPU."""
     import torch
 
-    lib = __import__("quant_row_workgroup_amd").load()
+    import quant_row_workgroup_amd as qrw
+
+    lib = qrw.load()
     n = (mib << 20) // 4
     xs = [torch.empty(n, dtype=torch.float32, device="cuda").uniform_() for _ in range(sets)]
     ys = [torch.empty_like(x) for x in xs]
