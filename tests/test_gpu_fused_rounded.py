@@ -3,11 +3,17 @@ operator, "TileLang tutorial, ch. 13", s3.3.4: the normalised row is rounded to
 x's dtype and rotated there, then cast per token) against the oracle's
 composition of RMSNorm, RoPE and the per-token cast, through the C ABI.
 
-Bar: scales within 1e-6 relative; codes bit-exact on >= 99.9% of elements.  A
-stored intermediate that lands one 16-bit ulp away (the binary32 product is
-rounded once more on its way to the 16-bit format) can move a code near a RoPE
-cancellation by several of the fine steps of small codes, so codes more than
-one step apart must be small: below 4 in units of the scale (of 448)."""
+Bar.  A stored intermediate can land one 16-bit ulp away from the oracle's (the
+binary32 product is rounded once more on its way to the 16-bit format).  So:
+- a row's scale is within 1e-6 of the oracle's, or, where its largest stored
+  value was such an intermediate, within one 16-bit ulp of it (2^-10 relative
+  in f16, 2^-7 in bf16), in at most max(1, 1%) of the rows;
+- codes more than one step apart must be small, below 4 in units of the
+  scale (of 448): a moved intermediate near a RoPE cancellation can move a
+  small code by several of its fine steps;
+- in the rows whose scale matches, codes are bit-exact on all but at most
+  max(1, 0.1%) of them (in a row whose scale moved, codes near an E4M3
+  rounding boundary move by a step)."""
 import numpy as np
 import pytest
 import torch
@@ -25,17 +31,32 @@ def _value(q):
         torch.float64).numpy()
 
 
+def assert_staged(q, sc, wq, wsc, dt, what):
+    """The staged form's bar (see the module docstring) on codes [T, n] and
+    scales [T]."""
+    rel = np.abs(sc.astype(np.float64) - wsc.astype(np.float64)) / wsc.astype(np.float64)
+    ulp = 2.0 ** (-10 if dt == "f16" else -7)
+    assert np.all(rel <= ulp), f"{what}: scale rel err {rel.max():.3e}"
+    moved = rel > 1e-6
+    assert int(moved.sum()) <= max(1, moved.size // 100), f"{what}: {int(moved.sum())} scales moved"
+    steps = np.abs(ord8(q) - ord8(wq))
+    far = steps > 1
+    assert np.all(np.maximum(np.abs(_value(q)), np.abs(_value(wq)))[far] < 4), what
+    kept = steps[~moved]
+    differ = int((kept != 0).sum())
+    assert differ <= max(1, kept.size // 1000), f"{what}: {differ} codes differ"
+    return {"max_step": int(steps.max()) if steps.size else 0,
+            "exact_frac": float((steps == 0).mean()) if steps.size else 1.0,
+            "scale_rel": float(rel.max()) if rel.size else 0.0, "scales_moved": int(moved.sum()),
+            "far": int(far.sum())}
+
+
 def _check(x, w, c, s, H, D, R, dt, cs, neox, what, eps=1e-6):
     q, sc = qrw.rmsnorm_rope_fp8_rounded_fwd(dev(x, dt), None if w is None else dev(w, dt),
                                              dev(c, cs), dev(s, cs), H, D, R, neox=neox, eps=eps)
     q, sc = host(q), host(sc)
     wq, wsc = oracle.rmsnorm_rope_fp8_rounded(x, w, c, s, H, D, R, dt, cs, neox, eps)
-    rel = assert_scales(sc, wsc, what=what)
-    steps = np.abs(ord8(q) - ord8(wq))
-    far = steps > 1
-    assert np.all(np.maximum(np.abs(_value(q)), np.abs(_value(wq)))[far] < 4), what
-    st = assert_codes(q, wq, max_step=int(steps.max()) if steps.size else 0, what=what)
-    return dict(st, scale_rel=rel, far=int(far.sum()))
+    return assert_staged(q, sc, wq, wsc, dt, what)
 
 
 def test_rounded_workload_shape():

@@ -14,7 +14,8 @@ import pytest
 import oracle
 import quant_row_workgroup_amd as qrw
 from quant_row_workgroup_amd import synth
-from tests import test_gpu_ew, test_gpu_fused, test_gpu_qk_kv, test_gpu_qk_norm_rope
+from tests import (test_gpu_ew, test_gpu_fused, test_gpu_fused_rounded, test_gpu_qk_kv,
+                   test_gpu_qk_norm_rope)
 from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_terms
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +25,7 @@ N_CASES = 32
 
 def _rng(op, i):
     return np.random.default_rng(1000 * (1 + ["norm", "rope", "fused", "aq", "qk", "kv",
-                                              "ew"].index(op)) + i)
+                                              "ew", "staged"].index(op)) + i)
 
 
 def _row_len(r, lo, hi):
@@ -199,3 +200,22 @@ def test_random_elementwise(i):
     got = test_gpu_ew._run(kind, x, b, alpha, xf, yf)
     want = oracle.ew_scale_add(x, b, alpha, xf, yf)
     test_gpu_ew._compare(got, want, yf, what=f"ew {kind} n={n} {xf}->{yf} alpha={alpha}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_staged_fused(i):
+    # the staged form's own bar (test_gpu_fused_rounded.assert_staged)
+    r = _rng("staged", i)
+    dt = ["f16", "bf16"][int(r.integers(0, 2))]
+    cs = ["f32", dt][int(r.integers(0, 2))]
+    neox = bool(r.integers(0, 2))
+    H, D, R = _heads(r)
+    T = _tokens(r, H * D)
+    x = synth.normal(i, (T, H * D), 0.0, 2.0, dt, outlier_frac=0.01, outlier_mul=10.0)
+    w = synth.normal(i + 1, (H * D,), 1.0, 0.1, dt) if r.integers(0, 3) else None
+    c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 4 else 7.0)
+    q, sc = qrw.rmsnorm_rope_fp8_rounded_fwd(dev(x, dt), None if w is None else dev(w, dt),
+                                             dev(c, cs), dev(s, cs), H, D, R, neox=neox)
+    wq, wsc = oracle.rmsnorm_rope_fp8_rounded(x, w, c, s, H, D, R, dt, cs, neox, 1e-6)
+    test_gpu_fused_rounded.assert_staged(host(q), host(sc), wq, wsc, dt,
+                                         f"staged {T}x{H}x{D}/{R} {dt}/{cs}")
