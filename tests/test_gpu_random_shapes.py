@@ -20,7 +20,7 @@ from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_term
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 96
 
 
 def _rng(op, i):
