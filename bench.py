@@ -21,8 +21,14 @@ read once, every output written once): 51,404,800 B for this workload.
 size) as recorded in profiles/<workload>_traffic.txt, and only while the
 kernel sources are the ones those counters were taken on; otherwise null.
 
-`cpu_baseline` times the CPU checker (single-threaded C, float64) on a bounded
-sample of the same workload on this host.
+`cpu_baseline` times the CPU checker (plain C, float64) on a bounded sample of
+the same workload on this host: on one thread per core (at most 16) over
+contiguous blocks of rows (`value`, `cores`), and on one thread
+(`single_thread_value`).
+
+Options: --workload runs any of the named workloads instead, --rows runs it at
+another row (token) count, and --copy-ceiling MIB adds `copy_ceiling`, a bare
+copy of that size through the library's elementwise kernel, for context.
 
 Prints one JSON line on stdout.
 """
