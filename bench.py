@@ -8,8 +8,10 @@ One step = one launch of the operator over one 4096 x 4096 batch.  The batch
 rotates over --sets independent input/output buffer sets (default 8 x 51.4 MB,
 more than the 256 MB last-level cache), so every launch reads inputs that sit
 in HBM rather than in cache.  The K timed steps are captured once into a HIP
-graph and replayed, bracketed by HIP events on the launch stream; the events
-give the average launch duration, and
+graph; untimed replays run for about 50 ms first (the GPU settles at its
+steady clocks), and the timed replay is enqueued behind the last of them,
+bracketed by HIP events on the launch stream, so the host-side graph launch
+is not in the timed region, which holds exactly K launches.  The events give the average launch duration, and
 
     achieved GB/s = counted bytes per launch / average launch duration
 
@@ -26,9 +28,19 @@ the same workload on this host: on one thread per core (at most 16) over
 contiguous blocks of rows (`value`, `cores`), and on one thread
 (`single_thread_value`).
 
+`copy_ceiling` (fused workloads with rows of 4096 bf16 channels, on by
+default): the same launches with the operator's arithmetic replaced by byte
+selection -- the same grid, loads and stores on the same buffers
+(qrw_probe_copy_fused_traffic) -- i.e. what a kernel with this access
+structure reaches at this size, its variant without the row dependency, and
+the same grid doing nothing (the fixed cost of a launch).
+
 Options: --workload runs any of the named workloads instead, --rows runs it at
-another row (token) count, and --copy-ceiling MIB adds `copy_ceiling`, a bare
-copy of that size through the library's elementwise kernel, for context.
+another row (token) count, --plain-copy MIB adds `plain_copy`, a bare copy of
+that size through the library's elementwise kernel, --timeline L adds
+per-wave timestamps of the fused kernel over L consecutive launches, and
+--trace-summary CSV prints p10/p50/p90 kernel durations of a rocprofv3
+kernel-trace file.
 
 Prints one JSON line on stdout.
 """
@@ -57,8 +69,8 @@ KERNEL_SOURCES = {
     "rmsnorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "layernorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
-    "fused": ("qrw_rope.hip", "qrw_fused_tail.hip", "qrw_plan.h", "qrw_device.h",
-              "qrw_launch.h"),
+    "fused": ("qrw_rope.hip", "qrw_fused_contig.h", "qrw_fused_tail.hip", "qrw_plan.h",
+              "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
                      "qrw_qknorm_gc_b.hip", "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),
@@ -288,6 +300,11 @@ def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
             if not torch.equal(a, b):
                 raise RuntimeError("graph replay differs from eager launches")
         torch.cuda.synchronize()
+        settle(g)
+        # The last untimed replay is still running when the host submits the
+        # timed one, so the start event fires when the GPU finishes it and the
+        # timed region holds exactly `steps` launches back to back, with no
+        # host-side graph launch inside it.
         start.record()
         g.replay()
         end.record()
@@ -313,7 +330,55 @@ def compute_dtype(cfg: dict) -> str:
     return "f32"
 
 
-def copy_ceiling(mib: int, sets: int, steps: int = 50):
+SETTLE_MS = 50.0
+
+
+def settle(g) -> None:
+    """Replay graph ``g`` untimed for about SETTLE_MS of GPU time, ending with
+    one replay left running: the GPU reaches its steady clocks before a timed
+    region (a short run otherwise times part of the ramp), and the host can
+    enqueue the timed replay behind it."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    b.synchronize()
+    per = max(a.elapsed_time(b), 1e-3)
+    for _ in range(max(1, min(2000, int(SETTLE_MS / per) + 1))):
+        g.replay()
+
+
+def graph_time(launch, steps: int, warmup: int = 3) -> float:
+    """Milliseconds per launch of ``launch(i, stream_ptr)`` (i = 0 .. steps-1),
+    captured once in a HIP graph: one untimed replay is enqueued, then the timed
+    replay between HIP events on the same stream, so the host-side graph launch
+    stays outside the timed region."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i, cur.cuda_stream)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(cur)
+    with torch.cuda.graph(g, stream=cap):
+        sp = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            launch(i, sp)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(g)
+    start.record()
+    g.replay()
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def plain_copy(mib: int, sets: int, steps: int = 50):
     """A plain device copy of ``mib`` MiB (f32, y = x * 1) through the library's
     elementwise kernel, over ``sets`` rotating buffer pairs and graph-replayed:
     what a bare 16-byte-per-lane copy of that size reaches on this GPU."""
@@ -333,33 +398,153 @@ def copy_ceiling(mib: int, sets: int, steps: int = 50):
         if rc != 0:
             raise RuntimeError(f"ew_scale_cast_fwd failed: {rc}")
 
-    cur = torch.cuda.current_stream()
-    for i in range(3):
-        go(i, cur.cuda_stream)
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(cur)
-    with torch.cuda.graph(g, stream=cap):
-        sp = torch.cuda.current_stream().cuda_stream
-        for i in range(steps):
-            go(i, sp)
+    ms = graph_time(go, steps)
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    end.synchronize()
     if not torch.equal(ys[(steps - 1) % sets], xs[(steps - 1) % sets]):
         raise RuntimeError("copy through the elementwise kernel is not exact")
-    us = start.elapsed_time(end) / steps * 1e3
+    us = ms * 1e3
     moved = 2 * n * 4
-    print(f"[bench] copy ceiling: {mib} MiB in {us:.2f} us, {moved / us / 1e3:.1f} GB/s",
+    print(f"[bench] plain copy: {mib} MiB in {us:.2f} us, {moved / us / 1e3:.1f} GB/s",
           file=sys.stderr, flush=True)
     return {"mib": mib, "us_per_copy": round(us, 3), "GB/s": round(moved / us / 1e3, 1),
             "frac": round(moved / us / 1e3 / PEAK_HBM_GBS, 4),
             "kernel": "ew_scale_cast_fwd f32 -> f32, alpha 1 (16 B per lane)"}
+
+
+def fused_probe_shape(cfg: dict) -> bool:
+    """The probes reproduce the fused operator's benchmark layout only: rows of
+    4096 bf16 channels in 32 heads of 128 rotating whole (NeoX), bf16 tables."""
+    return (cfg["op"] == "fused" and cfg["heads"] * cfg["head_dim"] == 4096
+            and cfg["head_dim"] == 128 and cfg["rope_dim"] == 128 and cfg["dtype"] == "bf16"
+            and cfg["cs_dtype"] == "bf16" and cfg["neox"] and not cfg.get("staged"))
+
+
+def same_traffic_ceiling(wl, steps: int):
+    """The fused operator's memory traffic and grid with no arithmetic
+    (qrw_probe_copy_fused_traffic, include/qrw_probe.h) on the workload's own
+    buffers, and the same grid doing nothing (qrw_probe_empty): what a kernel
+    with this access structure reaches at this size, and a launch's fixed cost."""
+    import torch
+
+    import quant_row_workgroup_amd as qrw
+
+    P = qrw.load_probe()
+    T = wl.cfg["tokens"]
+    blocks = (T + 3) // 4
+    empty = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def copy(dep):
+        def go(i, sp):
+            s = wl.sets[i % len(wl.sets)]
+            rc = P.qrw_probe_copy_fused_traffic(ptr(s["x"]), ptr(s["w"]), ptr(s["cos"]),
+                                                ptr(s["sin"]), ptr(s["q"]), ptr(s["scales"]), T,
+                                                4096, dep, ctypes.c_void_p(sp))
+            if rc != 0:
+                raise RuntimeError(f"qrw_probe_copy_fused_traffic: status {rc}")
+        return go
+
+    def nothing(i, sp):
+        rc = P.qrw_probe_empty(ptr(empty), blocks, ctypes.c_void_p(sp))
+        if rc != 0:
+            raise RuntimeError(f"qrw_probe_empty: status {rc}")
+
+    out = {}
+    for key, fn in (("row_dependency", copy(1)), ("no_dependency", copy(0))):
+        ms = graph_time(fn, steps)
+        gbs = wl.counted / (ms * 1e-3) / 1e9
+        out[key] = {"us_per_launch": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    ms = graph_time(nothing, steps)
+    torch.cuda.synchronize()
+    if not torch.equal(empty.view(-1, 4)[:, 0].cpu(), torch.arange(blocks, dtype=torch.int32)):
+        raise RuntimeError("empty-grid probe wrote the wrong words")
+    wl.reset()
+    print(f"[bench] same-traffic copy: {out['row_dependency']['us_per_launch']:.3f} us "
+          f"(no row dependency {out['no_dependency']['us_per_launch']:.3f} us); empty grid "
+          f"of {blocks} workgroups {ms * 1e3:.3f} us", file=sys.stderr, flush=True)
+    return {
+        "kernel": ("qrw_probe_copy_fused_traffic: the fused operator's grid, loads and stores "
+                   "(51.4 MB at 4096 tokens) with byte selection in place of arithmetic; no "
+                   "store before the wave's whole row has arrived"),
+        "us_per_launch": out["row_dependency"]["us_per_launch"],
+        "GB/s": out["row_dependency"]["GB/s"],
+        "frac": out["row_dependency"]["frac"],
+        "no_row_dependency": out["no_dependency"],
+        "empty_grid_us_per_launch": round(ms * 1e3, 3),
+    }
+
+
+def timeline(wl, launches: int):
+    """Per-wave timestamps of the fused kernel (qrw_probe_fused_timeline: the
+    library's contiguous kernel with the constant 100 MHz clock read at entry,
+    once the row's sum of squares is known, after the last store is issued and
+    once the stores are done) over ``launches`` consecutive graph-replayed
+    launches on rotating buffer sets.  Times are microseconds from each
+    launch's first wave; ``gap_to_next`` runs from a launch's last completed
+    store to the next launch's first wave."""
+    import numpy as np
+    import torch
+
+    import quant_row_workgroup_amd as qrw
+
+    P = qrw.load_probe()
+    T = wl.cfg["tokens"]
+    stamps = torch.zeros((launches, T, 4), dtype=torch.int64, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def go(i, sp):
+        s = wl.sets[i % len(wl.sets)]
+        rc = P.qrw_probe_fused_timeline(ptr(s["x"]), ptr(s["w"]), ptr(s["cos"]), ptr(s["sin"]),
+                                        ptr(s["q"]), ptr(s["scales"]), T, wl.cfg["eps"],
+                                        ptr(stamps[i % launches]), ctypes.c_void_p(sp))
+        if rc != 0:
+            raise RuntimeError(f"qrw_probe_fused_timeline: status {rc}")
+
+    ms = graph_time(go, launches)
+    st = stamps.cpu().numpy().astype(np.float64) * 0.01  # 100 MHz ticks -> us
+    names = ("entry", "row_arrived", "stores_issued", "stores_done")
+    per = {k: [] for k in names}
+    gaps, spans = [], []
+    for k in range(launches):
+        t0 = st[k, :, 0].min()
+        for j, nm in enumerate(names):
+            per[nm].append(st[k, :, j] - t0)
+        spans.append(st[k, :, 3].max() - t0)
+        if k + 1 < launches:
+            gaps.append(st[k + 1, :, 0].min() - st[k, :, 3].max())
+    q = lambda a, p: round(float(np.percentile(np.concatenate(a), p)), 3)
+    out = {"launches": launches, "us_per_launch": round(ms * 1e3, 3),
+           "first_wave_to_last_store_done_us": round(float(np.median(spans)), 3),
+           "gap_to_next_us": round(float(np.median(gaps)), 3) if gaps else None}
+    for nm in names:
+        out[nm] = {f"p{p}": q(per[nm], p) for p in (0, 10, 50, 90, 99, 100)}
+    arith = [per["stores_issued"][k] - per["row_arrived"][k] for k in range(launches)]
+    out["arrived_to_issued"] = {f"p{p}": q(arith, p) for p in (0, 50, 99, 100)}
+    print(f"[bench] timeline: {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
+
+
+def trace_summary(path: str) -> str:
+    """Per-kernel duration statistics (count, mean, p10, p50, p90, min, max, in
+    microseconds) of a rocprofv3 --kernel-trace CSV."""
+    import csv
+
+    import numpy as np
+
+    durs = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
+            durs.setdefault(row["Kernel_Name"], []).append(d)
+    lines = [f"{'count':>7} {'mean_us':>9} {'p10_us':>9} {'p50_us':>9} {'p90_us':>9} "
+             f"{'min_us':>9} {'max_us':>9}  kernel"]
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        p10, p50, p90 = np.percentile(a, [10, 50, 90])
+        lines.append(f"{len(a):>7} {a.mean():9.3f} {p10:9.3f} {p50:9.3f} {p90:9.3f} "
+                     f"{a.min():9.3f} {a.max():9.3f}  {name[:160]}")
+    return "\n".join(lines)
 
 
 def resized_workload(name: str, rows: int) -> str:
@@ -491,14 +676,27 @@ def main() -> int:
                          "elementwise family) instead of its own count; every other size stays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-ceiling", type=int, default=0, metavar="MIB",
+    ap.add_argument("--plain-copy", type=int, default=0, metavar="MIB",
                     help="also time a plain copy of MIB MiB through the library's 16-byte-per-lane "
                          "elementwise kernel (f32, alpha 1), graph-replayed like the workload, and "
-                         "report it as copy_ceiling (context: what a bare copy of that size reaches)")
+                         "report it as plain_copy (context: what a bare copy of that size reaches)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the same-traffic copy and empty-grid probes (fused 4096-wide "
+                         "workloads run them by default and report copy_ceiling)")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="fused 4096-wide workloads: per-wave timestamps over LAUNCHES "
+                         "consecutive launches, reported as timeline")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-kernel duration statistics of a rocprofv3 kernel-trace CSV "
+                         "and exit (no GPU work)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 5 plain device copies of MIB MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -524,7 +722,12 @@ def main() -> int:
     gbs = wl.counted / (ms * 1e-3) / 1e9
     print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
-    ceiling = copy_ceiling(args.copy_ceiling, args.sets) if args.copy_ceiling else None
+    ceiling = None
+    if fused_probe_shape(wl.cfg) and not args.no_ceiling:
+        ceiling = same_traffic_ceiling(wl, args.steps)
+        ceiling["kernel_over_ceiling"] = round(ms * 1e3 / ceiling["us_per_launch"], 4)
+    tl = timeline(wl, args.timeline) if args.timeline and fused_probe_shape(wl.cfg) else None
+    plain = plain_copy(args.plain_copy, args.sets) if args.plain_copy else None
 
     if args.calibrate_copy:
         nb = args.calibrate_copy << 20
@@ -582,6 +785,10 @@ def main() -> int:
     }
     if ceiling is not None:
         line["copy_ceiling"] = ceiling
+    if tl is not None:
+        line["timeline"] = tl
+    if plain is not None:
+        line["plain_copy"] = plain
     print(json.dumps(line), flush=True)
     return 0
 

@@ -10,6 +10,8 @@ are a thin ctypes binding with the same names.
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    PROBE_EXPORTS,
+    PROBE_LIB_PATH,
     QrwError,
     act_quant_fp8_fwd,
     layernorm_fwd,
@@ -17,6 +19,7 @@ from ._binding import (  # noqa: F401
     ew_scale_add_fwd,
     ew_scale_cast_fwd,
     load,
+    load_probe,
     qk_norm_rope_fp8_kv_fwd,
     rmsnorm_rope_fp8_rounded_fwd,
     qk_norm_rope_fwd,

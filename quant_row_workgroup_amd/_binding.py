@@ -16,6 +16,7 @@ import torch  # the library shares torch's HIP runtime: load torch first
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqrw.so")
+PROBE_LIB_PATH = os.path.join(_HERE, "libqrw_probe.so")
 
 F16, BF16, F32 = 1, 2, 3
 _DTYPE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
@@ -73,6 +74,35 @@ def load():
     L.qrw_status_string.argtypes = [i32]
     L.qrw_status_string.restype = ctypes.c_char_p
     _lib = L
+    return L
+
+
+PROBE_EXPORTS = ("qrw_probe_copy_fused_traffic", "qrw_probe_empty", "qrw_probe_fused_timeline",
+                 "qrw_probe_sweep", "qrw_probe_recip_values")
+
+_probe = None
+
+
+def load_probe():
+    """Load libqrw_probe.so (include/qrw_probe.h): the benchmark's and the GPU
+    tests' measurement and self-check kernels, not operators."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise ImportError(f"{PROBE_LIB_PATH} is missing: build it with "
+                          "`python -m quant_row_workgroup_amd.build`")
+    L = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, i64, i32, u32, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                              ctypes.c_float)
+    L.qrw_probe_copy_fused_traffic.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]
+    L.qrw_probe_empty.argtypes = [vp, i64, vp]
+    L.qrw_probe_fused_timeline.argtypes = [vp, vp, vp, vp, vp, vp, i64, f32, vp, vp]
+    L.qrw_probe_sweep.argtypes = [i32, u32, u32, u32, vp, i64, vp]
+    L.qrw_probe_recip_values.argtypes = [vp, vp, vp, i64, vp]
+    for name in PROBE_EXPORTS:
+        getattr(L, name).restype = i32
+    _probe = L
     return L
 
 

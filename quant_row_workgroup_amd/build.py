@@ -1,4 +1,6 @@
-"""Build the HIP library ``libqrw.so`` in-tree for gfx950.
+"""Build the HIP library ``libqrw.so`` in-tree for gfx950, and beside it
+``libqrw_probe.so`` (csrc/probe: the benchmark's same-traffic copy, empty-grid
+and timeline kernels, and the GPU tests' exhaustive arithmetic sweeps).
 
 Compiled with hipcc -O3 and no fast-math; packed-fp32 instruction generation
 is switched off (``-packed-fp32-ops``) so binary32 math is emitted as scalar
@@ -18,11 +20,16 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqrw.so")
+PROBE_LIB = os.path.join(PKG, "libqrw_probe.so")
 ARCH = "gfx950"
 
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def probe_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
 
 
 def torch_lib_dir():
@@ -45,15 +52,29 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall"]
 
 
+def _link(objs, out, verbose):
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp"] + objs
+    tl = torch_lib_dir()
+    if tl:
+        cmd += [f"-Wl,-rpath,{tl}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     """Compile each source to an object in parallel (bounded by ``jobs``, default
-    the CPU count, at most 16), then link the shared library."""
+    the CPU count, at most 16), then link the operator library and the probe
+    library.  Returns the operator library's path."""
     from concurrent.futures import ThreadPoolExecutor
 
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
+    psrcs = probe_sources()
     objs = [os.path.join(objdir, os.path.basename(f)[:-4] + ".o") for f in srcs]
+    pobjs = [os.path.join(objdir, "probe_" + os.path.basename(f)[:-4] + ".o") for f in psrcs]
 
     def compile_one(pair):
         src, obj = pair
@@ -64,9 +85,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     n = jobs or min(16, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=n) as ex:
-        results = list(ex.map(compile_one, zip(srcs, objs)))
+        results = list(ex.map(compile_one, zip(srcs + psrcs, objs + pobjs)))
     failed = False
-    for src, r in zip(srcs, results):
+    for src, r in zip(srcs + psrcs, results):
         out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops' is not a recognized feature" not in line)
         if out.strip():
@@ -76,14 +97,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             failed = True
     if failed:
         raise subprocess.CalledProcessError(1, "hipcc")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
-    tl = torch_lib_dir()
-    if tl:
-        cmd += [f"-Wl,-rpath,{tl}"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    _link(objs, LIB, verbose)
+    _link(pobjs, PROBE_LIB, verbose)
     return LIB
 
 

@@ -301,10 +301,13 @@ __device__ __forceinline__ float tree8(const float (&a)[8]) {
 // ----------------------------------------------------------------- FP8
 // Eight f32 values (already scaled into [-448, 448]) to eight E4M3FN codes,
 // element k in byte k.
+// Each conversion writes one 16-bit half of its destination and keeps the
+// other; the first of each pair starts from v[0] (resp. v[4]) as the kept half,
+// which the second overwrites, so no destination needs zeroing first.
 __device__ __forceinline__ u32x2 fp8x8(const float (&v)[8]) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], __builtin_bit_cast(int, v[0]), false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], __builtin_bit_cast(int, v[4]), false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
   return (u32x2){(uint32_t)lo, (uint32_t)hi};
 }

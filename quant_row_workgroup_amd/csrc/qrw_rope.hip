@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "qrw_device.h"
+#include "qrw_fused_contig.h"
 #include "qrw_launch.h"
 #include "qrw_plan.h"
 
@@ -258,123 +259,17 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
 
 
 // ------------------------------------------------------------------ fused, contiguous
-// The operator when every head rotates whole (rope_dim == head_dim), a head is
-// 2*XD granules with XD = head_dim/16 in {1, 2, 4, 8, 16}, and the row is G
-// whole wave blocks (n == 512 * G).  Lane l takes granules l, l+64, ..., so
-// every load and store instruction of the wave covers one contiguous block
-// (1 KiB of x, 512 B of codes).  A head then occupies 2*XD consecutive lanes:
-// in the NeoX pairing the partner of lane l is lane l ^ XD, read with a lane
-// exchange (lane_xor); in the interleaved pairing both members of a pair sit
-// in the same granule.  Each lane needs a single table granule per token.
-// The arithmetic is that of rotate(): first of a pair x_a c - x_b s as
-// fma(x_a, c, x_b * (-s)), second x_b c + x_a s as fma(x_b, c, x_a * s).
-// Rows (waves) per workgroup: 4 for the exact form; 16 for the staged form,
-// whose longer arithmetic measured faster with 1024-thread workgroups on
-// 4096 x 4096 bf16 (12.7 against 13.4 us; the exact form: 11.0 at 4, 11.1-11.3
-// at 8, 11.5-12.1 at 16).
-template <bool MID>
-constexpr int kContigRows = MID ? 16 : 4;
+// One wave per token, kContigRows<MID> tokens per workgroup; the token body
+// and its layout are in qrw_fused_contig.h.
 template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID>
 __global__ __launch_bounds__(kWave * kContigRows<MID>) void rmsnorm_rope_fp8_contig_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
-    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, float n_f,
-    float eps) {
+    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kContigRows<MID> + (threadIdx.x >> 6);
   if (t >= tokens) return;
-  const uint16_t* xr = x + t * xs;
-  uint8_t* qr = q + t * qs;
-  const int j = lane & (2 * XD - 1);  // granule index inside the head
-
-  u32x4 r[G], wr[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
-  if (HAS_W) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) wr[g] = ld16(w + 8 * (kWave * g + lane));
-  }
-  float c[8], sn[8];
-  const char* crow = table_row<CS>(cosv, t, half);
-  const char* srow = table_row<CS>(sinv, t, half);
-  if (NEOX) {
-    Table8<CS>::load(crow, j & (XD - 1), c);
-    Table8<CS>::load(srow, j & (XD - 1), sn);
-    if (j < XD) {  // first half of the head: y = x c - x_partner s
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sn[e] = -sn[e];
-    }
-  } else {
-    float c4[4], s4[4];
-    Table4<CS>::load(crow, j, c4);
-    Table4<CS>::load(srow, j, s4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      c[k] = c4[k];
-      sn[k] = s4[k];
-    }
-  }
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[(2 * g + k) & 7] = sumsq2(T{}, r[g][k], acc[(2 * g + k) & 7]);
-  }
-  const float ss = wave_sum(tree8(acc));
-  const float rstd = 1.0f / sqrtf(ss / n_f + eps);
-
-  float v[G][8];
-  float m[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    widen8<T>(r[g], v[g]);
-    if (HAS_W) {
-      float f[8];
-      widen8<T>(wr[g], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[g][e] *= f[e];
-    }
-    if (MID) {  // the staged form (see rmsnorm_rope_fp8_kernel): store x*w*rstd in T
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[g][e] *= rstd;
-      round8<T>(v[g]);
-    }
-    if (NEOX) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[g][e] = fmaf(v[g][e], c[e], lane_xor<XD>(v[g][e]) * sn[e]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = v[g][2 * k], x1 = v[g][2 * k + 1];
-        v[g][2 * k] = fmaf(x0, c[k], -(x1 * sn[k]));
-        v[g][2 * k + 1] = fmaf(x1, c[k], x0 * sn[k]);
-      }
-    }
-    if (MID) round8<T>(v[g]);
-#pragma unroll
-    for (int e = 0; e < 8; e += 2)
-      m[(e >> 1) & 3] = fmaxf(m[(e >> 1) & 3], fmaxf(fabsf(v[g][e]), fabsf(v[g][e + 1])));
-  }
-  const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-  const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
-  const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
-  const float kq = rstd / scale;
-  const float inv = recip_rn(scale);
-  if (lane == 0) scales[t] = scale;
-
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float a[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = MID ? div_rn(v[g][e], scale, inv) : v[g][e] * kq;
-    // codes: plain stores for the exact form, non-temporal for the staged one
-    // (each measured faster on 4096 x 4096 bf16: 10.97 against 11.45 us, and
-    // 12.29 against 12.71 us)
-    if (MID)
-      st8_stream(qr + 8 * (kWave * g + lane), fp8x8(a));
-    else
-      st8(qr + 8 * (kWave * g + lane), fp8x8(a));
-  }
+  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs, qs,
+                                                       eps, lane, nullptr);
 }
 
 // ------------------------------------------------------------------ fused, dense
@@ -595,20 +490,20 @@ void contig_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, 
     const dim3 cg((unsigned)((tokens + R - 1) / R));
     if (w)
       rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, true><<<cg, kWave * R, 0, st>>>(
-          x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
     else
       rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, true><<<cg, kWave * R, 0, st>>>(
-          x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
     return;
   }
   constexpr int R = kContigRows<false>;
   const dim3 cg((unsigned)((tokens + R - 1) / R));
   if (w)
     rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false><<<cg, kWave * R, 0, st>>>(
-        x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+        x, w, c, s, q, sc, tokens, xs, qs, eps);
   else
     rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, false><<<cg, kWave * R, 0, st>>>(
-        x, w, c, s, q, sc, tokens, xs, qs, pl.half, n_f, eps);
+        x, w, c, s, q, sc, tokens, xs, qs, eps);
 }
 
 template <typename T, typename CS, bool NEOX, int G>

@@ -12,6 +12,7 @@ import quant_row_workgroup_amd as qrw
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qrw.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "qrw_probe.h")
 
 OK, NULL, DTYPE, SHAPE, STRIDE, ALIGN, ALIAS, LAUNCH, VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F16, BF16, F32 = 1, 2, 3
@@ -31,8 +32,8 @@ def _host_only():
         pytest.skip("argument-validation cases use fake device addresses: run without a GPU")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
@@ -45,6 +46,37 @@ def test_library_exports_every_declared_symbol():
     L = qrw.load()
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_probe_header_matches_the_probe_library():
+    # include/qrw_probe.h: the measurement and self-check kernels' library
+    assert declared_functions(PROBE_HEADER) == sorted(qrw.PROBE_EXPORTS)
+    P = qrw.load_probe()
+    for name in declared_functions(PROBE_HEADER):
+        assert hasattr(P, name), name
+
+
+def test_probe_validation():
+    P = qrw.load_probe()
+    # wrong row length, negative sizes, bad sweep ranges, bad block counts:
+    # refused before anything is enqueued
+    assert P.qrw_probe_copy_fused_traffic(X, W, C, S, Q, SC, 4, 2048, 1, None) == SHAPE
+    assert P.qrw_probe_copy_fused_traffic(X, W, C, S, Q, SC, 0, 4096, 1, None) == OK
+    assert P.qrw_probe_copy_fused_traffic(None, W, C, S, Q, SC, 4, 4096, 1, None) == NULL
+    assert P.qrw_probe_copy_fused_traffic(ctypes.c_void_p((1 << 32) + 8), W, C, S, Q, SC, 4,
+                                          4096, 1, None) == ALIGN
+    assert P.qrw_probe_empty(X, -1, None) == SHAPE
+    assert P.qrw_probe_empty(None, 4, None) == NULL
+    assert P.qrw_probe_fused_timeline(X, W, C, S, Q, SC, 4, -1.0, Y, None) == VALUE
+    assert P.qrw_probe_fused_timeline(X, W, C, S, Q, SC, 4, 1e-6, None, None) == NULL
+    assert P.qrw_probe_sweep(3, 1, 2, 1, Y, 1, None) == VALUE
+    assert P.qrw_probe_sweep(0, 2, 2, 1, Y, 1, None) == SHAPE
+    assert P.qrw_probe_sweep(0, 0, 0x7F800001, 1, Y, 1, None) == SHAPE
+    assert P.qrw_probe_sweep(0, 0, 512, 1, Y, 1, None) == SHAPE      # needs 2 blocks
+    assert P.qrw_probe_sweep(0, 0, 512, 4097, Y, 1, None) == SHAPE
+    assert P.qrw_probe_sweep(0, 0, 512, 1, None, 2, None) == NULL
+    assert P.qrw_probe_recip_values(X, Y, W, -1, None) == SHAPE
+    assert P.qrw_probe_recip_values(X, Y, W, 0, None) == OK
 
 
 def test_status_strings():
