@@ -63,11 +63,11 @@ def _load():
     L.oracle_encode_bf16.restype = ctypes.c_uint16
     L.oracle_encode_e4m3.argtypes = [ctypes.c_double]
     L.oracle_encode_e4m3.restype = ctypes.c_uint8
-    L.oracle_rmsnorm.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, f32]
+    L.oracle_rmsnorm.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, f32, vp]
     L.oracle_rmsnorm.restype = None
     L.oracle_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32]
     L.oracle_layernorm.restype = None
-    L.oracle_rope.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32]
+    L.oracle_rope.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
     L.oracle_rope.restype = None
     L.oracle_rmsnorm_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                           i64, i64, i32, i32, i32, f32, vp]
@@ -129,8 +129,10 @@ def encode_e4m3(v: float) -> int:
 
 # ---------------------------------------------------------------- operators
 def rmsnorm(x, w, dtype: str, eps: float, n: int | None = None, y_stride: int | None = None,
-            fill: int = 0):
-    """y[r, :n] = RMSNorm(x[r, :n]) * w, rounded once to ``dtype``."""
+            fill: int = 0, want_u: bool = False):
+    """y[r, :n] = RMSNorm(x[r, :n]) * w, rounded once to ``dtype``.  With
+    ``want_u`` also returns u = x * rstd * w in float64 before the rounding,
+    [rows, n]."""
     L = _load()
     x = _check(x, dtype, "x")
     w = _check(w, dtype, "w")
@@ -138,8 +140,9 @@ def rmsnorm(x, w, dtype: str, eps: float, n: int | None = None, y_stride: int | 
     n = xs if n is None else n
     ys = n if y_stride is None else y_stride
     y = np.full((rows, ys), fill, dtype=_STORAGE[dtype])
-    L.oracle_rmsnorm(_ptr(x), _ptr(w), _ptr(y), rows, n, xs, ys, DTYPE_CODE[dtype], eps)
-    return y
+    u = np.zeros((rows, n), dtype=np.float64) if want_u else None
+    L.oracle_rmsnorm(_ptr(x), _ptr(w), _ptr(y), rows, n, xs, ys, DTYPE_CODE[dtype], eps, _ptr(u))
+    return (y, u) if want_u else y
 
 
 def layernorm(x, gamma, beta, dtype: str, eps: float, n: int | None = None,
@@ -159,9 +162,10 @@ def layernorm(x, gamma, beta, dtype: str, eps: float, n: int | None = None,
 
 
 def rope(x, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str, cs_dtype: str,
-         neox: bool, y_stride: int | None = None, fill: int = 0):
+         neox: bool, y_stride: int | None = None, fill: int = 0, want_z: bool = False):
     """RoPE on each head's tail span.  x: [tokens, >= heads*head_dim];
-    cos/sin: [tokens, rope_dim/2]."""
+    cos/sin: [tokens, rope_dim/2].  With ``want_z`` also returns every output
+    in float64 before its rounding, [tokens, heads*head_dim]."""
     L = _load()
     x = _check(x, dtype, "x")
     cos = _check(cos, cs_dtype, "cos")
@@ -171,9 +175,10 @@ def rope(x, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str, cs_d
     assert cos.shape == (tokens, rope_dim // 2) and sin.shape == cos.shape
     ys = n if y_stride is None else y_stride
     y = np.full((tokens, ys), fill, dtype=_STORAGE[dtype])
+    z = np.zeros((tokens, n), dtype=np.float64) if want_z else None
     L.oracle_rope(_ptr(x), _ptr(cos), _ptr(sin), _ptr(y), tokens, heads, head_dim, rope_dim,
-                  xs, ys, DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)))
-    return y
+                  xs, ys, DTYPE_CODE[dtype], DTYPE_CODE[cs_dtype], int(bool(neox)), _ptr(z))
+    return (y, z) if want_z else y
 
 
 def rmsnorm_rope_fp8(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str,
@@ -286,13 +291,19 @@ def ew_scale_add(x, b, alpha: float, x_dtype: str, y_dtype: str | None = None):
 
 
 def rmsnorm_rope_fp8_rounded(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int,
-                             dtype: str, cs_dtype: str, neox: bool, eps: float):
+                             dtype: str, cs_dtype: str, neox: bool, eps: float,
+                             want_intermediates: bool = False):
     """The staged form of the fused operator ("TileLang tutorial, ch. 13", s3.3.4:
     the normalised row is written back in x's dtype and rotated there): RMSNorm
     rounded once to ``dtype``, RoPE of those values rounded once to ``dtype``, then
     the per-token cast (s3.1.5) of the result.  That is the composition of the
-    three operators above; returns (codes [tokens, n], scales [tokens])."""
-    u = rmsnorm(x, w, dtype, eps)
-    z = rope(u, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox)
+    three operators above; returns (codes [tokens, n], scales [tokens]).  With
+    ``want_intermediates`` also returns a dict of the stored intermediates and
+    their unrounded values: u (bits), u_exact, z (bits), z_exact."""
+    n = heads * head_dim
+    u, u_exact = rmsnorm(x, w, dtype, eps, n=n, want_u=True)
+    z, z_exact = rope(u, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox, want_z=True)
     q, scales = act_quant_fp8(z, dtype, None)
+    if want_intermediates:
+        return q, scales[:, 0].copy(), {"u": u, "u_exact": u_exact, "z": z, "z_exact": z_exact}
     return q, scales[:, 0].copy()

@@ -202,9 +202,11 @@ static void copy_el(const void* src, int64_t si, void* dst, int64_t di, int dtyp
 /* RMSNorm  ([EW] s3.2.1 reference definition)                           */
 /*   rstd = 1/sqrt(mean_j x_j^2 + eps);  y_j = x_j * rstd * w_j          */
 /*   weight optional (absent = 1); one rounding, at the output.          */
+/* `u_out` (nullable, [rows, n] packed) receives x_j * rstd * w_j as      */
+/* double, before the rounding.                                           */
 /* ------------------------------------------------------------------ */
 void oracle_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t n,
-                    int64_t x_stride, int64_t y_stride, int dtype, float eps) {
+                    int64_t x_stride, int64_t y_stride, int dtype, float eps, double* u_out) {
   for (int64_t r = 0; r < rows; ++r) {
     double ss = 0.0;
     for (int64_t j = 0; j < n; ++j) {
@@ -215,7 +217,9 @@ void oracle_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t
     for (int64_t j = 0; j < n; ++j) {
       double v = load_el(x, r * x_stride + j, dtype);
       double wj = w ? load_el(w, j, dtype) : 1.0;
-      store_el(y, r * y_stride + j, dtype, v * rstd * wj);
+      double u = v * rstd * wj;
+      if (u_out) u_out[r * n + j] = u;
+      store_el(y, r * y_stride + j, dtype, u);
     }
   }
 }
@@ -256,6 +260,8 @@ void oracle_layernorm(const void* x, const void* gamma, const void* beta, void* 
 /*   position, one column per pair p.                                     */
 /*   interleaved: pair (2p, 2p+1);  NeoX half-split: pair (p, p + R/2).   */
 /*   y_a = x_a c - x_b s;  y_b = x_a s + x_b c   (a first, b second).     */
+/* `z_out` (nullable, [tokens, heads * head_dim] packed) receives every   */
+/* output as double before its rounding (a pass-through channel: x).      */
 /* ------------------------------------------------------------------ */
 static void rope_pair_index(int64_t p, int64_t half, int neox, int64_t* a, int64_t* b) {
   if (neox) {
@@ -269,14 +275,19 @@ static void rope_pair_index(int64_t p, int64_t half, int neox, int64_t* a, int64
 
 void oracle_rope(const void* x, const void* cosv, const void* sinv, void* y,
                  int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_dim,
-                 int64_t x_stride, int64_t y_stride, int dtype, int cs_dtype, int neox) {
+                 int64_t x_stride, int64_t y_stride, int dtype, int cs_dtype, int neox,
+                 double* z_out) {
   int64_t half = rope_dim / 2;
   int64_t start = head_dim - rope_dim;
   for (int64_t t = 0; t < tokens; ++t) {
     for (int64_t h = 0; h < heads; ++h) {
       int64_t xb = t * x_stride + h * head_dim;
       int64_t yb = t * y_stride + h * head_dim;
-      for (int64_t j = 0; j < start; ++j) copy_el(x, xb + j, y, yb + j, dtype);
+      int64_t zb = (t * heads + h) * head_dim;
+      for (int64_t j = 0; j < start; ++j) {
+        copy_el(x, xb + j, y, yb + j, dtype);
+        if (z_out) z_out[zb + j] = load_el(x, xb + j, dtype);
+      }
       for (int64_t p = 0; p < half; ++p) {
         int64_t a, b;
         rope_pair_index(p, half, neox, &a, &b);
@@ -284,8 +295,13 @@ void oracle_rope(const void* x, const void* cosv, const void* sinv, void* y,
         double s = load_el(sinv, t * half + p, cs_dtype);
         double xa = load_el(x, xb + start + a, dtype);
         double xb_ = load_el(x, xb + start + b, dtype);
-        store_el(y, yb + start + a, dtype, xa * c - xb_ * s);
-        store_el(y, yb + start + b, dtype, xa * s + xb_ * c);
+        double za = xa * c - xb_ * s, zb2 = xa * s + xb_ * c;
+        if (z_out) {
+          z_out[zb + start + a] = za;
+          z_out[zb + start + b] = zb2;
+        }
+        store_el(y, yb + start + a, dtype, za);
+        store_el(y, yb + start + b, dtype, zb2);
       }
     }
   }

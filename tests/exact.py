@@ -126,14 +126,19 @@ def sqrt(v: Decimal) -> Decimal:
 
 
 # ----------------------------------------------------------------- references
-def rmsnorm_ref(xrow, wrow, fmt, eps32):
-    """Exact RMSNorm of one row; returns output codes."""
+def rmsnorm_values(xrow, wrow, fmt, eps32):
+    """Exact RMSNorm of one row before its rounding (Decimal values)."""
     xs = [dec(b, fmt) for b in xrow]
     ws = [dec(b, fmt) for b in wrow] if wrow is not None else [Decimal(1)] * len(xs)
     n = len(xs)
     ms = sum(x * x for x in xs) / n
     r = 1 / sqrt(ms + Decimal(float(np.float32(eps32))))
-    return [round_to(x * r * w, fmt) for x, w in zip(xs, ws)]
+    return [x * r * w for x, w in zip(xs, ws)]
+
+
+def rmsnorm_ref(xrow, wrow, fmt, eps32):
+    """Exact RMSNorm of one row; returns output codes."""
+    return [round_to(v, fmt) for v in rmsnorm_values(xrow, wrow, fmt, eps32)]
 
 
 def layernorm_ref(xrow, grow, brow, fmt, eps32):

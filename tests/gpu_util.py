@@ -180,3 +180,148 @@ def assert_codes_away_from_ties(got, want, quotient, rel=2.0 ** -20, what=""):
                            f"boundary, e.g. at {np.argwhere(bad)[0]}")
     return {"exact_frac": float((d == 0).mean()), "near_tie_frac": float(near.mean()),
             "max_step": int(d.max()) if d.size else 0}
+
+
+# ------------------------------------------------------------ staged fused form
+def rn16_bits(v, dtype):
+    """float64 values -> 16-bit storage bits, rounded to nearest, ties to even.
+    binary16: numpy's direct float64 -> float16 conversion.  bfloat16: the value
+    is first rounded to odd at binary32 precision, then to bfloat16 with ties to
+    even, which together round once (24 >= 8 + 2 bits)."""
+    v = np.asarray(v, dtype=np.float64)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return v.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):
+        f = v.astype(np.float32)
+    b = f.view(np.uint32).copy()
+    inexact = (f.astype(np.float64) != v) & np.isfinite(v)
+    even = (b & 1) == 0
+    toward = np.where((f.astype(np.float64) < v) == (f >= 0), 1, -1).astype(np.int64)
+    b = np.where(inexact & even, (b.astype(np.int64) + toward).astype(np.uint32), b)
+    return ((b.astype(np.uint64) + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _e4m3_of_f32(q):
+    """binary32 values (clamped to +-448) -> E4M3FN codes, ties to even."""
+    q = np.clip(np.asarray(q, dtype=np.float32), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def _pair_layout(T, H, D, R, neox):
+    """Per output channel of [T, H*D]: is it rotated, its role (first or second
+    of its pair) and its pair index p; in the rotated span partner(j) is the
+    other member of j's pair."""
+    start = D - R
+    half = R // 2
+    k = np.arange(D)
+    rot = k >= start
+    local = np.where(rot, k - start, 0)
+    if neox:
+        first = local < half
+        p = np.where(first, local, local - half)
+        partner = np.where(first, local + half, local - half) + start
+    else:
+        first = local % 2 == 0
+        p = local // 2
+        partner = np.where(first, local + 1, local - 1) + start
+    partner = np.where(rot, partner, k)
+    return rot, first, p, partner
+
+
+# Bound on the relative error of the kernels' binary32 rstd, as a multiple of
+# 2^-24: a sum of n <= 8192 squares with at most 16 serial additions per lane
+# slot (two roundings per packed dot), a 3-level slot tree and a 6-level wave
+# reduction (<= 25 roundings of non-negative terms), the mean (one rounding
+# unless n is a power of two) and eps (one), then a correctly rounded sqrt
+# (half the argument's error plus one) and reciprocal (one):
+# 27/2 + 2 = 15.5 -> 16.  The normalised product x*w*rstd is rounded once
+# more to binary32 before its 16-bit rounding (one more).
+STAGED_U_REL = 17.0 * 2.0 ** -24
+# A rotated output is one binary32 fma of u_a*c and a binary32 product u_b*s
+# (exact for 16-bit tables): at most 2^-24 of the product's magnitude plus
+# 2^-24 of the result's, both within 2^-23 of |u_a c| + |u_b s|.
+STAGED_Z_REL = 2.0 ** -23
+
+
+def staged_intervals(x, w, c, s, H, D, R, dt, cs, neox, eps):
+    """For the staged fused form, the interval of each stored 16-bit value that a
+    binary32 evaluation within the bounds above can produce: returns the
+    oracle's codes and scales and dicts of float64 interval ends for the
+    normalised values u and the rotated values z ([T, H*D] each)."""
+    import oracle
+
+    T = x.shape[0]
+    q_o, sc_o, it = oracle.rmsnorm_rope_fp8_rounded(x, w, c, s, H, D, R, dt, cs, neox, eps,
+                                                    want_intermediates=True)
+    ue = it["u_exact"]
+    eta = np.abs(ue) * STAGED_U_REL
+    u_lo_bits, u_hi_bits = rn16_bits(ue - eta, dt), rn16_bits(ue + eta, dt)
+    u_lo = synth.storage_to_f64(u_lo_bits, dt)
+    u_hi = synth.storage_to_f64(u_hi_bits, dt)
+    assert np.all(u_lo <= u_hi)
+    # the exact rotation at the four corners of each pair's (u_a, u_b) box
+    rot, first, p, partner = _pair_layout(T, H, D, R, neox)
+    rot_n, first_n = np.tile(rot, H), np.tile(first, H)
+    corners = []
+    for a_hi in (False, True):
+        for b_hi in (False, True):
+            pick = np.where(first_n, a_hi, b_hi)[None, :] & rot_n[None, :]
+            ub = np.where(pick, u_hi_bits, u_lo_bits)
+            _, ze = oracle.rope(np.ascontiguousarray(ub), c, s, H, D, R, dt, cs, neox,
+                                want_z=True)
+            corners.append(ze)
+    corners = np.stack(corners)
+    # magnitude of the two products of each rotated output
+    cv = synth.storage_to_f64(c, cs)
+    sv = synth.storage_to_f64(s, cs)
+    pp = np.tile(p, H)
+    part = (np.arange(H)[:, None] * D + partner[None, :]).reshape(-1)
+    umax = np.maximum(np.abs(u_lo), np.abs(u_hi))
+    terms = umax * np.abs(cv[:, pp]) + umax[:, part] * np.abs(sv[:, pp])
+    dz = np.where(rot_n[None, :], terms * STAGED_Z_REL, 0.0)
+    z_lo = np.where(rot_n[None, :], corners.min(axis=0) - dz, u_lo)
+    z_hi = np.where(rot_n[None, :], corners.max(axis=0) + dz, u_hi)
+    z_lo = synth.storage_to_f64(rn16_bits(z_lo, dt), dt)
+    z_hi = synth.storage_to_f64(rn16_bits(z_hi, dt), dt)
+    return q_o, sc_o, {"u": (u_lo, u_hi), "z": (z_lo, z_hi)}
+
+
+def assert_staged_consistent(q, sc, x, w, c, s, H, D, R, dt, cs, neox, eps=1e-6, what=""):
+    """The staged form's bar.  Each stored intermediate may be either 16-bit
+    neighbour only where the oracle's unrounded value lies within the kernel's
+    binary32 error bound of a rounding boundary (staged_intervals); a row's
+    scale must follow from a possible row maximum, and each code must be the
+    E4M3 rounding of a possible stored value divided by the kernel's own scale.
+    Wherever the intervals hold one value, codes and scales are therefore
+    bit-exact.  Returns the oracle's codes and some statistics."""
+    q = np.asarray(q)
+    sc = np.asarray(sc, dtype=np.float32)
+    q_o, sc_o, iv = staged_intervals(x, w, c, s, H, D, R, dt, cs, neox, eps)
+    z_lo, z_hi = iv["z"]
+    amag_lo = np.where((z_lo <= 0) & (z_hi >= 0), 0.0, np.minimum(np.abs(z_lo), np.abs(z_hi)))
+    amag_hi = np.maximum(np.abs(z_lo), np.abs(z_hi))
+    floor = float(np.float32(1e-4))
+    a_lo = np.maximum(amag_lo.max(axis=1), floor)
+    a_hi = np.maximum(amag_hi.max(axis=1), floor)
+    s_lo = (a_lo / 448.0).astype(np.float32)
+    s_hi = (a_hi / 448.0).astype(np.float32)
+    bad = (sc < s_lo) | (sc > s_hi)
+    assert not bad.any(), (f"{what}: scale of row {int(np.argmax(bad))} outside what the "
+                           f"possible row maxima give: {sc[bad][0]!r} not in "
+                           f"[{s_lo[bad][0]!r}, {s_hi[bad][0]!r}]")
+    S = sc.astype(np.float64)[:, None]
+    c_lo = ord8(_e4m3_of_f32((z_lo / S).astype(np.float32)))
+    c_hi = ord8(_e4m3_of_f32((z_hi / S).astype(np.float32)))
+    got = ord8(q)
+    badc = (got < c_lo) | (got > c_hi)
+    assert not badc.any(), (f"{what}: {int(badc.sum())} codes outside the codes of their "
+                            f"possible stored values, e.g. at {np.argwhere(badc)[0]}")
+    d = np.abs(got - ord8(q_o))
+    amb = (z_lo != z_hi)
+    return {"exact_frac": float((d == 0).mean()) if d.size else 1.0,
+            "max_step": int(d.max()) if d.size else 0,
+            "ambiguous_frac": float(amb.mean()) if amb.size else 0.0,
+            "scale_rel": float(np.max(np.abs(sc.astype(np.float64) - sc_o) / sc_o))
+            if sc.size else 0.0}

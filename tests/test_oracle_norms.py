@@ -1,6 +1,8 @@
 """Pins of the oracle's RMSNorm and LayerNorm ("TileLang tutorial, ch. 13",
 s3.2.1 reference definitions; s5.4 on ragged rows) against exact brute force,
 closed forms, invariants and torch's float64 implementations."""
+from decimal import Decimal
+
 import numpy as np
 import pytest
 import torch
@@ -171,3 +173,18 @@ def test_single_element_rows():
     assert list(y[:, 0]) == [2.0, -2.0]
     z = _f64(oracle.layernorm(x, w, b, "bf16", 1e-5), "bf16")
     assert list(z[:, 0]) == [0.25, 0.25]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_rmsnorm_unrounded_output_is_the_exact_value(fmt):
+    # the optional float64 output carries x * rstd * w before the rounding: it
+    # agrees with the 400-digit value to binary64 precision, and it rounds to
+    # the stored output
+    x = synth.normal(41, (4, 24), 0.0, 2.0, fmt, outlier_frac=0.1, outlier_mul=10.0)
+    w = synth.normal(42, (24,), 1.0, 0.3, fmt)
+    y, u = oracle.rmsnorm(x, w, fmt, 1e-6, want_u=True)
+    for r in range(4):
+        ex = exact.rmsnorm_values(x[r], w, fmt, 1e-6)
+        for j, v in enumerate(ex):
+            assert abs(Decimal(float(u[r, j])) - v) <= abs(v) * Decimal(2) ** -50, (r, j)
+            assert exact.round_to(Decimal(float(u[r, j])), fmt) == int(y[r, j])

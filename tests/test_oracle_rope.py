@@ -1,5 +1,7 @@
 """Pins of the oracle's RoPE ("TileLang tutorial, ch. 13", s3.3.1 pairing
 conventions and partial rotation, s3.3.2 reference, s5.3 self-check)."""
+from decimal import Decimal
+
 import numpy as np
 import pytest
 
@@ -122,3 +124,21 @@ def test_rotation_preserves_pair_norm():
         cv, sv = c.astype(np.float64), s.astype(np.float64)
         unit = np.sqrt(cv ** 2 + sv ** 2)[:, None, :]
         assert np.all(np.abs(ny - nx * unit) <= 2.0 ** -10 * nx + 1e-7)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("fmt,cs", [("bf16", "bf16"), ("f16", "f32")])
+def test_unrounded_output_is_the_exact_rotation(fmt, cs, neox):
+    # the optional float64 output carries each rotated value before its
+    # rounding (pass-through channels: x itself)
+    T, H, D, R = 3, 2, 24, 16
+    x = synth.normal(51, (T, H * D), 0.0, 2.0, fmt)
+    c, s = synth.rope_table(T, R, cs, base=7.0)
+    y, z = oracle.rope(x, c, s, H, D, R, fmt, cs, neox, want_z=True)
+    for t in range(T):
+        xs = [exact.dec(b, fmt) for b in x[t]]
+        ex = exact.rope_values(xs, [exact.dec(b, cs) for b in c[t]],
+                               [exact.dec(b, cs) for b in s[t]], H, D, R, neox)
+        for j, v in enumerate(ex):
+            assert abs(Decimal(float(z[t, j])) - v) <= abs(v) * Decimal(2) ** -50, (t, j)
+            assert exact.round_to(Decimal(float(z[t, j])), fmt) == int(y[t, j])
