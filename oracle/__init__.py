@@ -70,9 +70,9 @@ def _load():
     L.oracle_rope.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
     L.oracle_rope.restype = None
     L.oracle_rmsnorm_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
-                                          i64, i64, i32, i32, i32, f32, vp]
+                                          i64, i64, i32, i32, i32, f32, vp, i32]
     L.oracle_rmsnorm_rope_fp8.restype = None
-    L.oracle_act_quant_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32]
+    L.oracle_act_quant_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, i32]
     L.oracle_act_quant_fp8.restype = None
     L.oracle_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                       i32, i32, i32, f32]
@@ -183,8 +183,10 @@ def rope(x, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str, cs_d
 
 def rmsnorm_rope_fp8(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int, dtype: str,
                      cs_dtype: str, neox: bool, eps: float, q_stride: int | None = None,
-                     want_z: bool = False, fill: int = 0):
-    """Fused RMSNorm -> RoPE -> per-token E4M3FN.  Returns (codes, scales[, z])."""
+                     want_z: bool = False, fill: int = 0, quotient64: bool = False):
+    """Fused RMSNorm -> RoPE -> per-token E4M3FN.  Returns (codes, scales[, z]).
+    ``quotient64`` (a diagnostic, not the parity reference) decides each code on
+    the double quotient z / scale instead of the binary32 one."""
     L = _load()
     x = _check(x, dtype, "x")
     w = _check(w, dtype, "w")
@@ -199,14 +201,16 @@ def rmsnorm_rope_fp8(x, w, cos, sin, heads: int, head_dim: int, rope_dim: int, d
     z = np.zeros((tokens, n), dtype=np.float64) if want_z else None
     L.oracle_rmsnorm_rope_fp8(_ptr(x), _ptr(w), _ptr(cos), _ptr(sin), _ptr(q), _ptr(scales),
                               tokens, heads, head_dim, rope_dim, xs, qs, DTYPE_CODE[dtype],
-                              DTYPE_CODE[cs_dtype], int(bool(neox)), eps, _ptr(z))
+                              DTYPE_CODE[cs_dtype], int(bool(neox)), eps, _ptr(z),
+                              int(bool(quotient64)))
     return (q, scales, z) if want_z else (q, scales)
 
 
 def act_quant_fp8(x, dtype: str, group: int | None = None, n: int | None = None,
-                  q_stride: int | None = None, fill: int = 0):
+                  q_stride: int | None = None, fill: int = 0, quotient64: bool = False):
     """E4M3FN codes and scales of x[:, :n] with one scale per ``group`` channels
-    (None: one per row).  Returns (codes [rows, q_stride], scales [rows, n/group])."""
+    (None: one per row).  Returns (codes [rows, q_stride], scales [rows, n/group]).
+    ``quotient64``: see rmsnorm_rope_fp8."""
     L = _load()
     x = _check(x, dtype, "x")
     rows, xs = x.shape
@@ -216,7 +220,8 @@ def act_quant_fp8(x, dtype: str, group: int | None = None, n: int | None = None,
     qs = n if q_stride is None else q_stride
     q = np.full((rows, qs), fill, dtype=np.uint8)
     scales = np.zeros((rows, n // g), dtype=np.float32)
-    L.oracle_act_quant_fp8(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, DTYPE_CODE[dtype])
+    L.oracle_act_quant_fp8(_ptr(x), _ptr(q), _ptr(scales), rows, n, g, xs, qs, DTYPE_CODE[dtype],
+                           int(bool(quotient64)))
     return q, scales
 
 

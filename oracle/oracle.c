@@ -13,19 +13,27 @@
  *
  * How it computes: every input value is decoded exactly to double; every
  * formula is evaluated in double in the order the definitions state; every
- * output is rounded ONCE, directly from double, to its storage format with
- * round-to-nearest-even, by the encoders below (written from the IEEE-754
- * binary16 layout, the bfloat16 layout (the top half of binary32) and the OCP
- * 8-bit floating point spec for E4M3FN).  There is no fusion, blocking or
- * reordering: one row at a time, one element at a time, single thread.
+ * 16-bit output and every scale is rounded ONCE, directly from double, to its
+ * storage format with round-to-nearest-even, by the encoders below (written
+ * from the IEEE-754 binary16 layout, the bfloat16 layout (the top half of
+ * binary32) and the OCP 8-bit floating point spec for E4M3FN).  The one
+ * exception is the FP8 codes, whose quotient is rounded to binary32 first
+ * (next point).  There is no fusion, blocking or reordering: one row at a
+ * time, one element at a time, single thread.
  *
  * Readings of points the pages leave open:
  *  - FP8 is OCP E4M3FN (bias 7, max finite 448 = 0x7E, S.1111.111 is NaN, no
  *    infinities); the quantisation divides by the scale and clamps to +-448
  *    before encoding, as the per-token cast in [EW] s3.1.5 does.  That cast
  *    divides in float32 fragments, so the code is decided on the binary32
- *    quotient: (float)(v / (double)scale) is the correctly rounded binary32
- *    quotient (a double quotient of two binary32 values rounds innocuously).
+ *    quotient.  Where the dividend is a stored 16-bit value (the per-token
+ *    and per-group cast, the v cache) (float)(v / (double)scale) is the
+ *    correctly rounded binary32 quotient (a double quotient of two binary32
+ *    values rounds innocuously).  Where it is the unrounded double z of the
+ *    fused operators, the same expression rounds z / scale twice, first to
+ *    53 bits, far below the binary32 decision it feeds.  A diagnostic switch
+ *    (quotient64) encodes the double quotient directly instead; it is not
+ *    used for parity.
  *  - The per-token scale is max(amax, floor)/448 with the floor 1e-4 taken as
  *    the binary32 constant the kernels hold; the scale is stored as binary32.
  *  - The fused operator does not round between the norm and the rotation.
@@ -198,6 +206,14 @@ static void copy_el(const void* src, int64_t si, void* dst, int64_t di, int dtyp
   memcpy((char*)dst + w * di, (const char*)src + w * si, w);
 }
 
+/* The value an FP8 code is decided on: the binary32 quotient of v by the */
+/* scale (the per-token cast divides in float32, [EW] s3.1.5), or with     */
+/* quotient64 (a diagnostic, not used for parity) the double quotient.     */
+static double fp8_quotient(double v, float scale, int quotient64) {
+  double q = v / (double)scale;
+  return quotient64 ? q : (double)(float)q;
+}
+
 /* ------------------------------------------------------------------ */
 /* RMSNorm  ([EW] s3.2.1 reference definition)                           */
 /*   rstd = 1/sqrt(mean_j x_j^2 + eps);  y_j = x_j * rstd * w_j          */
@@ -321,7 +337,7 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
                              uint8_t* q, float* scales, int64_t tokens, int64_t heads,
                              int64_t head_dim, int64_t rope_dim, int64_t x_stride,
                              int64_t q_stride, int dtype, int cs_dtype, int neox, float eps,
-                             double* z_out) {
+                             double* z_out, int quotient64) {
   int64_t n = heads * head_dim;
   int64_t half = rope_dim / 2;
   int64_t start = head_dim - rope_dim;
@@ -374,7 +390,7 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
       for (int64_t j = 0; j < start; ++j) {
         double wj = w ? load_el(w, h * head_dim + j, dtype) : 1.0;
         double z = load_el(x, xb + j, dtype) * rstd * wj;
-        double v = (double)(float)(z / (double)scale);
+        double v = fp8_quotient(z, scale, quotient64);
         if (v > fp8_max) v = fp8_max;
         if (v < -fp8_max) v = -fp8_max;
         q[qb + j] = oracle_encode_e4m3(v);
@@ -391,7 +407,7 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
         double zz[2] = {na * c - nb * s, na * s + nb * c};
         int64_t idx[2] = {a, b};
         for (int k = 0; k < 2; ++k) {
-          double v = (double)(float)(zz[k] / (double)scale);
+          double v = fp8_quotient(zz[k], scale, quotient64);
           if (v > fp8_max) v = fp8_max;
           if (v < -fp8_max) v = -fp8_max;
           q[qb + start + idx[k]] = oracle_encode_e4m3(v);
@@ -409,7 +425,8 @@ void oracle_rmsnorm_rope_fp8(const void* x, const void* w, const void* cosv, con
 /* [rows, n / group], packed.                                            */
 /* ------------------------------------------------------------------ */
 void oracle_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
-                          int64_t group, int64_t x_stride, int64_t q_stride, int dtype) {
+                          int64_t group, int64_t x_stride, int64_t q_stride, int dtype,
+                          int quotient64) {
   const double fp8_max = 448.0;
   const double floor_amax = (double)1e-4f;
   const int64_t groups = n / group;
@@ -423,7 +440,7 @@ void oracle_act_quant_fp8(const void* x, uint8_t* q, float* scales, int64_t rows
       float scale = (float)(fmax(amax, floor_amax) / fp8_max);
       scales[r * groups + k] = scale;
       for (int64_t j = k * group; j < (k + 1) * group; ++j) {
-        double v = (double)(float)(load_el(x, r * x_stride + j, dtype) / (double)scale);
+        double v = fp8_quotient(load_el(x, r * x_stride + j, dtype), scale, quotient64);
         if (v > fp8_max) v = fp8_max;
         if (v < -fp8_max) v = -fp8_max;
         q[r * q_stride + j] = oracle_encode_e4m3(v);
@@ -498,7 +515,7 @@ static void quant_head_e4m3(const double* z, int64_t n, uint8_t* codes, float* s
   float scale = (float)(fmax(amax, (double)1e-4f) / fp8_max);
   *scale_out = scale;
   for (int64_t j = 0; j < n; ++j) {
-    double v = (double)(float)(z[j] / (double)scale);
+    double v = fp8_quotient(z[j], scale, 0);
     if (v > fp8_max) v = fp8_max;
     if (v < -fp8_max) v = -fp8_max;
     codes[j] = oracle_encode_e4m3(v);
