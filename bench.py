@@ -39,6 +39,7 @@ Options: --workload runs any of the named workloads instead, --rows runs it at
 another row (token) count, --plain-copy MIB adds `plain_copy`, a bare copy of
 that size through the library's elementwise kernel, --timeline L adds
 per-wave timestamps of the fused kernel over L consecutive launches, and
+--host-cost adds the C ABI's host time per call measured from plain C, and
 --trace-summary CSV prints p10/p50/p90 kernel durations of a rocprofv3
 kernel-trace file.
 
@@ -53,6 +54,7 @@ import hashlib
 import json
 import os
 import platform
+import subprocess
 import sys
 import time
 
@@ -525,6 +527,55 @@ def timeline(wl, launches: int):
     return out
 
 
+def host_cost(wl) -> dict:
+    """Host time per call of the fused operator's launch path.  From plain C
+    (csrc/probe/host_cost.c, a child process with its own buffers): argument
+    validation alone (invalid and empty calls, nanoseconds), and valid
+    asynchronous calls at the benchmark shape beside bare launches of the same
+    grid (microseconds).  From Python, on the workload's buffers: the raw
+    ctypes call bench.py times in eager mode, and the torch binding with
+    preallocated outputs (microseconds)."""
+    import time as _time
+
+    import torch
+
+    import quant_row_workgroup_amd as qrw
+    from quant_row_workgroup_amd import build
+
+    out = {}
+    for mode, n in (("validate", "1000000"), ("launch", "200")):
+        r = subprocess.run([build.HOST_COST, mode, n], capture_output=True, text=True,
+                           timeout=300)
+        if r.returncode != 0:
+            raise RuntimeError(f"host_cost {mode}: {r.stderr.strip()}")
+        out.update({f"c_{k}": float(v)
+                    for k, v in (ln.split() for ln in r.stdout.strip().splitlines())})
+    n = 200
+    cur = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    t0 = _time.perf_counter()
+    for i in range(n):
+        wl.launch(i, cur)
+    t1 = _time.perf_counter()
+    torch.cuda.synchronize()
+    s = wl.sets[0]
+    c = wl.cfg
+    args = (s["x"], s["w"], s["cos"], s["sin"], c["heads"], c["head_dim"], c["rope_dim"],
+            c["neox"], c["eps"], s["q"], s["scales"])
+    qrw.rmsnorm_rope_fp8_fwd(*args)
+    torch.cuda.synchronize()
+    t2 = _time.perf_counter()
+    for _ in range(n):
+        qrw.rmsnorm_rope_fp8_fwd(*args)
+    t3 = _time.perf_counter()
+    torch.cuda.synchronize()
+    wl.reset()
+    out["python_ctypes_launch_us_per_call"] = round((t1 - t0) / n * 1e6, 3)
+    out["python_binding_us_per_call"] = round((t3 - t2) / n * 1e6, 3)
+    print(f"[bench] host cost: {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
+
+
 def trace_summary(path: str) -> str:
     """Per-kernel duration statistics (count, mean, p10, p50, p90, min, max, in
     microseconds) of a rocprofv3 --kernel-trace CSV."""
@@ -686,6 +737,9 @@ def main() -> int:
     ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
                     help="fused 4096-wide workloads: per-wave timestamps over LAUNCHES "
                          "consecutive launches, reported as timeline")
+    ap.add_argument("--host-cost", action="store_true",
+                    help="also time the C ABI's host path from plain C (validation alone; valid "
+                         "calls of the fused operator and bare launches), reported as host_cost")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-kernel duration statistics of a rocprofv3 kernel-trace CSV "
                          "and exit (no GPU work)")
@@ -728,6 +782,7 @@ def main() -> int:
         ceiling["kernel_over_ceiling"] = round(ms * 1e3 / ceiling["us_per_launch"], 4)
     tl = timeline(wl, args.timeline) if args.timeline and fused_probe_shape(wl.cfg) else None
     plain = plain_copy(args.plain_copy, args.sets) if args.plain_copy else None
+    hcost = host_cost(wl) if args.host_cost and wl.cfg["op"] == "fused" else None
 
     if args.calibrate_copy:
         nb = args.calibrate_copy << 20
@@ -789,6 +844,8 @@ def main() -> int:
         line["timeline"] = tl
     if plain is not None:
         line["plain_copy"] = plain
+    if hcost is not None:
+        line["host_cost"] = hcost
     print(json.dumps(line), flush=True)
     return 0
 

@@ -99,7 +99,27 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         raise subprocess.CalledProcessError(1, "hipcc")
     _link(objs, LIB, verbose)
     _link(pobjs, PROBE_LIB, verbose)
+    build_host_cost(verbose)
     return LIB
+
+
+HOST_COST = os.path.join(PKG, "qrw_host_cost")
+
+
+def build_host_cost(verbose: bool = False) -> str:
+    """The C host-cost harness (csrc/probe/host_cost.c), linked against both
+    libraries and the system HIP runtime."""
+    rocm_lib = "/opt/rocm/lib"
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", "/opt/rocm/include",
+           os.path.join(CSRC, "probe", "host_cost.c"), "-o", HOST_COST + ".tmp",
+           "-L", PKG, "-lqrw", "-lqrw_probe", "-L", rocm_lib, "-lamdhip64",
+           f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{rocm_lib}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(HOST_COST + ".tmp", HOST_COST)
+    return HOST_COST
 
 
 if __name__ == "__main__":
