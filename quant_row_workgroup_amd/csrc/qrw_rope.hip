@@ -260,16 +260,20 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
 
 // ------------------------------------------------------------------ fused, contiguous
 // One wave per token, kContigRows<MID> tokens per workgroup; the token body
-// and its layout are in qrw_fused_contig.h.
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID>
+// and its layout are in qrw_fused_contig.h.  PACKED: the codes' row stride is
+// x's (one stride for both; a packed call, as in the benchmark), which
+// measured 0.25 us faster than two separate strides on 4096 x 4096 bf16
+// (10.37 against 10.62 us, same-box A/B).
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID,
+          bool PACKED = false>
 __global__ __launch_bounds__(kWave * kContigRows<MID>) void rmsnorm_rope_fp8_contig_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kContigRows<MID> + (threadIdx.x >> 6);
   if (t >= tokens) return;
-  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs, qs,
-                                                       eps, lane, nullptr);
+  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs,
+                                                       PACKED ? xs : qs, eps, lane, nullptr);
 }
 
 // ------------------------------------------------------------------ fused, dense
@@ -498,7 +502,10 @@ void contig_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, 
   }
   constexpr int R = kContigRows<false>;
   const dim3 cg((unsigned)((tokens + R - 1) / R));
-  if (w)
+  if (w && qs == xs)
+    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false, true>
+        <<<cg, kWave * R, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, eps);
+  else if (w)
     rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false><<<cg, kWave * R, 0, st>>>(
         x, w, c, s, q, sc, tokens, xs, qs, eps);
   else
