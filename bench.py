@@ -7,11 +7,13 @@ E4M3FN codes + binary32 per-token scales out).
 One step = one launch of the operator over one 4096 x 4096 batch.  The batch
 rotates over --sets independent input/output buffer sets (default 8 x 51.4 MB,
 more than the 256 MB last-level cache), so every launch reads inputs that sit
-in HBM rather than in cache.  The K timed steps are captured once into a HIP
-graph; untimed replays run for about 50 ms first (the GPU settles at its
-steady clocks), and the timed replay is enqueued behind the last of them,
-bracketed by HIP events on the launch stream, so the host-side graph launch
-is not in the timed region, which holds exactly K launches.  The events give the average launch duration, and
+in HBM rather than in cache.  The K steps are captured once into a HIP graph,
+whose untimed replays run for about 50 ms first (the GPU settles at its
+steady clocks); behind them, still queued, the host enqueues a HIP event, the
+K launches and a second event on the same stream, and checks that the first
+event had not yet fired when it finished, so the timed region holds exactly
+K launches back to back, with neither host time nor a graph boundary in it
+(see timed_launches).  The events give the average launch duration, and
 
     achieved GB/s = counted bytes per launch / average launch duration
 
@@ -71,8 +73,9 @@ KERNEL_SOURCES = {
     "rmsnorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "layernorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
-    "fused": ("qrw_rope.hip", "qrw_fused_contig.h", "qrw_fused_tail.hip", "qrw_plan.h",
-              "qrw_device.h", "qrw_launch.h"),
+    "fused": ("qrw_rope.hip", "qrw_fused_contig.h", "qrw_fused_contig_bf16.hip",
+              "qrw_fused_contig_f16.hip", "qrw_fused_tail.hip", "qrw_plan.h", "qrw_device.h",
+              "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
                      "qrw_qknorm_gc_b.hip", "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),
@@ -270,54 +273,30 @@ class Workload:
 
 
 def time_gpu(wl: Workload, steps: int, warmup: int, mode: str):
+    """Milliseconds per step of the workload (see timed_launches); first checks
+    that a graph replay of the steps gives the same outputs as the same launches
+    made eagerly, bit for bit (from the same starting inputs, since an in-place
+    operator consumes them), since the backlog is made of graph replays."""
     import torch
 
     cur = torch.cuda.current_stream()
     for i in range(warmup):
         wl.launch(i, cur.cuda_stream)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    if mode == "graph":
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(cur)
-        with torch.cuda.graph(g, stream=cap):
-            sp = torch.cuda.current_stream().cuda_stream
-            for i in range(steps):
-                wl.launch(i, sp)
-        torch.cuda.synchronize()
-        # the graph's outputs match the same launches made eagerly, bit for bit
-        # (from the same starting inputs, since an in-place operator consumes them)
-        wl.reset()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        ref = wl.outputs(steps - 1)
-        wl.reset()
-        for i in range(steps):
-            wl.launch(i, cur.cuda_stream)
-        torch.cuda.synchronize()
-        for a, b in zip(ref, wl.outputs(steps - 1)):
-            if not torch.equal(a, b):
-                raise RuntimeError("graph replay differs from eager launches")
-        torch.cuda.synchronize()
-        settle(g)
-        # The last untimed replay is still running when the host submits the
-        # timed one, so the start event fires when the GPU finishes it and the
-        # timed region holds exactly `steps` launches back to back, with no
-        # host-side graph launch inside it.
-        start.record()
-        g.replay()
-        end.record()
-    else:
-        start.record()
-        for i in range(steps):
-            wl.launch(i, cur.cuda_stream)
-        end.record()
-    end.synchronize()
+    g = capture(wl.launch, steps)
+    wl.reset()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per step
+    g.replay()
+    torch.cuda.synchronize()
+    ref = wl.outputs(steps - 1)
+    wl.reset()
+    for i in range(steps):
+        wl.launch(i, cur.cuda_stream)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, wl.outputs(steps - 1)):
+        if not torch.equal(a, b):
+            raise RuntimeError("graph replay differs from eager launches")
+    return timed_launches(wl.launch, steps, 0, mode, graph=g)
 
 
 # ---------------------------------------------------------------- CPU side
@@ -335,11 +314,11 @@ def compute_dtype(cfg: dict) -> str:
 SETTLE_MS = 50.0
 
 
-def settle(g) -> None:
-    """Replay graph ``g`` untimed for about SETTLE_MS of GPU time, ending with
-    one replay left running: the GPU reaches its steady clocks before a timed
-    region (a short run otherwise times part of the ramp), and the host can
-    enqueue the timed replay behind it."""
+def settle(g, ms: float = None) -> None:
+    """Replay graph ``g`` untimed for about ``ms`` (default SETTLE_MS) of GPU
+    time and return while those replays are still queued: the GPU reaches its
+    steady clocks before a timed region (a short run otherwise times part of
+    the ramp), and the host can enqueue the timed work behind them."""
     import torch
 
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -348,20 +327,15 @@ def settle(g) -> None:
     b.record()
     b.synchronize()
     per = max(a.elapsed_time(b), 1e-3)
-    for _ in range(max(1, min(2000, int(SETTLE_MS / per) + 1))):
+    for _ in range(max(1, min(4000, int((ms or SETTLE_MS) / per) + 1))):
         g.replay()
 
 
-def graph_time(launch, steps: int, warmup: int = 3) -> float:
-    """Milliseconds per launch of ``launch(i, stream_ptr)`` (i = 0 .. steps-1),
-    captured once in a HIP graph: one untimed replay is enqueued, then the timed
-    replay between HIP events on the same stream, so the host-side graph launch
-    stays outside the timed region."""
+def capture(launch, steps: int):
+    """A HIP graph of ``launch(i, stream_ptr)`` for i = 0 .. steps-1."""
     import torch
 
     cur = torch.cuda.current_stream()
-    for i in range(warmup):
-        launch(i, cur.cuda_stream)
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(cur)
@@ -370,20 +344,76 @@ def graph_time(launch, steps: int, warmup: int = 3) -> float:
         for i in range(steps):
             launch(i, sp)
     torch.cuda.synchronize()
+    return g
+
+
+# How the last timed region was measured (reported in the JSON line).
+TIMING = {}
+
+
+def timed_launches(launch, steps: int, warmup: int = 3, mode: str = "stream", graph=None):
+    """Milliseconds per launch of ``launch(i, stream_ptr)``, i = 0 .. steps-1,
+    between two HIP events on the launch stream.
+
+    mode "stream" (the default): the graph of the same launches is replayed
+    untimed for about SETTLE_MS of GPU time, then the start event and the
+    `steps` launches are enqueued directly on the stream behind that backlog,
+    then the end event.  If the start event is still pending once the host has
+    enqueued everything, every timed launch was queued before the first one
+    ran, so the region holds the launches back to back with no host time in
+    it.  Otherwise (a kernel shorter than the host's launch cost outran a
+    too-short backlog) the backlog is doubled, twice at most, and then the
+    graph mode is used.
+
+    mode "graph": the same backlog, then the launches as one graph replay.  A
+    replay carries a fixed cost of its own on the GPU (about 4 us on MI355X),
+    part of the region.
+
+    mode "eager": the launches enqueued from an idle GPU (the host's launch
+    cost is part of the region whenever it exceeds the kernel's)."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i, cur.cuda_stream)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if mode == "eager":
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            launch(i, cur.cuda_stream)
+        end.record()
+        end.synchronize()
+        TIMING.update(mode="eager", ahead=None)
+        return start.elapsed_time(end) / steps
+    g = graph if graph is not None else capture(launch, steps)
+    if mode == "stream":
+        for attempt in range(3):
+            settle(g, SETTLE_MS * 2 ** attempt)
+            start.record()
+            for i in range(steps):
+                launch(i, cur.cuda_stream)
+            end.record()
+            ahead = not start.query()
+            end.synchronize()
+            torch.cuda.synchronize()
+            if ahead:
+                TIMING.update(mode="stream", ahead=True, backlog_ms=SETTLE_MS * 2 ** attempt)
+                return start.elapsed_time(end) / steps
     settle(g)
     start.record()
     g.replay()
     end.record()
     end.synchronize()
     torch.cuda.synchronize()
+    TIMING.update(mode="graph", ahead=None if mode == "graph" else False)
     return start.elapsed_time(end) / steps
 
 
 def plain_copy(mib: int, sets: int, steps: int = 50):
     """A plain device copy of ``mib`` MiB (f32, y = x * 1) through the library's
-    elementwise kernel, over ``sets`` rotating buffer pairs and graph-replayed:
-    what a bare 16-byte-per-lane copy of that size reaches on this GPU."""
+    elementwise kernel, over ``sets`` rotating buffer pairs and timed like the
+    workload: what a bare 16-byte-per-lane copy of that size reaches here."""
     import torch
 
     import quant_row_workgroup_amd as qrw
@@ -400,7 +430,7 @@ def plain_copy(mib: int, sets: int, steps: int = 50):
         if rc != 0:
             raise RuntimeError(f"ew_scale_cast_fwd failed: {rc}")
 
-    ms = graph_time(go, steps)
+    ms = timed_launches(go, steps)
     torch.cuda.synchronize()
     if not torch.equal(ys[(steps - 1) % sets], xs[(steps - 1) % sets]):
         raise RuntimeError("copy through the elementwise kernel is not exact")
@@ -453,11 +483,12 @@ def same_traffic_ceiling(wl, steps: int):
 
     out = {}
     for key, fn in (("row_dependency", copy(1)), ("no_dependency", copy(0))):
-        ms = graph_time(fn, steps)
+        ms = timed_launches(fn, steps)
         gbs = wl.counted / (ms * 1e-3) / 1e9
         out[key] = {"us_per_launch": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
-                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    ms = graph_time(nothing, steps)
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "timing": TIMING["mode"]}
+    ms = timed_launches(nothing, steps)
+    empty_timing = TIMING["mode"]
     torch.cuda.synchronize()
     if not torch.equal(empty.view(-1, 4)[:, 0].cpu(), torch.arange(blocks, dtype=torch.int32)):
         raise RuntimeError("empty-grid probe wrote the wrong words")
@@ -472,8 +503,10 @@ def same_traffic_ceiling(wl, steps: int):
         "us_per_launch": out["row_dependency"]["us_per_launch"],
         "GB/s": out["row_dependency"]["GB/s"],
         "frac": out["row_dependency"]["frac"],
+        "timing": out["row_dependency"]["timing"],
         "no_row_dependency": out["no_dependency"],
         "empty_grid_us_per_launch": round(ms * 1e3, 3),
+        "empty_grid_timing": empty_timing,
     }
 
 
@@ -481,8 +514,8 @@ def timeline(wl, launches: int):
     """Per-wave timestamps of the fused kernel (qrw_probe_fused_timeline: the
     library's contiguous kernel with the constant 100 MHz clock read at entry,
     once the row's sum of squares is known, after the last store is issued and
-    once the stores are done) over ``launches`` consecutive graph-replayed
-    launches on rotating buffer sets.  Times are microseconds from each
+    once the stores are done) over ``launches`` consecutive launches on
+    rotating buffer sets, timed like the workload.  Times are microseconds from each
     launch's first wave; ``gap_to_next`` runs from a launch's last completed
     store to the next launch's first wave."""
     import numpy as np
@@ -503,7 +536,7 @@ def timeline(wl, launches: int):
         if rc != 0:
             raise RuntimeError(f"qrw_probe_fused_timeline: status {rc}")
 
-    ms = graph_time(go, launches)
+    ms = timed_launches(go, launches)
     st = stamps.cpu().numpy().astype(np.float64) * 0.01  # 100 MHz ticks -> us
     names = ("entry", "row_arrived", "stores_issued", "stores_done")
     per = {k: [] for k in names}
@@ -516,7 +549,7 @@ def timeline(wl, launches: int):
         if k + 1 < launches:
             gaps.append(st[k + 1, :, 0].min() - st[k, :, 3].max())
     q = lambda a, p: round(float(np.percentile(np.concatenate(a), p)), 3)
-    out = {"launches": launches, "us_per_launch": round(ms * 1e3, 3),
+    out = {"launches": launches, "us_per_launch": round(ms * 1e3, 3), "timing": TIMING["mode"],
            "first_wave_to_last_store_done_us": round(float(np.median(spans)), 3),
            "gap_to_next_us": round(float(np.median(gaps)), 3) if gaps else None}
     for nm in names:
@@ -720,7 +753,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--sets", type=int, default=8)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--mode", choices=["stream", "graph", "eager"], default="stream",
+                    help="how the timed launches are enqueued (see timed_launches)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rows", type=int, default=0,
                     help="run the workload with this many rows (tokens, or elements for the "
@@ -773,6 +807,7 @@ def main() -> int:
     print(f"[bench] {args.workload}: {args.sets} sets, warmup {args.warmup}, steps {args.steps}, "
           f"mode {args.mode}", file=sys.stderr, flush=True)
     ms = time_gpu(wl, args.steps, args.warmup, args.mode)
+    timing = dict(TIMING)
     gbs = wl.counted / (ms * 1e-3) / 1e9
     print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
@@ -810,7 +845,9 @@ def main() -> int:
     else:
         cfg = {"workload": args.workload}
     cfg.update({"input_sets": args.sets, "counted_bytes_per_step": wl.counted,
-                "timing": f"{args.mode}, HIP events on the launch stream"})
+                "timing": (f"{timing['mode']}: HIP events on the launch stream"
+                           + (", launches queued behind a backlog before the first ran"
+                              if timing.get("ahead") else ""))})
 
     line = {
         "metric": METRIC if args.workload == DEFAULT_WORKLOAD else f"achieved HBM GB/s, {args.workload}",

@@ -79,11 +79,11 @@ __global__ __launch_bounds__(kProbeBlock) void empty_kernel(uint32_t* out) {
 }
 
 template <bool NEOX>
-__global__ __launch_bounds__(kWave * kContigRows<false>) void fused_timeline_kernel(
+__global__ __launch_bounds__(kWave * kContigRows) void fused_timeline_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, float eps, uint64_t* stamps) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kContigRows<false> + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kContigRows + (threadIdx.x >> 6);
   if (t >= tokens) return;
   contig_token<BF16, BF16, NEOX, 8, true, 8, false, true>(x, w, cosv, sinv, q, scales, t, 4096,
                                                           4096, eps, lane, stamps);
@@ -189,7 +189,7 @@ extern "C" int qrw_probe_fused_timeline(const void* x, const void* w, const void
   if (!x || !w || !cos || !sin || !q || !scales || !stamps) return QRW_ERR_NULL;
   if (!al16(x) || !al16(w) || !al16(cos) || !al16(sin) || !al16(q)) return QRW_ERR_ALIGN;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return QRW_ERR_VALUE;
-  constexpr int R = kContigRows<false>;
+  constexpr int R = kContigRows;
   const dim3 grid((unsigned)((tokens + R - 1) / R));
   fused_timeline_kernel<true><<<grid, kWave * R, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), cos, sin, q, scales,

@@ -28,12 +28,11 @@
 
 namespace qrw {
 
-// Rows (waves) per workgroup: 4 for the exact form; 16 for the staged form,
-// whose longer arithmetic measured faster with 1024-thread workgroups on
-// 4096 x 4096 bf16 (12.7 against 13.4 us; the exact form: 11.0 at 4, 11.1-11.3
-// at 8, 11.5-12.1 at 16).
-template <bool MID>
-constexpr int kContigRows = MID ? 16 : 4;
+// Rows (waves) per workgroup: 4.  Measured on 4096 x 4096 bf16 (same-box
+// A/B): the exact form 11.0 us at 4 rows against 11.1-11.3 at 8 and 11.5-12.1
+// at 16; the staged form 11.03 at 4 against 11.03-11.08 at 8 and 11.42 at 16
+// (with the one-stride instance and non-temporal code stores).
+constexpr int kContigRows = 4;
 
 // Timeline slots per wave (TL = true).
 constexpr int kTimelineSlots = 4;
@@ -157,6 +156,96 @@ __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* 
       p[3] = t3;
     }
   }
+}
+
+// ------------------------------------------------------------------ kernel
+// One wave per token, kContigRows tokens per workgroup.  PACKED: the codes'
+// row stride is x's (one stride for both: a packed call, the benchmark's
+// included), which measured faster than two separate strides on 4096 x 4096
+// bf16 (same-box A/B: the exact form 10.37 against 10.62 us, the staged form
+// 11.03 against 11.6 us), since the scheduler then issues the row's loads in a
+// better order.
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID, bool PACKED>
+__global__ __launch_bounds__(kWave * kContigRows) void rmsnorm_rope_fp8_contig_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
+    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * kContigRows + (threadIdx.x >> 6);
+  if (t >= tokens) return;
+  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs,
+                                                       PACKED ? xs : qs, eps, lane, nullptr);
+}
+
+template <typename T, typename CS, bool NEOX, int G, int XD>
+hipError_t contig_launch(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                         uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs, float eps,
+                         bool mid, hipStream_t st) {
+  const dim3 grid((unsigned)((tokens + kContigRows - 1) / kContigRows));
+  const dim3 block(kWave * kContigRows);
+  // the packed instances are the weighted ones (the usual call); the rest take
+  // two strides
+  if (mid) {
+    if (w && qs == xs)
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, true, true><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+    else if (w)
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, true, false><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+    else
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, true, false><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+  } else {
+    if (w && qs == xs)
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false, true><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+    else if (w)
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false, false><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+    else
+      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, false, false><<<grid, block, 0, st>>>(
+          x, w, c, s, q, sc, tokens, xs, qs, eps);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, typename CS, bool NEOX, int G>
+hipError_t contig_launch_xd(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                            uint8_t* q, float* sc, int64_t tokens, int64_t head_dim, int64_t xs,
+                            int64_t qs, float eps, bool mid, hipStream_t st) {
+  switch (head_dim / 16) {
+    case 1: return contig_launch<T, CS, NEOX, G, 1>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+    case 2: return contig_launch<T, CS, NEOX, G, 2>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+    case 4: return contig_launch<T, CS, NEOX, G, 4>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+    case 8: return contig_launch<T, CS, NEOX, G, 8>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+    default: return contig_launch<T, CS, NEOX, G, 16>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+  }
+}
+
+template <typename T, typename CS, bool NEOX>
+hipError_t contig_launch_g(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                           uint8_t* q, float* sc, int64_t tokens, int64_t head_dim, int g,
+                           int64_t xs, int64_t qs, float eps, bool mid, hipStream_t st) {
+  switch (g) {
+    case 1: return contig_launch_xd<T, CS, NEOX, 1>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 2: return contig_launch_xd<T, CS, NEOX, 2>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 4: return contig_launch_xd<T, CS, NEOX, 4>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    default: return contig_launch_xd<T, CS, NEOX, 8>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+  }
+}
+
+// Launch for x dtype T: cs_dtype 3 = binary32 tables, else T; neox selects
+// the pairing.
+template <typename T>
+hipError_t contig_launch_dtype(const uint16_t* x, const uint16_t* w, const void* c,
+                               const void* s, uint8_t* q, float* sc, int64_t tokens,
+                               int64_t head_dim, int g, int64_t xs, int64_t qs, int cs_dtype,
+                               bool neox, float eps, bool mid, hipStream_t st) {
+  if (cs_dtype == 3) {
+    if (neox) return contig_launch_g<T, float, true>(x, w, c, s, q, sc, tokens, head_dim, g, xs, qs, eps, mid, st);
+    return contig_launch_g<T, float, false>(x, w, c, s, q, sc, tokens, head_dim, g, xs, qs, eps, mid, st);
+  }
+  if (neox) return contig_launch_g<T, T, true>(x, w, c, s, q, sc, tokens, head_dim, g, xs, qs, eps, mid, st);
+  return contig_launch_g<T, T, false>(x, w, c, s, q, sc, tokens, head_dim, g, xs, qs, eps, mid, st);
 }
 
 }  // namespace qrw

@@ -35,6 +35,23 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
                                    float eps, bool round_mid, hipStream_t stream);
 
+// The fused operator in the contiguous layout when every head rotates whole
+// (qrw_fused_contig_{f16,bf16}.hip): rope_dim == head_dim, head_dim / 16 in
+// {1, 2, 4, 8, 16}, rows of g = 1, 2, 4 or 8 blocks of 512 channels.  One
+// source per x dtype, so that the library's sources compile in parallel.
+hipError_t launch_rmsnorm_rope_fp8_contig_f16(const uint16_t* x, const uint16_t* w,
+                                              const void* cos, const void* sin, uint8_t* q,
+                                              float* scales, int64_t tokens, int64_t head_dim,
+                                              int g, int64_t xs, int64_t qs, int cs_dtype,
+                                              bool neox, float eps, bool round_mid,
+                                              hipStream_t stream);
+hipError_t launch_rmsnorm_rope_fp8_contig_bf16(const uint16_t* x, const uint16_t* w,
+                                               const void* cos, const void* sin, uint8_t* q,
+                                               float* scales, int64_t tokens, int64_t head_dim,
+                                               int g, int64_t xs, int64_t qs, int cs_dtype,
+                                               bool neox, float eps, bool round_mid,
+                                               hipStream_t stream);
+
 // The fused operator when heads rotate only their tail span, in the
 // contiguous layout (qrw_fused_tail.hip): applies when rope_dim < head_dim,
 // both powers of two, 16 <= rope_dim <= 256, and the row is 1, 2, 4 or 8

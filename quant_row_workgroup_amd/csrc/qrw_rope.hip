@@ -30,7 +30,6 @@
 #include <type_traits>
 
 #include "qrw_device.h"
-#include "qrw_fused_contig.h"
 #include "qrw_launch.h"
 #include "qrw_plan.h"
 
@@ -258,24 +257,6 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
 }
 
 
-// ------------------------------------------------------------------ fused, contiguous
-// One wave per token, kContigRows<MID> tokens per workgroup; the token body
-// and its layout are in qrw_fused_contig.h.  PACKED: the codes' row stride is
-// x's (one stride for both; a packed call, as in the benchmark), which
-// measured 0.25 us faster than two separate strides on 4096 x 4096 bf16
-// (10.37 against 10.62 us, same-box A/B).
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID,
-          bool PACKED = false>
-__global__ __launch_bounds__(kWave * kContigRows<MID>) void rmsnorm_rope_fp8_contig_kernel(
-    const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
-    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, float eps) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kContigRows<MID> + (threadIdx.x >> 6);
-  if (t >= tokens) return;
-  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs,
-                                                       PACKED ? xs : qs, eps, lane, nullptr);
-}
-
 // ------------------------------------------------------------------ fused, dense
 // The same operator when every lane owns exactly K rope items and a single
 // table granule: no pass-through channels, rope_dim/16 a power of two that
@@ -484,48 +465,6 @@ bool dense_ok(const RowPlan& pl, int kk) {
   return pl.n_plain == 0 && pl.lane_hoist && pow2 && pl.n_rope == kWave * kk;
 }
 
-template <typename T, typename CS, bool NEOX, int G, int XD>
-void contig_go(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
-               const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-               const RowPlan& pl, float n_f, float eps, bool mid) {
-  (void)grid;  // the contiguous kernel sizes its own grid (kContigRows)
-  if (mid) {
-    constexpr int R = kContigRows<true>;
-    const dim3 cg((unsigned)((tokens + R - 1) / R));
-    if (w)
-      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, true><<<cg, kWave * R, 0, st>>>(
-          x, w, c, s, q, sc, tokens, xs, qs, eps);
-    else
-      rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, true><<<cg, kWave * R, 0, st>>>(
-          x, w, c, s, q, sc, tokens, xs, qs, eps);
-    return;
-  }
-  constexpr int R = kContigRows<false>;
-  const dim3 cg((unsigned)((tokens + R - 1) / R));
-  if (w && qs == xs)
-    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false, true>
-        <<<cg, kWave * R, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, eps);
-  else if (w)
-    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, true, XD, false><<<cg, kWave * R, 0, st>>>(
-        x, w, c, s, q, sc, tokens, xs, qs, eps);
-  else
-    rmsnorm_rope_fp8_contig_kernel<T, CS, NEOX, G, false, XD, false><<<cg, kWave * R, 0, st>>>(
-        x, w, c, s, q, sc, tokens, xs, qs, eps);
-}
-
-template <typename T, typename CS, bool NEOX, int G>
-void contig_go_xd(dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w, const void* c,
-                  const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-                  const RowPlan& pl, float n_f, float eps, bool mid) {
-  switch (pl.head_dim / 16) {
-    case 1: contig_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
-    case 2: contig_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
-    case 4: contig_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
-    case 8: contig_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
-    default: contig_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); break;
-  }
-}
-
 // Granules per lane of the contiguous path, or 0 if it does not apply: whole
 // heads rotate, head_dim / 16 is 1, 2, 4, 8 or 16, and the row is 1, 2, 4 or
 // 8 blocks of 512 channels.
@@ -541,13 +480,6 @@ template <typename T, typename CS, bool NEOX>
 void fused_go(int kk, dim3 grid, hipStream_t st, const uint16_t* x, const uint16_t* w,
               const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
               int64_t qs, const RowPlan& pl, float n_f, float eps, bool mid) {
-  switch (contig_blocks(pl)) {
-    case 1: contig_go_xd<T, CS, NEOX, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
-    case 2: contig_go_xd<T, CS, NEOX, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
-    case 4: contig_go_xd<T, CS, NEOX, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
-    case 8: contig_go_xd<T, CS, NEOX, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps, mid); return;
-    default: break;
-  }
   if (mid) {  // the staged form on any other shape: the item kernel
     switch (kk) {
       case 1: rmsnorm_rope_fp8_kernel<T, CS, NEOX, 1, true><<<grid, kBlock, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, pl, n_f, eps); break;
@@ -615,7 +547,17 @@ hipError_t launch_rmsnorm_rope_fp8(const void* x, const void* w, const void* cos
                                    int64_t xs, int64_t qs, int dtype, int cs_dtype, bool neox,
                                    float eps, bool round_mid, hipStream_t stream) {
   const RowPlan pl = make_plan(heads, head_dim, rope_dim);
-  if (contig_blocks(pl) == 0 && fused_tail_ok(heads, head_dim, rope_dim))
+  const int g = contig_blocks(pl);
+  if (g != 0) {
+    const auto* xp = static_cast<const uint16_t*>(x);
+    const auto* wp = static_cast<const uint16_t*>(w);
+    if (dtype == 1)
+      return launch_rmsnorm_rope_fp8_contig_f16(xp, wp, cos, sin, q, scales, tokens, head_dim, g,
+                                                xs, qs, cs_dtype, neox, eps, round_mid, stream);
+    return launch_rmsnorm_rope_fp8_contig_bf16(xp, wp, cos, sin, q, scales, tokens, head_dim, g,
+                                               xs, qs, cs_dtype, neox, eps, round_mid, stream);
+  }
+  if (fused_tail_ok(heads, head_dim, rope_dim))
     return launch_rmsnorm_rope_fp8_tail(x, w, cos, sin, q, scales, tokens, heads, head_dim,
                                         rope_dim, xs, qs, dtype, cs_dtype, neox, eps, round_mid,
                                         stream);
