@@ -19,6 +19,8 @@
 // Arithmetic (binary32, one final rounding):
 //   RMSNorm   y = (x * w) * rstd      x*w is exact in binary32 for 16-bit x, w
 //   LayerNorm y = fma(((x - mu0) - r) * rstd, gamma, beta), mu = mu0 + r
+#include <algorithm>
+
 #include "qrw_device.h"
 #include "qrw_launch.h"
 
@@ -342,6 +344,130 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
                n & 7);
 }
 
+// ------------------------------------------- rows of many waves, pipelined
+// RMSNorm rows of exactly 8 granules per thread of W = 4, 8 or 16 waves (n =
+// 16384, 32768 or 65536 elements), where the grid is only as large as the GPU
+// holds at once.  Each workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x,
+// ...; it issues the loads of its next row as soon as the current row's sum of
+// squares is known, before the current row's stores, so that its reads overlap
+// its own writes instead of every resident row loading and then every one
+// storing in lock step.  w (or ones when absent: x * 1 is exact, so the result
+// equals the unweighted one) stays in registers for the whole walk, and x is
+// read non-temporally.
+//
+// Measured on MI355X against the one-row-per-workgroup kernel above (bf16, 8
+// or more rotating buffer sets of at least 1 GiB in all): 1024 x 32768 23.7
+// against 25.5 us, 2048 x 16384 23.6 against 24.9, 512 x 65536 23.3 against
+// 25.4, 4096 x 16384 46.6 against 47.1, but 8192 x 16384 92.2 against 91.2;
+// rows with masked granules (1024 x 32760, 4096 x 8200, 8192 x 12288) were 2-4%
+// slower.  So it takes whole rows and at most four rows per resident workgroup.
+constexpr int kRowpipeGpl = 8;
+constexpr int kRowpipeMaxRowsPerBlock = 4;
+
+template <typename T>
+constexpr uint32_t kOnePair = std::is_same<T, BF16>::value ? 0x3F803F80u : 0x3C003C00u;
+
+template <typename T, int W, bool HAS_W>
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_rowpipe_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int64_t rows, int64_t xs,
+    int64_t ys, float n_f, float eps) {
+  constexpr int GPL = kRowpipeGpl;
+  __shared__ float slot[2][W];  // alternate per row: a wave may start the next row's sum early
+  const int t = threadIdx.x;
+  const u32x4 ones = (u32x4){kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>};
+  u32x4 wr[GPL], cur[GPL];
+  int64_t row = blockIdx.x;
+  // w and the first row interleaved, with no branch between the loads
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave * W + t;
+    wr[g] = HAS_W ? ld16(w + 8 * gi) : ones;
+    cur[g] = ld16_stream(x + row * xs + 8 * gi);
+  }
+  for (int it = 0; row < rows; row += gridDim.x, ++it) {
+    // keep w packed: widening it once outside the loop would double its registers
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(wr[g]));
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      float v[8];
+      widen8<T>(cur[g], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+    }
+    const float ss = block_sum<W>(tree8(acc), slot[it & 1]);
+    // and widen the row again below rather than keep its 64 floats live
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(cur[g]));
+    const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+    const int64_t next = row + gridDim.x;
+    u32x4 nxt[GPL];
+    if (next < rows) {  // uniform across the workgroup
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) nxt[g] = ld16_stream(x + next * xs + 8 * (g * kWave * W + t));
+    } else {
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) nxt[g] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    uint16_t* yr = y + row * ys;
+#pragma unroll
+    for (int g = 0; g < GPL; ++g)
+      st16_stream(yr + 8 * (g * kWave * W + t), rmsnorm_granule<T>(cur[g], wr[g], true, rstd));
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) cur[g] = nxt[g];
+  }
+}
+
+// Workgroups of one rowpipe instance resident on the current device at once,
+// cached per device (the runtime's occupancy figure times the CU count).
+constexpr int kMaxDevices = 64;
+template <typename T, int W, bool HAS_W>
+int64_t rowpipe_capacity() {
+  static int64_t cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int64_t* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
+  if (slot && __atomic_load_n(slot, __ATOMIC_RELAXED) > 0) return __atomic_load_n(slot, __ATOMIC_RELAXED);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rmsnorm_rowpipe_kernel<T, W, HAS_W>,
+                                                   kWave * W, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int64_t v = (int64_t)per_cu * cus;
+  if (slot) __atomic_store_n(slot, v, __ATOMIC_RELAXED);
+  return v;
+}
+
+template <typename T, int W, bool HAS_W>
+bool rowpipe_go(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t xs,
+                int64_t ys, float n_f, float eps, hipStream_t st) {
+  const int64_t cap = rowpipe_capacity<T, W, HAS_W>();
+  if (rows > kRowpipeMaxRowsPerBlock * cap) return false;
+  rmsnorm_rowpipe_kernel<T, W, HAS_W><<<dim3((unsigned)std::min(rows, cap)), kWave * W, 0, st>>>(
+      x, w, y, rows, xs, ys, n_f, eps);
+  return true;
+}
+
+// Launch the pipelined kernel if it takes this shape (whole rows of
+// kRowpipeGpl granules per thread, n % 8 == 0); false leaves the row to the
+// row-block kernel.
+template <typename T>
+bool try_rowpipe(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t n,
+                 int64_t xs, int64_t ys, float n_f, float eps, hipStream_t st) {
+  constexpr int64_t unit = 8 * kRowpipeGpl * kWave;  // elements per wave
+  switch (n % 8 == 0 && n % unit == 0 ? n / unit : 0) {
+    case 4: return w ? rowpipe_go<T, 4, true>(x, w, y, rows, xs, ys, n_f, eps, st)
+                     : rowpipe_go<T, 4, false>(x, w, y, rows, xs, ys, n_f, eps, st);
+    case 8: return w ? rowpipe_go<T, 8, true>(x, w, y, rows, xs, ys, n_f, eps, st)
+                     : rowpipe_go<T, 8, false>(x, w, y, rows, xs, ys, n_f, eps, st);
+    case 16: return w ? rowpipe_go<T, 16, true>(x, w, y, rows, xs, ys, n_f, eps, st)
+                      : rowpipe_go<T, 16, false>(x, w, y, rows, xs, ys, n_f, eps, st);
+    default: return false;
+  }
+}
+
 template <typename T, int W, int GPL, bool TAIL>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <= 4 ? (TAIL ? 7 : 8) : 4))) void layernorm_rowblock_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
@@ -582,6 +708,9 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
       QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
                         ni, xs, ys, nf, eps);
   } else if (ng <= kResidentGranules) {
+    const bool piped = dtype == 1 ? try_rowpipe<F16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream)
+                                  : try_rowpipe<BF16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream);
+    if (piped) return hipGetLastError();
     const BlockShape b = block_shape(ng, 16);
     if (dtype == 1)
       QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, b.waves, b.gpt, tail, rows, stream, xp, wp, yp, nfull,

@@ -1,8 +1,9 @@
 """GPU parity of rmsnorm_fwd / layernorm_fwd on ragged and long rows against the
 fp64 oracle, through the C ABI ("TileLang tutorial, ch. 13", s5.4: a row whose
 length is not a multiple of the vector width; s3.2.3 and s3.2.4: rows longer
-than one wave's registers, and the two-pass split-K RMSNorm with its reversed
-second pass).  Rows are stored padded (stride a multiple of 8); the padding
+than one wave's registers, including the pipelined RMSNorm kernel whose
+workgroups walk several rows, and the two-pass split-K RMSNorm with its
+reversed second pass).  Rows are stored padded (stride a multiple of 8); the padding
 columns of y must come back untouched."""
 import numpy as np
 import pytest
@@ -106,6 +107,22 @@ def test_long_rows_in_place_and_without_weights():
     _ln(4, 16391, "f16", seed=9, in_place=True, affine=False)
 
 
+# RMSNorm rows of exactly 8 granules per thread of 4, 8 or 16 waves (16384,
+# 32768, 65536 elements) take the pipelined kernel, whose workgroups each walk
+# several rows when there are more rows than resident workgroups (at most four
+# per workgroup; more rows go back to the row-block kernel).  On MI355X 1024,
+# 512 and 256 workgroups are resident for the three lengths: the cases walk
+# 2-4 rows per workgroup, with and without weights, in place, and fall back.
+@pytest.mark.parametrize("rows,n,dt,with_w,in_place", [
+    (3000, 16384, "bf16", True, False), (1500, 32768, "f16", True, False),
+    (1500, 32768, "bf16", False, True), (700, 65536, "bf16", True, False),
+    (1000, 65536, "f16", False, False), (1100, 65536, "bf16", True, False),
+    (2100, 32768, "f16", True, True), (1, 32768, "bf16", True, False)])
+def test_pipelined_rmsnorm_rows(rows, n, dt, with_w, in_place):
+    st = _rms(rows, n, dt, seed=rows + n, with_w=with_w, in_place=in_place)
+    assert st["within_2ulp_of_result"] >= 0.9999
+
+
 @pytest.mark.parametrize("n,dt,with_w", [(1 << 26, "bf16", True), ((1 << 26) - 3, "f16", False)])
 def test_longest_rmsnorm_rows(n, dt, with_w):
     # the longest row the split-K kernel accepts (QRW_MAX_ROW_SPLIT = 2^26
@@ -113,7 +130,7 @@ def test_longest_rmsnorm_rows(n, dt, with_w):
     _rms(1, n, dt, seed=13, with_w=with_w)
 
 
-@pytest.mark.parametrize("n", [16391, 262147])
+@pytest.mark.parametrize("n", [16391, 32768, 262147])
 def test_long_rows_are_batch_invariant(n):
     # a row's output does not depend on which other rows share the launch
     x = synth.normal(11, (6, n), 0.0, 1.0, "bf16")
