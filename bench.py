@@ -43,7 +43,7 @@ that size through the library's elementwise kernel, --timeline L adds
 per-wave timestamps of the fused kernel over L consecutive launches, and
 --host-cost adds the C ABI's host time per call measured from plain C, and
 --trace-summary CSV prints p10/p50/p90 kernel durations of a rocprofv3
-kernel-trace file.
+kernel-trace file (or per-kernel counter values of a --pmc file).
 
 Prints one JSON line on stdout.
 """
@@ -609,25 +609,59 @@ def host_cost(wl) -> dict:
     return out
 
 
-def trace_summary(path: str) -> str:
-    """Per-kernel duration statistics (count, mean, p10, p50, p90, min, max, in
-    microseconds) of a rocprofv3 --kernel-trace CSV."""
+def trace_summary(path: str, last: int = 0) -> str:
+    """Summary of a rocprofv3 CSV, in microseconds.  A --kernel-trace file:
+    per kernel the dispatch count and mean, p10, p50, p90, min and max
+    duration, its launch shape, and, with ``last``, the same statistics over
+    its last ``last`` dispatches (bench.py's timed launches come last).  A
+    --pmc counter file: per kernel and counter the dispatch count and the
+    median, min and max value."""
     import csv
 
     import numpy as np
 
-    durs = {}
     with open(path, newline="") as fh:
-        for row in csv.DictReader(fh):
-            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
-            durs.setdefault(row["Kernel_Name"], []).append(d)
-    lines = [f"{'count':>7} {'mean_us':>9} {'p10_us':>9} {'p50_us':>9} {'p90_us':>9} "
-             f"{'min_us':>9} {'max_us':>9}  kernel"]
-    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-        a = np.array(v)
-        p10, p50, p90 = np.percentile(a, [10, 50, 90])
-        lines.append(f"{len(a):>7} {a.mean():9.3f} {p10:9.3f} {p50:9.3f} {p90:9.3f} "
-                     f"{a.min():9.3f} {a.max():9.3f}  {name[:160]}")
+        rows = list(csv.DictReader(fh))
+    if not rows:
+        return "empty"
+    stat = lambda a: (f"{len(a):>7} {a.mean():9.3f} {np.percentile(a, 10):9.3f} "
+                      f"{np.percentile(a, 50):9.3f} {np.percentile(a, 90):9.3f} "
+                      f"{a.min():9.3f} {a.max():9.3f}")
+    head = (f"{'count':>7} {'mean_us':>9} {'p10_us':>9} {'p50_us':>9} {'p90_us':>9} "
+            f"{'min_us':>9} {'max_us':>9}  kernel")
+    if "Counter_Name" in rows[0]:
+        vals = {}
+        for r in rows:
+            vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(
+                float(r["Counter_Value"]))
+        lines = [f"{'count':>7} {'median':>14} {'min':>14} {'max':>14}  counter  kernel"]
+        for (name, ctr), v in sorted(vals.items(), key=lambda kv: -len(kv[1])):
+            a = np.array(v)
+            lines.append(f"{len(a):>7} {np.median(a):14.1f} {a.min():14.1f} {a.max():14.1f}  "
+                         f"{ctr}  {name[:160]}")
+        return "\n".join(lines)
+    durs, shape = {}, {}
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        name = r["Kernel_Name"]
+        durs.setdefault(name, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        if name not in shape:
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X", "?")
+            wg = r.get("Workgroup_Size") or r.get("Workgroup_Size_X", "?")
+            vg = r.get("Arch_VGPR_Count") or r.get("VGPR_Count", "?")
+            shape[name] = f"grid {grid} threads, workgroups of {wg}, {vg} arch VGPRs"
+    lines = [head]
+    order = sorted(durs.items(), key=lambda kv: -sum(kv[1]))
+    for name, v in order:
+        lines.append(f"{stat(np.array(v))}  {name[:160]}")
+    lines.append("")
+    for name, v in order:
+        lines.append(f"launch: {shape[name]}  {name[:160]}")
+    if last:
+        lines += ["", f"last {last} dispatches of each kernel with at least that many:", head]
+        for name, v in order:
+            if len(v) >= last:
+                lines.append(f"{stat(np.array(v[-last:]))}  {name[:160]}")
     return "\n".join(lines)
 
 
@@ -775,15 +809,19 @@ def main() -> int:
                     help="also time the C ABI's host path from plain C (validation alone; valid "
                          "calls of the fused operator and bare launches), reported as host_cost")
     ap.add_argument("--trace-summary", metavar="CSV",
-                    help="print per-kernel duration statistics of a rocprofv3 kernel-trace CSV "
-                         "and exit (no GPU work)")
+                    help="print per-kernel duration statistics of a rocprofv3 kernel-trace CSV, "
+                         "or per-kernel counter statistics of a --pmc counter CSV, and exit (no "
+                         "GPU work)")
+    ap.add_argument("--trace-last", type=int, default=0, metavar="K",
+                    help="with --trace-summary: also the statistics of each kernel's last K "
+                         "dispatches (the timed launches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 5 plain device copies of MIB MiB (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     args = ap.parse_args()
 
     if args.trace_summary:
-        print(trace_summary(args.trace_summary))
+        print(trace_summary(args.trace_summary, args.trace_last))
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

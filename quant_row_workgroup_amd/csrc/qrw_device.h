@@ -265,7 +265,8 @@ __device__ __forceinline__ float div_rn(float x, float s, float y) {
 
 // The quantiser's scale RN(a / 448), a >= 1e-4 finite, by the same correction
 // with the constant RN(1/448); equal to the correctly rounded quotient for
-// every binary32 a in [2^-14, 2^128) (checked exhaustively against it).
+// every binary32 a in [2^-14, 2^128): tests/test_gpu_recip.py sweeps every
+// such a on the GPU against the binary32 value nearest the binary64 quotient.
 __device__ __forceinline__ float scale_e4m3(float a) {
   constexpr float kInv = 1.0f / 448.0f;  // folded correctly rounded
   return div_rn(a, 448.0f, kInv);
@@ -273,9 +274,12 @@ __device__ __forceinline__ float scale_e4m3(float a) {
 
 // RN(1 / s) for s in [2^-23, 2^120): the hardware reciprocal refined by one
 // Newton step, y0 + y0 (1 - s y0).  On gfx950 this equals the IEEE quotient
-// 1.0f / s for every binary32 s in that range (checked exhaustively), in three
-// instructions instead of the division sequence.  A scale of a finite amax is
-// in the range: max(amax, 1e-4) / 448 >= 2^-22.
+// 1.0f / s for every binary32 s in that range, in three instructions instead
+// of the division sequence: tests/test_gpu_recip.py sweeps every such s on the
+// GPU (about 1.2e9 values) against the binary32 value nearest the binary64
+// quotient.  A scale of a finite amax is in the range: max(amax, 1e-4) / 448
+// >= 2^-22.  div_rn's correction relies on this reciprocal being correctly
+// rounded.
 __device__ __forceinline__ float recip_rn(float s) {
   const float y0 = __builtin_amdgcn_rcpf(s);
   return fmaf(fmaf(-s, y0, 1.0f), y0, y0);
