@@ -221,5 +221,5 @@ def test_random_staged_fused(i):
     x = synth.normal(i, (T, H * D), 0.0, 2.0, dt, outlier_frac=0.01, outlier_mul=10.0)
     w = synth.normal(i + 1, (H * D,), 1.0, 0.1, dt) if r.integers(0, 3) else None
     c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 4 else 7.0)
-    test_gpu_fused_rounded._check(x, w, c, s, H, D, R, dt, cs, neox,
-                                  f"staged {T}x{H}x{D}/{R} {dt}/{cs}")
+    what = f"staged {T}x{H}x{D}/{R} {dt}/{cs} {'weight' if w is not None else 'no weight'}"
+    print(what, test_gpu_fused_rounded._check(x, w, c, s, H, D, R, dt, cs, neox, what))
