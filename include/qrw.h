@@ -160,10 +160,13 @@ int rmsnorm_rope_fp8_fwd(const void* x, const void* weight, const void* cos, con
  * normalised row is written back in x's dtype and rotated there, so
  *   u = round_T( x[t,:] * rstd_t * weight )       (T = dtype, nearest-even)
  *   z = round_T( RoPE(u) )                        (unrotated channels: z = u)
- * and scales / codes are formed from z as in rmsnorm_rope_fp8_fwd.  The
- * result equals rmsnorm_fwd, then rope_apply_*, then act_quant_fp8_fwd with
- * one group per row.  Same arguments, layout, limits and errors as
- * rmsnorm_rope_fp8_fwd.
+ * and the scale is formed from z as in rmsnorm_rope_fp8_fwd, the codes as the
+ * correctly rounded binary32 quotient z / scale.  This is the composition of
+ * rmsnorm_fwd, rope_apply_* and act_quant_fp8_fwd with one group per row.
+ * Both evaluate in binary32, so where an exact intermediate lies within that
+ * evaluation's error of a 16-bit rounding boundary either neighbour may be
+ * stored, by this call or by the three calls; elsewhere they agree.  Same
+ * arguments, layout, limits and errors as rmsnorm_rope_fp8_fwd.
  */
 int rmsnorm_rope_fp8_rounded_fwd(const void* x, const void* weight, const void* cos,
                                  const void* sin, uint8_t* q, float* scales, int64_t tokens,

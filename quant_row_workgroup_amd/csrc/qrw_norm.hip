@@ -419,22 +419,29 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-// Workgroups of one rowpipe instance resident on the current device at once,
-// cached per device (the runtime's occupancy figure times the CU count).
+// Workgroups of one rowpipe instance resident on the current device at once
+// (the runtime's occupancy figure times the CU count), cached per device; 0 if
+// either query fails, which is not cached, and the row-block kernel then
+// takes the call.
 constexpr int kMaxDevices = 64;
 template <typename T, int W, bool HAS_W>
 int64_t rowpipe_capacity() {
   static int64_t cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   int64_t* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
-  if (slot && __atomic_load_n(slot, __ATOMIC_RELAXED) > 0) return __atomic_load_n(slot, __ATOMIC_RELAXED);
+  if (slot) {
+    const int64_t v = __atomic_load_n(slot, __ATOMIC_RELAXED);
+    if (v > 0) return v;
+  }
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rmsnorm_rowpipe_kernel<T, W, HAS_W>,
-                                                   kWave * W, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 1;
+                                                   kWave * W, 0) != hipSuccess || per_cu < 1 ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();  // leave no error for the caller's launch check
+    return 0;
+  }
   const int64_t v = (int64_t)per_cu * cus;
   if (slot) __atomic_store_n(slot, v, __ATOMIC_RELAXED);
   return v;
@@ -444,7 +451,7 @@ template <typename T, int W, bool HAS_W>
 bool rowpipe_go(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t xs,
                 int64_t ys, float n_f, float eps, hipStream_t st) {
   const int64_t cap = rowpipe_capacity<T, W, HAS_W>();
-  if (rows > kRowpipeMaxRowsPerBlock * cap) return false;
+  if (cap == 0 || rows > kRowpipeMaxRowsPerBlock * cap) return false;
   rmsnorm_rowpipe_kernel<T, W, HAS_W><<<dim3((unsigned)std::min(rows, cap)), kWave * W, 0, st>>>(
       x, w, y, rows, xs, ys, n_f, eps);
   return true;

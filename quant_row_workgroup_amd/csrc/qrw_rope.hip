@@ -127,9 +127,10 @@ __global__ __launch_bounds__(kBlock) void rope_kernel(const uint16_t* x, const v
 // MID: the staged form of the page's fused dataflow, which writes the
 // normalised row back to shared memory in x's dtype and rotates it there: the
 // normalised values x * rstd * w and the rotated values are each rounded to
-// T, and the codes quantise those stored values (the same results as the
-// three operators run one after another).  Without MID the row stays in
-// binary32 from the load to the codes.
+// T, and the codes quantise those stored values: the composition of the three
+// operators, up to the 16-bit neighbour chosen where an exact intermediate is
+// within the binary32 evaluation's error of a rounding boundary.  Without MID
+// the row stays in binary32 from the load to the codes.
 template <typename T, typename CS, bool NEOX, int K, bool MID>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_fp8_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,

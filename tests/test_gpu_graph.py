@@ -8,7 +8,12 @@ write, LayerNorm, both RoPE conventions, the staged fused form, scale-add) and
 the ragged, row-block, split-K and tail-rotation paths; there, bytes the
 operators do not own (cache rows no token maps to, row padding) must keep
 their fill.  (No memset node is recorded: the graphs contain only the
-library's kernels.)"""
+library's kernels.)  A third test makes a process's first call of the
+pipelined RMSNorm inside a capture."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -166,3 +171,51 @@ def test_graph_replays_match_eager_all_entry_points():
             assert torch.equal(o[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
         _run_rest(i, other)  # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+_FIRST_CALL = r"""
+import hashlib, sys
+import torch
+sys.path.insert(0, sys.argv[2])
+import quant_row_workgroup_amd as qrw
+g0 = torch.Generator(device="cuda").manual_seed(5)
+x = (torch.randn(1500, 32768, device="cuda", generator=g0) * 2 + 0.3).to(torch.bfloat16)
+w = (torch.randn(32768, device="cuda", generator=g0) * 0.1 + 1).to(torch.bfloat16)
+y = torch.empty_like(x)
+if sys.argv[1] == "graph":
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        qrw.rmsnorm_fwd(x, w, 1e-6, out=y)  # this process's first call of the operator
+    ref = torch.empty_like(x)
+    for rep in range(3):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        qrw.rmsnorm_fwd(x, w, 1e-6, out=ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), rep
+else:
+    qrw.rmsnorm_fwd(x, w, 1e-6, out=y)
+    torch.cuda.synchronize()
+print(hashlib.sha256(y.view(torch.int16).cpu().numpy().tobytes()).hexdigest())
+"""
+
+
+def test_first_call_inside_a_capture():
+    # the pipelined RMSNorm queries the device's occupancy on its first call;
+    # when that call is being captured, the replays must still give the eager
+    # result of a process that never captured, bit for bit (the pipelined and
+    # the row-block kernel sum in different orders, so this also shows that
+    # the captured call took the same kernel)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = {}
+    for mode in ("graph", "eager"):
+        print(f"[first call] {mode}", flush=True)
+        r = subprocess.run([sys.executable, "-c", _FIRST_CALL, mode, root], capture_output=True,
+                           text=True, timeout=240)
+        assert r.returncode == 0, (mode, r.stderr[-2000:])
+        out[mode] = r.stdout.strip().splitlines()[-1]
+    assert out["graph"] == out["eager"], out
