@@ -178,6 +178,19 @@ template <typename T>
 __device__ __forceinline__ void round8(float (&v)[8]) {
   widen8<T>(narrow8<T>(v), v);
 }
+// bf16: one v_cvt_pk_bf16_f32 per element.  The pair (0, v) packed to bf16
+// and read back as one binary32 word is RN_bf16(v) itself (bf16 is the upper
+// half of binary32; the lower half is the packed zero), so no widening step is
+// needed.  NaN, infinities and signed zeros give the same words as the
+// narrow-then-widen form.
+template <>
+__device__ __forceinline__ void round8<BF16>(float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bf16x2 h = __builtin_convertvector((f32x2){0.0f, v[k]}, bf16x2);
+    v[k] = __builtin_bit_cast(float, h);
+  }
+}
 
 // ----------------------------------------------------------- wave64 reductions
 template <int CTRL>
