@@ -797,7 +797,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--plain-copy", type=int, default=0, metavar="MIB",
                     help="also time a plain copy of MIB MiB through the library's 16-byte-per-lane "
-                         "elementwise kernel (f32, alpha 1), graph-replayed like the workload, and "
+                         "elementwise kernel (f32, alpha 1), timed like the workload, and "
                          "report it as plain_copy (context: what a bare copy of that size reaches)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the same-traffic copy and empty-grid probes (fused 4096-wide "
