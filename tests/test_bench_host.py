@@ -1,5 +1,6 @@
 """Host logic of bench.py on the CPU: the row-count override, the reported
-arithmetic type, and the refusal of more than one GPU."""
+arithmetic type, the refusal of more than one GPU, the oracle baseline, and
+the summaries of rocprofv3 kernel-trace and counter files."""
 import subprocess
 import sys
 
@@ -66,3 +67,48 @@ def test_cpu_baseline_reports_both_thread_counts(name):
     assert r["kind"] == "oracle" and r["unit"] == "GB/s"
     assert 1 <= r["cores"] <= 16 and r["value"] > 0 and r["single_thread_value"] > 0
     assert f"{r['cores']} threads" in r["sample"]
+
+
+def _write_csv(path, rows):
+    import csv
+
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_trace_summary_of_a_kernel_trace(tmp_path):
+    # rocprofv3 --kernel-trace rows: durations from the timestamps (ns), per
+    # kernel in launch order, and the statistics of each kernel's last K
+    # dispatches (bench.py's timed launches come last)
+    rows, t = [], 0
+    for i in range(30):
+        for name, d in (("kA", 1000 * (i + 1)), ("kB", 500)):
+            rows.append({"Kind": "KERNEL_DISPATCH", "Kernel_Name": name, "Start_Timestamp": t,
+                         "End_Timestamp": t + d, "Grid_Size": 4096, "Workgroup_Size": 256,
+                         "Arch_VGPR_Count": 40})
+            t += d + 10
+    p = tmp_path / "k_kernel_trace.csv"
+    _write_csv(p, rows)
+    out = bench.trace_summary(str(p), last=10).splitlines()
+    a = next(l for l in out if l.endswith("kA"))
+    assert a.split()[:2] == ["30", "15.500"]  # mean of 1..30 us
+    assert any(l.startswith("launch: grid 4096 threads, workgroups of 256, 40 arch VGPRs  kA")
+               for l in out)
+    i = next(k for k, l in enumerate(out) if l.startswith("last 10 dispatches"))
+    a10 = next(l for l in out[i:] if l.endswith("kA"))
+    assert a10.split()[:2] == ["10", "25.500"]  # mean of 21..30 us
+    assert float(a10.split()[5]) == 21.0 and float(a10.split()[6]) == 30.0
+
+
+def test_trace_summary_of_a_counter_file(tmp_path):
+    rows = [{"Dispatch_Id": i, "Kernel_Name": "kA", "Counter_Name": "FETCH_SIZE",
+             "Counter_Value": 100.0 + (i % 3)} for i in range(9)]
+    rows += [{"Dispatch_Id": 9, "Kernel_Name": "copy", "Counter_Name": "FETCH_SIZE",
+              "Counter_Value": 131072.0}]
+    p = tmp_path / "k_counter_collection.csv"
+    _write_csv(p, rows)
+    out = bench.trace_summary(str(p)).splitlines()
+    a = next(l for l in out if l.endswith("kA"))
+    assert a.split()[:4] == ["9", "101.0", "100.0", "102.0"] and "FETCH_SIZE" in a
