@@ -356,11 +356,14 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
 // read non-temporally.
 //
 // Measured on MI355X against the one-row-per-workgroup kernel above (bf16, 8
-// or more rotating buffer sets of at least 1 GiB in all): 1024 x 32768 23.7
-// against 25.5 us, 2048 x 16384 23.6 against 24.9, 512 x 65536 23.3 against
-// 25.4, 4096 x 16384 46.6 against 47.1, but 8192 x 16384 92.2 against 91.2;
-// rows with masked granules (1024 x 32760, 4096 x 8200, 8192 x 12288) were 2-4%
-// slower.  So it takes whole rows and at most four rows per resident workgroup.
+// or more rotating buffer sets of at least 1 GiB in all), by rows per resident
+// workgroup: from 1.5 to 4 it was 1.00-1.17x as fast (1024 x 32768 23.8
+// against 25.4 us, 768 x 32768 17.0 against 19.8, 512 x 65536 23.0 against
+// 25.3), at 1 or less mostly slower (512 x 32768 0.91x, 1024 x 16384 0.83x: a
+// workgroup then holds one row with fewer waves than the row-block kernel), at
+// 8 0.99x; rows with masked granules (1024 x 32760, 4096 x 8200, 8192 x 12288)
+// were 2-4% slower.  So it takes whole rows, from 1.5 to 4 rows per resident
+// workgroup.
 constexpr int kRowpipeGpl = 8;
 constexpr int kRowpipeMaxRowsPerBlock = 4;
 
@@ -451,7 +454,8 @@ template <typename T, int W, bool HAS_W>
 bool rowpipe_go(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t xs,
                 int64_t ys, float n_f, float eps, hipStream_t st) {
   const int64_t cap = rowpipe_capacity<T, W, HAS_W>();
-  if (cap == 0 || rows > kRowpipeMaxRowsPerBlock * cap) return false;
+  // pipelining needs rows to walk: at least half the workgroups take two
+  if (cap == 0 || 2 * rows < 3 * cap || rows > kRowpipeMaxRowsPerBlock * cap) return false;
   rmsnorm_rowpipe_kernel<T, W, HAS_W><<<dim3((unsigned)std::min(rows, cap)), kWave * W, 0, st>>>(
       x, w, y, rows, xs, ys, n_f, eps);
   return true;

@@ -108,16 +108,17 @@ def test_long_rows_in_place_and_without_weights():
 
 
 # RMSNorm rows of exactly 8 granules per thread of 4, 8 or 16 waves (16384,
-# 32768, 65536 elements) take the pipelined kernel, whose workgroups each walk
-# several rows when there are more rows than resident workgroups (at most four
-# per workgroup; more rows go back to the row-block kernel).  On MI355X 1024,
-# 512 and 256 workgroups are resident for the three lengths: the cases walk
-# 2-4 rows per workgroup, with and without weights, in place, and fall back.
+# 32768, 65536 elements) take the pipelined kernel when there are 1.5 to 4 rows
+# per resident workgroup; its workgroups then walk several rows.  Fewer or
+# more rows go to the row-block kernel.  On MI355X 1024, 512 and 256
+# workgroups are resident for the three lengths: the cases walk 2-4 rows per
+# workgroup, with and without weights, in place, and fall back on both sides.
 @pytest.mark.parametrize("rows,n,dt,with_w,in_place", [
     (3000, 16384, "bf16", True, False), (1500, 32768, "f16", True, False),
     (1500, 32768, "bf16", False, True), (700, 65536, "bf16", True, False),
     (1000, 65536, "f16", False, False), (1100, 65536, "bf16", True, False),
-    (2100, 32768, "f16", True, True), (1, 32768, "bf16", True, False)])
+    (2100, 32768, "f16", True, True), (1, 32768, "bf16", True, False),
+    (768, 32768, "bf16", True, False), (700, 32768, "f16", False, True)])
 def test_pipelined_rmsnorm_rows(rows, n, dt, with_w, in_place):
     st = _rms(rows, n, dt, seed=rows + n, with_w=with_w, in_place=in_place)
     assert st["within_2ulp_of_result"] >= 0.9999
