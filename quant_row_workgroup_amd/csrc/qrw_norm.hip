@@ -344,38 +344,182 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
                n & 7);
 }
 
+// Row-block shape for kOneWaveGranules < ng <= kResidentGranules: gpt granules
+// per thread (4, or 8 for rows beyond 4 granules x max_waves waves), and the
+// smallest power of two in [2, 16] of waves whose threads hold the row.  At 4
+// granules (16 VGPRs of row data) the kernels run at up to 8 waves per SIMD;
+// at 8 (32 VGPRs) a 1024-thread workgroup stays within 128 VGPRs per lane.
+// Measured on MI355X (bf16): RMSNorm 2048 x 16384 25.3 against 27.3 us and
+// 1024 x 32768 26.6 against 27.3 us at 4; LayerNorm, whose three block sums
+// cost more at 16 waves, takes 4 only up to 8 waves (2048 x 16384: 27.7
+// against 28.2 us; 1024 x 32768 at 16 waves x 4: 29.5 against 28.2 us).
+struct BlockShape {
+  int waves, gpt;
+};
+constexpr int kRmsMaxWavesAt4 = 16, kLnMaxWavesAt4 = 8;  // the two operators' choices above
+inline BlockShape block_shape(int ng, int max_waves_at_4) {
+  const int gpt = ng <= max_waves_at_4 * kWave * 4 ? 4 : 8;
+  int w = 2;
+  while (w < 16 && w * kWave * gpt < ng) w *= 2;
+  return {w, gpt};
+}
+
 // ------------------------------------------- rows of many waves, pipelined
-// RMSNorm rows of exactly 8 granules per thread of W = 4, 8 or 16 waves (n =
-// 16384, 32768 or 65536 elements), where the grid is only as large as the GPU
-// holds at once.  Each workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x,
-// ...; it issues the loads of its next row as soon as the current row's sum of
-// squares is known, before the current row's stores, so that its reads overlap
-// its own writes instead of every resident row loading and then every one
-// storing in lock step.  w (or ones when absent: x * 1 is exact, so the result
-// equals the unweighted one) stays in registers for the whole walk, and x is
-// read non-temporally.
+// Rows of exactly 8 granules per thread of W = 4, 8 or 16 waves (n = 16384,
+// 32768 or 65536 elements), where the grid is only as large as the GPU holds
+// at once.  Each workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ...
+// and loads its next row while it finishes the current one, so that its reads
+// overlap its own writes instead of every resident row loading and then every
+// one storing in lock step.  The per-row constants (RMSNorm's w, LayerNorm's
+// gamma and beta) are loaded once per workgroup, and x is read non-temporally.
 //
-// Measured on MI355X against the one-row-per-workgroup kernel above (bf16, 8
-// or more rotating buffer sets of at least 1 GiB in all), by rows per resident
-// workgroup: from 1.5 to 4 it was 1.00-1.17x as fast (1024 x 32768 23.8
+// Which kernel takes a row depends on how many rows share the launch, so the
+// pipelined kernels reproduce the row-block kernel's sums bit for bit, and a
+// row's output is the same in any batch.  LayerNorm's row-block kernel has
+// the same shape on these rows.  RMSNorm's gives each of S * W waves' threads
+// 8 / S granules (S = 2 at n = 16384 and 32768): thread t here holds the
+// granules of its threads t + 64W*h, h < S, keeps S partial sums, and
+// block_sum_split adds the S * W wave sums in block_sum's order.
+//
+// Measured on MI355X against the one-row-per-workgroup kernel (bf16, 8 or more
+// rotating buffer sets of at least 1 GiB in all), by rows per resident
+// workgroup: RMSNorm from 1.5 to 4 was 1.00-1.17x as fast (1024 x 32768 23.8
 // against 25.4 us, 768 x 32768 17.0 against 19.8, 512 x 65536 23.0 against
 // 25.3), at 1 or less mostly slower (512 x 32768 0.91x, 1024 x 16384 0.83x: a
 // workgroup then holds one row with fewer waves than the row-block kernel), at
 // 8 0.99x; rows with masked granules (1024 x 32760, 4096 x 8200, 8192 x 12288)
-// were 2-4% slower.  So it takes whole rows, from 1.5 to 4 rows per resident
-// workgroup.
+// were 2-4% slower.  So both operators take whole rows, from 1.5 to 4 rows per
+// resident workgroup.
 constexpr int kRowpipeGpl = 8;
 constexpr int kRowpipeMaxRowsPerBlock = 4;
 
 template <typename T>
 constexpr uint32_t kOnePair = std::is_same<T, BF16>::value ? 0x3F803F80u : 0x3C003C00u;
 
-template <typename T, int W, bool HAS_W>
+// block_sum<S * W> of a workgroup of S * W waves, computed by W waves whose
+// thread t (of wave i) holds in v[h] the partial sum of that workgroup's
+// thread t + 64W*h: the wave sums go to slots h*W + i, and after one barrier
+// the S * W slots are added in block_sum's pairwise order.
+template <int W, int S>
+__device__ __forceinline__ float block_sum_split(const float (&v)[S], float* slot) {
+  float ws[S];
+#pragma unroll
+  for (int h = 0; h < S; ++h) ws[h] = wave_sum(v[h]);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+    for (int h = 0; h < S; ++h) slot[h * W + (threadIdx.x >> 6)] = ws[h];
+  }
+  __syncthreads();
+  float s[S * W];
+#pragma unroll
+  for (int i = 0; i < S * W; ++i) s[i] = slot[i];
+#pragma unroll
+  for (int h = S * W / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i) s[i] += s[i + h];
+  return s[0];
+}
+
+// LayerNorm's statistics on rows of 8 whole granules per thread: each
+// thread's mean m and centred sum of squares q over its own c elements, merged pairwise by Chan, Golub and LeVeque's update for two
+// halves of equal count (the union's mean is the mean of the two means, and
+// q gains d^2 c / 2 for d the difference of the means), across the lanes of
+// a wave and then across the waves in block_sum's order, through one
+// barrier.  Every step is symmetric in the two halves (d changes sign
+// exactly, and no product is left for the compiler to contract), so both
+// partners of an exchange hold the same bits.
+__device__ __forceinline__ void chan_merge(float& m, float& q, float mo, float qo, float half_c) {
+  const float d = mo - m;
+  m = 0.5f * (m + mo);
+  q = fmaf(d * d, half_c, q + qo);
+}
+
+// The merge over a wave's 64 lanes, each holding c elements, in wave_sum's
+// pairing; every lane gets the result.
+__device__ __forceinline__ void wave_chan(float& m, float& q, float c) {
+  chan_merge(m, q, dpp<kDppXor1>(m), dpp<kDppXor1>(q), 0.5f * c);
+  chan_merge(m, q, dpp<kDppXor2>(m), dpp<kDppXor2>(q), c);
+  chan_merge(m, q, dpp<kDppHalfMirror>(m), dpp<kDppHalfMirror>(q), 2.0f * c);
+  chan_merge(m, q, dpp<kDppMirror>(m), dpp<kDppMirror>(q), 4.0f * c);
+  float m0 = lane_value(m, 0), q0 = lane_value(q, 0);
+  float m2 = lane_value(m, 32), q2 = lane_value(q, 32);
+  chan_merge(m0, q0, lane_value(m, 16), lane_value(q, 16), 8.0f * c);
+  chan_merge(m2, q2, lane_value(m, 48), lane_value(q, 48), 8.0f * c);
+  chan_merge(m0, q0, m2, q2, 16.0f * c);
+  m = m0;
+  q = q0;
+}
+
+// The merge over a workgroup of W waves whose threads hold statistics over
+// c elements each, through slot (2 * W floats) and one barrier.  Returns the
+// row's mean and its centred sum of squares.
+template <int W>
+__device__ __forceinline__ void block_chan(float m, float q, float c, float* slot, float& mean,
+                                           float& sq) {
+  wave_chan(m, q, c);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    slot[threadIdx.x >> 6] = m;
+    slot[W + (threadIdx.x >> 6)] = q;
+  }
+  __syncthreads();
+  float a[W], b[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    a[i] = slot[i];
+    b[i] = slot[W + i];
+  }
+  float cw = 64.0f * c;
+#pragma unroll
+  for (int h = W / 2; h >= 1; h /= 2) {
+#pragma unroll
+    for (int i = 0; i < h; ++i) chan_merge(a[i], b[i], a[i + h], b[i + h], 0.5f * cw);
+    cw *= 2.0f;
+  }
+  mean = a[0];
+  sq = b[0];
+}
+
+// One thread's statistics over its GPL granules: the mean, then the sum of
+// squares about it.  The row stays packed between the passes and after them
+// (an empty asm keeps the compiler from holding its widened floats).
+template <typename T, int GPL>
+__device__ __forceinline__ void thread_chan(u32x4 (&raw)[GPL], float& m, float& q) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    float v[8];
+    widen8<T>(raw[g], v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += v[k];
+  }
+  m = tree8(acc) * (1.0f / (8 * GPL));  // a power of two: exact
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(raw[g]));
+  float acc2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    float v[8];
+    widen8<T>(raw[g], v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float d = v[k] - m;
+      acc2[k] = fmaf(d, d, acc2[k]);
+    }
+  }
+  q = tree8(acc2);
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(raw[g]));  // and again for the output
+}
+
+// RMSNorm: the next row's loads are issued as soon as the current row's sum of
+// squares is known, before its stores.  w (or ones when absent: x * 1 is
+// exact, so the result equals the unweighted one) stays in registers.
+template <typename T, int W, int S, bool HAS_W>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void rmsnorm_rowpipe_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, uint16_t* y, int64_t rows, int64_t xs,
     int64_t ys, float n_f, float eps) {
   constexpr int GPL = kRowpipeGpl;
-  __shared__ float slot[2][W];  // alternate per row: a wave may start the next row's sum early
+  __shared__ float slot[2][S * W];  // alternate per row: a wave may start the next row's sum early
   const int t = threadIdx.x;
   const u32x4 ones = (u32x4){kOnePair<T>, kOnePair<T>, kOnePair<T>, kOnePair<T>};
   u32x4 wr[GPL], cur[GPL];
@@ -391,15 +535,18 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
     // keep w packed: widening it once outside the loop would double its registers
 #pragma unroll
     for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(wr[g]));
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[S][8] = {};
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       float v[8];
       widen8<T>(cur[g], v);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[k], v[k], acc[k]);
+      for (int k = 0; k < 8; ++k) acc[g % S][k] = fmaf(v[k], v[k], acc[g % S][k]);
     }
-    const float ss = block_sum<W>(tree8(acc), slot[it & 1]);
+    float part[S];
+#pragma unroll
+    for (int h = 0; h < S; ++h) part[h] = tree8(acc[h]);
+    const float ss = block_sum_split<W, S>(part, slot[it & 1]);
     // and widen the row again below rather than keep its 64 floats live
 #pragma unroll
     for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(cur[g]));
@@ -422,13 +569,63 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-// Workgroups of one rowpipe instance resident on the current device at once
-// (the runtime's occupancy figure times the CU count), cached per device; 0 if
-// either query fails, which is not cached, and the row-block kernel then
-// takes the call.
+// LayerNorm, with gamma and beta both given, and the same statistics as the
+// row-block kernel on these rows (thread_chan, block_chan), gamma in registers and
+// beta in LDS (each thread reads back only the granules it wrote, so no
+// barrier guards them).  The next row's granule g is loaded right after the
+// current row's granule g is stored: with all of them issued before the
+// stores (as RMSNorm does) the kernel needs more than 128 VGPRs and spills,
+// and on MI355X 1024 x 32768 bf16 took 27.3 us against 25.2 us this way.
+template <typename T, int W>
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_rowpipe_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
+    uint16_t* y, int64_t rows, int64_t xs, int64_t ys, float n_f, float eps) {
+  constexpr int GPL = kRowpipeGpl, HT = kWave * W;
+  __shared__ float slot[2][2 * W];  // alternate per row, as in the RMSNorm kernel
+  extern __shared__ u32x4 beta_lds[];   // GPL * HT granules
+  const int t = threadIdx.x;
+  u32x4 gr[GPL], cur[GPL];
+  int64_t row = blockIdx.x;
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * HT + t;
+    gr[g] = ld16(gam + 8 * gi);
+    beta_lds[gi] = ld16(bet + 8 * gi);
+    cur[g] = ld16_stream(x + row * xs + 8 * gi);
+  }
+  for (int it = 0; row < rows; row += gridDim.x, ++it) {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(gr[g]));
+    float m, q, mean, sq;
+    thread_chan<T, GPL>(cur, m, q);
+    block_chan<W>(m, q, 8.0f * GPL, slot[it & 1], mean, sq);
+    const float rstd = 1.0f / sqrtf(sq / n_f + eps);
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(cur[g]));
+    const int64_t next = row + gridDim.x;
+    const bool more = next < rows;  // uniform across the workgroup
+    const uint16_t* xn = x + (more ? next : row) * xs;
+    uint16_t* yr = y + row * ys;
+    u32x4 nxt[GPL];
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * HT + t;
+      st16_stream(yr + 8 * gi,
+                  layernorm_out<T>(cur[g], gr[g], beta_lds[gi], true, true, mean, 0.0f, rstd));
+      nxt[g] = more ? ld16_stream(xn + 8 * gi) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) cur[g] = nxt[g];
+  }
+}
+
+// Workgroups of one kernel resident on the current device at once (the
+// runtime's occupancy figure times the CU count), cached per device; 0 if a
+// query fails, which is not cached, and the row-block kernel then takes the
+// call.  Raises the kernel's dynamic LDS limit to lds bytes first.
 constexpr int kMaxDevices = 64;
-template <typename T, int W, bool HAS_W>
-int64_t rowpipe_capacity() {
+template <auto K>
+int64_t resident_workgroups(int threads, size_t lds) {
   static int64_t cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
@@ -438,8 +635,11 @@ int64_t rowpipe_capacity() {
     if (v > 0) return v;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rmsnorm_rowpipe_kernel<T, W, HAS_W>,
-                                                   kWave * W, 0) != hipSuccess || per_cu < 1 ||
+  if ((lds > 0 && hipFuncSetAttribute(reinterpret_cast<const void*>(K),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)lds) != hipSuccess) ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, lds) != hipSuccess ||
+      per_cu < 1 ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1) {
     (void)hipGetLastError();  // leave no error for the caller's launch check
@@ -450,31 +650,85 @@ int64_t rowpipe_capacity() {
   return v;
 }
 
-template <typename T, int W, bool HAS_W>
-bool rowpipe_go(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t xs,
-                int64_t ys, float n_f, float eps, hipStream_t st) {
-  const int64_t cap = rowpipe_capacity<T, W, HAS_W>();
-  // pipelining needs rows to walk: at least half the workgroups take two
-  if (cap == 0 || 2 * rows < 3 * cap || rows > kRowpipeMaxRowsPerBlock * cap) return false;
-  rmsnorm_rowpipe_kernel<T, W, HAS_W><<<dim3((unsigned)std::min(rows, cap)), kWave * W, 0, st>>>(
-      x, w, y, rows, xs, ys, n_f, eps);
+// Pipelining needs rows to walk: at least half the workgroups take two.
+inline bool rowpipe_window(int64_t rows, int64_t cap) {
+  return cap > 0 && 2 * rows >= 3 * cap && rows <= kRowpipeMaxRowsPerBlock * cap;
+}
+
+// The pipelined kernels' shape for n elements: W waves holding S row-block
+// threads each, or false if n is not 8 granules per thread of the row-block
+// kernel's threads (or of a pair of them).
+inline bool rowpipe_shape(int64_t n, int max_waves_at_4, int* W, int* S) {
+  if (n % (8 * kRowpipeGpl * kWave) != 0) return false;
+  const int ng = (int)(n / 8);
+  const BlockShape b = block_shape(ng, max_waves_at_4);
+  if (b.waves * kWave * b.gpt != ng || kRowpipeGpl % b.gpt != 0) return false;
+  *S = kRowpipeGpl / b.gpt;
+  *W = b.waves / *S;
+  return *W * *S == b.waves;
+}
+
+// Waves of 8 granules per thread that hold a row of n elements exactly, if
+// that is 4, 8 or 16; else 0.
+inline int whole_waves(int64_t n) {
+  const int64_t unit = 8 * kRowpipeGpl * kWave;  // elements per wave
+  const int64_t w = n % unit == 0 ? n / unit : 0;
+  return w == 4 || w == 8 || w == 16 ? (int)w : 0;
+}
+
+template <typename T, int W, int S, bool HAS_W>
+bool rmsnorm_rowpipe_go(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows,
+                        int64_t xs, int64_t ys, float n_f, float eps, hipStream_t st) {
+  constexpr auto K = rmsnorm_rowpipe_kernel<T, W, S, HAS_W>;
+  const int64_t cap = resident_workgroups<K>(kWave * W, 0);
+  if (!rowpipe_window(rows, cap)) return false;
+  K<<<dim3((unsigned)std::min(rows, cap)), kWave * W, 0, st>>>(x, w, y, rows, xs, ys, n_f, eps);
   return true;
 }
 
-// Launch the pipelined kernel if it takes this shape (whole rows of
-// kRowpipeGpl granules per thread, n % 8 == 0); false leaves the row to the
-// row-block kernel.
+// Launch the pipelined RMSNorm kernel if it takes this shape and row count;
+// false leaves the call to the row-block kernel.
 template <typename T>
-bool try_rowpipe(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int64_t n,
-                 int64_t xs, int64_t ys, float n_f, float eps, hipStream_t st) {
-  constexpr int64_t unit = 8 * kRowpipeGpl * kWave;  // elements per wave
-  switch (n % 8 == 0 && n % unit == 0 ? n / unit : 0) {
-    case 4: return w ? rowpipe_go<T, 4, true>(x, w, y, rows, xs, ys, n_f, eps, st)
-                     : rowpipe_go<T, 4, false>(x, w, y, rows, xs, ys, n_f, eps, st);
-    case 8: return w ? rowpipe_go<T, 8, true>(x, w, y, rows, xs, ys, n_f, eps, st)
-                     : rowpipe_go<T, 8, false>(x, w, y, rows, xs, ys, n_f, eps, st);
-    case 16: return w ? rowpipe_go<T, 16, true>(x, w, y, rows, xs, ys, n_f, eps, st)
-                      : rowpipe_go<T, 16, false>(x, w, y, rows, xs, ys, n_f, eps, st);
+bool try_rmsnorm_rowpipe(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows,
+                         int64_t n, int64_t xs, int64_t ys, float n_f, float eps,
+                         hipStream_t st) {
+  int W = 0, S = 0;
+  if (!rowpipe_shape(n, kRmsMaxWavesAt4, &W, &S)) return false;
+#define QRW_RMS_PIPE(WV, SV)                                                              \
+  if (W == WV && S == SV)                                                                 \
+    return w ? rmsnorm_rowpipe_go<T, WV, SV, true>(x, w, y, rows, xs, ys, n_f, eps, st)   \
+             : rmsnorm_rowpipe_go<T, WV, SV, false>(x, w, y, rows, xs, ys, n_f, eps, st);
+  QRW_RMS_PIPE(4, 2)
+  QRW_RMS_PIPE(8, 2)
+  QRW_RMS_PIPE(16, 1)
+#undef QRW_RMS_PIPE
+  return false;
+}
+
+template <typename T, int W>
+bool layernorm_rowpipe_go(const uint16_t* x, const uint16_t* g, const uint16_t* b, uint16_t* y,
+                          int64_t rows, int64_t xs, int64_t ys, float n_f, float eps,
+                          hipStream_t st) {
+  constexpr auto K = layernorm_rowpipe_kernel<T, W>;
+  constexpr size_t lds = sizeof(u32x4) * kRowpipeGpl * kWave * W;
+  const int64_t cap = resident_workgroups<K>(kWave * W, lds);
+  if (!rowpipe_window(rows, cap)) return false;
+  K<<<dim3((unsigned)std::min(rows, cap)), kWave * W, lds, st>>>(x, g, b, y, rows, xs, ys, n_f,
+                                                                 eps);
+  return true;
+}
+
+// The same for LayerNorm with both gamma and beta, whose row-block kernel on
+// these rows has the pipelined kernel's shape.
+template <typename T>
+bool try_layernorm_rowpipe(const uint16_t* x, const uint16_t* g, const uint16_t* b, uint16_t* y,
+                           int64_t rows, int64_t n, int64_t xs, int64_t ys, float n_f, float eps,
+                           hipStream_t st) {
+  if (!g || !b) return false;
+  switch (whole_waves(n)) {
+    case 4: return layernorm_rowpipe_go<T, 4>(x, g, b, y, rows, xs, ys, n_f, eps, st);
+    case 8: return layernorm_rowpipe_go<T, 8>(x, g, b, y, rows, xs, ys, n_f, eps, st);
+    case 16: return layernorm_rowpipe_go<T, 16>(x, g, b, y, rows, xs, ys, n_f, eps, st);
     default: return false;
   }
 }
@@ -554,6 +808,68 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
                n & 7);
 }
 
+// The row-block kernel on rows of 8 whole granules per thread of W = 4, 8 or
+// 16 waves (n = 16384, 32768, 65536): Chan statistics through one barrier,
+// which the pipelined kernel reproduces bit for bit.  Measured on MI355X
+// (bf16, against the two-part kernel above, which these rows took before):
+// with 8 waves at 4 granules, 16384-element rows ran 0.75x as fast at 1024
+// rows (1.05x at 8192); at 8 granules and up to 6 waves per SIMD, 1.00-1.04x
+// from 256 to 1024 rows and 0.98x at 8192.  At 8 and 16 waves, more than 4
+// waves per SIMD made it slower (640 x 32768: 0.89x; 4096 x 32768: 0.92x),
+// 4 gives 1.04x and 0.98x.
+template <typename T, int W, int GPL>
+__global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <= 4 ? 8 : 4))) void layernorm_rowblock_chan_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
+    uint16_t* y, int64_t xs, int64_t ys, float n_f, float eps) {
+  __shared__ float slot[2 * W];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * xs;
+  uint16_t* yr = y + row * ys;
+  u32x4 raw[GPL];
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) raw[g] = ld16_stream(xr + 8 * (g * kWave * W + t));
+  float m, q, mean, sq;
+  thread_chan<T, GPL>(raw, m, q);
+  block_chan<W>(m, q, 8.0f * GPL, slot, mean, sq);
+  const float rstd = 1.0f / sqrtf(sq / n_f + eps);
+  const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
+  if (gam && bet) {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], ld16(gam + 8 * gi), ld16(bet + 8 * gi),
+                                                true, true, mean, 0.0f, rstd));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const int gi = g * kWave * W + t;
+      st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], gam ? ld16(gam + 8 * gi) : zero,
+                                                bet ? ld16(bet + 8 * gi) : zero, gam != nullptr,
+                                                bet != nullptr, mean, 0.0f, rstd));
+    }
+  }
+}
+
+// Launch it for rows of n = 16384, 32768 or 65536 elements (W = n / 4096
+// waves; whole_waves gives W, or 0 for any other n); false otherwise.
+template <typename T>
+bool layernorm_rowblock_chan(int W, const uint16_t* x, const uint16_t* g, const uint16_t* bt,
+                             uint16_t* y, int64_t rows, int64_t xs, int64_t ys, float n_f,
+                             float eps, hipStream_t st) {
+  const dim3 grid((unsigned)rows);
+  if (W == 4)
+    layernorm_rowblock_chan_kernel<T, 4, 8><<<grid, kWave * 4, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
+  else if (W == 8)
+    layernorm_rowblock_chan_kernel<T, 8, 8><<<grid, kWave * 8, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
+  else if (W == 16)
+    layernorm_rowblock_chan_kernel<T, 16, 8><<<grid, kWave * 16, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
+  else
+    return false;
+  return true;
+}
+
 // ------------------------------------------------- split-K, two passes
 // Rows beyond what a workgroup's registers hold (s3.2.4): the first pass only
 // accumulates the sum of squares, chunk by chunk; the second pass walks the
@@ -622,25 +938,6 @@ namespace {
 
 int granules_per_lane(int ng) {
   return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16;
-}
-
-// Row-block shape for kOneWaveGranules < ng <= kResidentGranules: gpt granules
-// per thread (4, or 8 for rows beyond 4 granules x max_waves waves), and the
-// smallest power of two in [2, 16] of waves whose threads hold the row.  At 4
-// granules (16 VGPRs of row data) the kernels run at up to 8 waves per SIMD;
-// at 8 (32 VGPRs) a 1024-thread workgroup stays within 128 VGPRs per lane.
-// Measured on MI355X (bf16): RMSNorm 2048 x 16384 25.3 against 27.3 us and
-// 1024 x 32768 26.6 against 27.3 us at 4; LayerNorm, whose three block sums
-// cost more at 16 waves, takes 4 only up to 8 waves (2048 x 16384: 27.7
-// against 28.2 us; 1024 x 32768 at 16 waves x 4: 29.5 against 28.2 us).
-struct BlockShape {
-  int waves, gpt;
-};
-BlockShape block_shape(int ng, int max_waves_at_4) {
-  const int gpt = ng <= max_waves_at_4 * kWave * 4 ? 4 : 8;
-  int w = 2;
-  while (w < 16 && w * kWave * gpt < ng) w *= 2;
-  return {w, gpt};
 }
 
 }  // namespace
@@ -719,10 +1016,11 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
       QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
                         ni, xs, ys, nf, eps);
   } else if (ng <= kResidentGranules) {
-    const bool piped = dtype == 1 ? try_rowpipe<F16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream)
-                                  : try_rowpipe<BF16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream);
+    const bool piped =
+        dtype == 1 ? try_rmsnorm_rowpipe<F16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream)
+                   : try_rmsnorm_rowpipe<BF16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream);
     if (piped) return hipGetLastError();
-    const BlockShape b = block_shape(ng, 16);
+    const BlockShape b = block_shape(ng, kRmsMaxWavesAt4);
     if (dtype == 1)
       QRW_ROWBLOCK_DISPATCH(rmsnorm_rowblock_kernel, F16, b.waves, b.gpt, tail, rows, stream, xp, wp, yp, nfull,
                             ni, xs, ys, nf, eps);
@@ -765,7 +1063,17 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
       QRW_NORM_DISPATCH(layernorm_kernel, BF16, gpl, full, tail, grid, stream, xp, gp, bp, yp,
                         rows, nfull, ni, xs, ys, nf, eps);
   } else {
-    const BlockShape b = block_shape(ng, 8);
+    const bool piped =
+        dtype == 1 ? try_layernorm_rowpipe<F16>(xp, gp, bp, yp, rows, n, xs, ys, nf, eps, stream)
+                   : try_layernorm_rowpipe<BF16>(xp, gp, bp, yp, rows, n, xs, ys, nf, eps, stream);
+    if (piped) return hipGetLastError();
+    if (const int W = whole_waves(n)) {
+      const bool whole =
+          dtype == 1 ? layernorm_rowblock_chan<F16>(W, xp, gp, bp, yp, rows, xs, ys, nf, eps, stream)
+                     : layernorm_rowblock_chan<BF16>(W, xp, gp, bp, yp, rows, xs, ys, nf, eps, stream);
+      if (whole) return hipGetLastError();
+    }
+    const BlockShape b = block_shape(ng, kLnMaxWavesAt4);
     if (dtype == 1)
       QRW_ROWBLOCK_DISPATCH(layernorm_rowblock_kernel, F16, b.waves, b.gpt, tail, rows, stream, xp, gp, bp, yp,
                             nfull, ni, xs, ys, nf, eps);

@@ -1,8 +1,8 @@
 """GPU parity of rmsnorm_fwd / layernorm_fwd on ragged and long rows against the
 fp64 oracle, through the C ABI ("TileLang tutorial, ch. 13", s5.4: a row whose
 length is not a multiple of the vector width; s3.2.3 and s3.2.4: rows longer
-than one wave's registers, including the pipelined RMSNorm kernel whose
-workgroups walk several rows, and the two-pass split-K RMSNorm with its
+than one wave's registers, including the pipelined kernels whose workgroups
+walk several rows, and the two-pass split-K RMSNorm with its
 reversed second pass).  Rows are stored padded (stride a multiple of 8); the padding
 columns of y must come back untouched."""
 import numpy as np
@@ -122,6 +122,41 @@ def test_long_rows_in_place_and_without_weights():
 def test_pipelined_rmsnorm_rows(rows, n, dt, with_w, in_place):
     st = _rms(rows, n, dt, seed=rows + n, with_w=with_w, in_place=in_place)
     assert st["within_2ulp_of_result"] >= 0.9999
+
+
+# LayerNorm with gamma and beta takes the pipelined kernel on the same rows
+# and row counts; without them, or outside the window, the row-block kernel.
+@pytest.mark.parametrize("rows,n,dt,affine,in_place", [
+    (3000, 16384, "bf16", True, False), (1500, 32768, "f16", True, True),
+    (1024, 32768, "bf16", True, False), (700, 65536, "bf16", True, False),
+    (768, 32768, "bf16", True, False), (1100, 65536, "f16", True, False),
+    (2100, 32768, "bf16", True, True), (700, 32768, "f16", False, False)])
+def test_pipelined_layernorm_rows(rows, n, dt, affine, in_place):
+    st = _ln(rows, n, dt, seed=rows + n + 1, affine=affine, in_place=in_place)
+    assert st["within_2ulp_of_result"] >= 0.9999
+
+
+# Which kernel normalises a row depends on how many rows share the call, so
+# the pipelined kernels must reproduce the row-block kernel's sums bit for
+# bit ("The TileLang kernel DSL in DeepSeek-V4", batch invariance): every row
+# of a batch that takes the pipelined kernel equals the same row normalised
+# in batches of 128, which the row-block kernel takes.
+@pytest.mark.parametrize("op", ["rmsnorm", "rmsnorm_now", "layernorm"])
+@pytest.mark.parametrize("rows,n,dt", [(1536, 16384, "bf16"), (1024, 32768, "bf16"),
+                                       (1024, 32768, "f16"), (512, 65536, "bf16")])
+def test_pipelined_rows_are_batch_invariant(op, rows, n, dt):
+    x = dev(synth.normal(rows + n, (rows, n), 0.5, 2.0, dt, outlier_frac=0.01,
+                         outlier_mul=10.0), dt)
+    g = dev(synth.normal(5, (n,), 1.0, 0.1, dt), dt)
+    b = dev(synth.normal(6, (n,), 0.0, 0.1, dt), dt)
+    if op == "layernorm":
+        f = lambda t: qrw.layernorm_fwd(t, g, b, 1e-5)
+    else:
+        f = lambda t: qrw.rmsnorm_fwd(t, g if op == "rmsnorm" else None, 1e-6)
+    whole = host(f(x))
+    chunked = np.concatenate([host(f(x[r:r + 128])) for r in range(0, rows, 128)])
+    diff = np.flatnonzero((whole != chunked).any(axis=1))
+    assert diff.size == 0, f"{diff.size} rows differ, first {diff[:5]}"
 
 
 @pytest.mark.parametrize("n,dt,with_w", [(1 << 26, "bf16", True), ((1 << 26) - 3, "f16", False)])
