@@ -4,8 +4,9 @@ and the activation quant; groups in the per-group quant; heads in the QK
 norm; rotation pairs in RoPE; elements in the elementwise family.  Each test
 plants non-finite values in a few places and checks every other output
 against the oracle on the same input, at the usual bars; the long-row
-(workgroup per row) and split-K paths are included, where the rows of a
-batch share no reduction."""
+(workgroup per row), pipelined (1024 rows of 32768: a workgroup walks two
+rows) and split-K paths are included, where the rows of a batch share no
+reduction."""
 import numpy as np
 import pytest
 
@@ -31,7 +32,8 @@ def _plant(x, dt, spots):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("rows,n", [(8, 4096), (7, 1000), (6, 16384), (5, 40000), (3, 100000)])
+@pytest.mark.parametrize("rows,n", [(8, 4096), (7, 1000), (6, 16384), (5, 40000), (3, 100000),
+                                    (1024, 32768)])
 def test_rmsnorm_rows_stay_independent(dt, rows, n):
     x = _plant(synth.normal(rows + n, (rows, n), 0.0, 1.0, dt), dt,
                [(1, 7), (rows - 1, n - 1), (rows - 1, 0)])
@@ -42,7 +44,7 @@ def test_rmsnorm_rows_stay_independent(dt, rows, n):
                    what=f"rmsnorm {rows}x{n}")
 
 
-@pytest.mark.parametrize("rows,n", [(8, 4096), (6, 16384), (4, 65536)])
+@pytest.mark.parametrize("rows,n", [(8, 4096), (6, 16384), (4, 65536), (1024, 32768)])
 def test_layernorm_rows_stay_independent(rows, n):
     dt = "bf16"
     x = _plant(synth.normal(rows + n, (rows, n), 0.5, 2.0, dt), dt, [(0, 3), (rows - 2, n // 2)])

@@ -159,6 +159,35 @@ def test_pipelined_rows_are_batch_invariant(op, rows, n, dt):
     assert diff.size == 0, f"{diff.size} rows differ, first {diff[:5]}"
 
 
+# The whole-granule LayerNorm rows (16384, 32768, 65536 elements) take Chan's
+# pairwise statistics in both kernels: a constant row must still give beta
+# bit for bit (its per-thread means are exact and every merge adds zero), and
+# rows far from zero mean must stay within the bar.  Small batches take the
+# row-block kernel, 1.5-4 rows per resident workgroup the pipelined one.
+@pytest.mark.parametrize("rows,n", [(3, 16384), (1536, 16384), (3, 32768), (1024, 32768),
+                                    (2, 65536), (512, 65536)])
+def test_whole_layernorm_rows_constant_and_offset(rows, n):
+    dt = "bf16"
+    g = synth.normal(3, (n,), 1.0, 0.1, dt)
+    b = synth.normal(4, (n,), 0.0, 0.1, dt)
+    # rows far from zero mean (x ~ N(300, 4), 2 ulps of bf16 there), the first
+    # and last constant
+    x = synth.normal(rows + 5, (rows, n), 300.0, 4.0, dt)
+    const = [0, rows - 1]
+    x[0] = synth.to_storage(np.full(n, 0.75), dt)
+    x[rows - 1] = synth.to_storage(np.full(n, -3.0), dt)
+    mid = slice(1, rows - 1)
+    got = host(qrw.layernorm_fwd(dev(x, dt), dev(g, dt), dev(b, dt), 1e-5))
+    for r in const:
+        assert np.array_equal(got[r], b), f"constant row {r}"
+    if rows > 2:
+        xm = x[mid]
+        st = assert_close16(got[mid], oracle.layernorm(xm, g, b, dt, 1e-5), dt,
+                            term_scale=layernorm_terms(xm, g, b, dt, 1e-5),
+                            what=f"offset layernorm {rows}x{n}")
+        assert st["within_2ulp_of_result"] >= 0.9999
+
+
 @pytest.mark.parametrize("n,dt,with_w", [(1 << 26, "bf16", True), ((1 << 26) - 3, "f16", False)])
 def test_longest_rmsnorm_rows(n, dt, with_w):
     # the longest row the split-K kernel accepts (QRW_MAX_ROW_SPLIT = 2^26
