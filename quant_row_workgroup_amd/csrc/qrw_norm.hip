@@ -59,7 +59,20 @@ __device__ __forceinline__ u32x4 ld_tail(const uint16_t* p, bool mine, int nfull
 template <int GPL, bool TAIL>
 constexpr int kNormWaves = GPL <= 8 ? 4 : 2;
 
-template <typename T, int GPL, bool FULL, bool TAIL>
+// HAS_W: w is given.  Taking it as a template parameter rather than testing
+// the pointer keeps the weighted and unweighted paths from joining before the
+// row's sum: at such a join the compiler's wait for x counted the weight loads
+// as well, so the sum waited for the (cold, every-row) weight.  Measured on
+// MI355X (bf16/f16, 1 GiB of rotating buffers): 4096 x 4096 1.10x as fast,
+// 256 x 1024 1.05x, 16384 x 512 1.07x, 4096 x 8192 1.07x, 8192 x 1024-2048
+// 1.01-1.02x; 4096 x 4095 and 1024 x 4096 0.99x.
+// LATE_W: w is read at output time, after the row's sum, as the ragged form
+// always does.  With at least 4 workgroups per CU (then every wave of the
+// launch is resident at once and all of them would request w with x) that
+// measured 0.99-1.08x as fast (4096 x 4096 f16 1.06x, 65536 x 128 1.08x,
+// 4096 x 1000 1.05x); with fewer, where the extra round trip is exposed,
+// 0.90x (1024 x 4096).
+template <typename T, int GPL, bool FULL, bool TAIL, bool HAS_W, bool LATE_W>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWaves<GPL, TAIL>))) void rmsnorm_kernel(const uint16_t* x,
                                                          const uint16_t* __restrict__ w,
                                                          uint16_t* y, int64_t rows, int nfull,
@@ -84,9 +97,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   const u32x4 xt = ld_tail<TAIL>(xr, mine, nfull, n);
   // The weights are loaded with x, except in the ragged form, which reads
   // them at output time (measured faster there: 12.9 against 14.4 us on
-  // 4096 x 4095 bf16; the other way round costs on whole rows).
-  constexpr bool kPreW = !TAIL;
-  if (kPreW && w) {
+  // 4096 x 4095 bf16), and with LATE_W.
+  constexpr bool kPreW = !TAIL && !LATE_W;
+  if (kPreW && HAS_W) {
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave + lane;
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
   auto finish = [&](u32x4 xg, u32x4 wg) {
     float v[8];
     widen8<T>(xg, v);
-    if (w) {
+    if (HAS_W) {
       float wv[8];
       widen8<T>(wg, wv);
 #pragma unroll
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
     }
     return narrow8<T>(v);
   };
-  if (!kPreW && w) {  // late weights: the test stays outside the loop
+  if (!kPreW && HAS_W) {  // late weights
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave + lane;
@@ -134,11 +147,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kNormWav
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave + lane;
       if (FULL || gi < nfull)
-        st16_stream(yr + 8 * gi, finish(raw[g], w ? wr[g] : (u32x4){0u, 0u, 0u, 0u}));
+        st16_stream(yr + 8 * gi, finish(raw[g], HAS_W ? wr[g] : (u32x4){0u, 0u, 0u, 0u}));
     }
   }
-  if (mine) st_partial(yr + 8 * nfull, finish(xt, ld_tail<TAIL>(w, w != nullptr, nfull, n)), n & 7);
+  if (mine) st_partial(yr + 8 * nfull, finish(xt, ld_tail<TAIL>(w, HAS_W, nfull, n)), n & 7);
 }
+
+// The weight cases in the dispatch macro's four-parameter form.
+template <typename T, int GPL, bool FULL, bool TAIL>
+constexpr auto rmsnorm_w_kernel = rmsnorm_kernel<T, GPL, FULL, TAIL, true, false>;
+template <typename T, int GPL, bool FULL, bool TAIL>
+constexpr auto rmsnorm_wlate_kernel = rmsnorm_kernel<T, GPL, FULL, TAIL, true, true>;
+template <typename T, int GPL, bool FULL, bool TAIL>
+constexpr auto rmsnorm_now_kernel = rmsnorm_kernel<T, GPL, FULL, TAIL, false, false>;
 
 // LayerNorm's centred pass over one granule: the first cnt elements are
 // centred on mu0 and accumulated; padding elements are not centred.
@@ -628,7 +649,10 @@ template <auto K>
 int64_t resident_workgroups(int threads, size_t lds) {
   static int64_t cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
   int64_t* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
   if (slot) {
     const int64_t v = __atomic_load_n(slot, __ATOMIC_RELAXED);
@@ -940,6 +964,30 @@ int granules_per_lane(int ng) {
   return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16;
 }
 
+// Compute units of the current device, cached per device; 0 if the query
+// fails (not cached).
+int device_cus() {
+  static int cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
+  if (slot) {
+    const int v = __atomic_load_n(slot, __ATOMIC_RELAXED);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();  // leave no error for the caller's launch check
+    return 0;
+  }
+  if (slot) __atomic_store_n(slot, cus, __ATOMIC_RELAXED);
+  return cus;
+}
+
 }  // namespace
 
 #define QRW_NORM_DISPATCH(KERNEL, T, gpl, full, tail, grid, stream, ...)                      \
@@ -1009,12 +1057,24 @@ hipError_t launch_rmsnorm(const void* x, const void* w, void* y, int64_t rows, i
     const int gpl = granules_per_lane(ng);
     const bool full = !tail && ng == gpl * kWave;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (dtype == 1)
-      QRW_NORM_DISPATCH(rmsnorm_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
-                        ni, xs, ys, nf, eps);
-    else
-      QRW_NORM_DISPATCH(rmsnorm_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp, rows, nfull,
-                        ni, xs, ys, nf, eps);
+    // w at output time once the launch holds 4 or more workgroups per CU
+    const int cus = device_cus();
+    const bool late = cus > 0 && (int64_t)grid.x >= 4 * (int64_t)cus;
+    if (dtype == 1) {
+      if (!wp) QRW_NORM_DISPATCH(rmsnorm_now_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp,
+                                 rows, nfull, ni, xs, ys, nf, eps);
+      else if (late) QRW_NORM_DISPATCH(rmsnorm_wlate_kernel, F16, gpl, full, tail, grid, stream, xp,
+                                       wp, yp, rows, nfull, ni, xs, ys, nf, eps);
+      else QRW_NORM_DISPATCH(rmsnorm_w_kernel, F16, gpl, full, tail, grid, stream, xp, wp, yp,
+                             rows, nfull, ni, xs, ys, nf, eps);
+    } else {
+      if (!wp) QRW_NORM_DISPATCH(rmsnorm_now_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp,
+                                 rows, nfull, ni, xs, ys, nf, eps);
+      else if (late) QRW_NORM_DISPATCH(rmsnorm_wlate_kernel, BF16, gpl, full, tail, grid, stream, xp,
+                                       wp, yp, rows, nfull, ni, xs, ys, nf, eps);
+      else QRW_NORM_DISPATCH(rmsnorm_w_kernel, BF16, gpl, full, tail, grid, stream, xp, wp, yp,
+                             rows, nfull, ni, xs, ys, nf, eps);
+    }
   } else if (ng <= kResidentGranules) {
     const bool piped =
         dtype == 1 ? try_rmsnorm_rowpipe<F16>(xp, wp, yp, rows, n, xs, ys, nf, eps, stream)
