@@ -86,9 +86,9 @@ enum qrw_status {
  * x, y: [rows, n] with row strides x_row_stride / y_row_stride (elements,
  * multiples of 8, so every row starts 16-byte aligned).  Any 1 <= n <=
  * QRW_MAX_ROW_SPLIT: a row whose length is not a multiple of 8 ends in a
- * partial granule that is read and written element by element (columns at
- * and past n are never touched; the padding counts as zero and the mean
- * divides by n, s5.4).  Rows up to QRW_MAX_ROW_RESIDENT are read once; longer
+ * partial granule that is read and written in at most three accesses of 4,
+ * 2 and 1 elements (columns at and past n are never touched; the padding
+ * counts as zero and the mean divides by n, s5.4).  Rows up to QRW_MAX_ROW_RESIDENT are read once; longer
  * rows are read twice (sum of squares, then the output in reverse chunk
  * order, s3.2.4).
  * weight: [n], packed, same dtype, or NULL.

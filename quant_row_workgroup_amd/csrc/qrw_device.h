@@ -47,23 +47,47 @@ __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// The first `cnt` (0..8) 16-bit elements at p as one granule, the rest zero;
-// nothing at or past p + cnt is read.  (A row's partial last granule: its
-// padding contributes zero to every sum.)
+// The first `cnt` (0..7) 16-bit elements at p (16-byte aligned) as one
+// granule, the rest zero, in at most three accesses of 4, 2 and 1 elements
+// (the bits of cnt); nothing at or past p + cnt is read.  (A row's partial
+// last granule: its padding contributes zero to every sum.)  Measured on
+// MI355X: one access per element made 4096 x 4095 bf16 RMSNorm 13.2 us, this
+// 12.1 us; without the partial granule at all (a timing probe) it is 11.2 us.
 __device__ __forceinline__ u32x4 ld_partial(const uint16_t* p, int cnt) {
-  uint32_t e[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) e[k] = k < cnt ? (uint32_t)p[k] : 0u;
-  return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                 e[6] | (e[7] << 16)};
+  u32x4 g = (u32x4){0u, 0u, 0u, 0u};
+  const int a = cnt & 4, b = cnt & 2;
+  if (a) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    g[0] = v[0];
+    g[1] = v[1];
+  }
+  if (b) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p + a);
+    if (a) g[2] = v;
+    else g[0] = v;
+  }
+  if (cnt & 1) {
+    const uint32_t v = p[a + b];
+    switch ((a + b) >> 1) {
+      case 0: g[0] = v; break;
+      case 1: g[1] = v; break;
+      case 2: g[2] = v; break;
+      default: g[3] = v; break;
+    }
+  }
+  return g;
 }
-// Store the first `cnt` (0..8) elements of a granule; nothing past p + cnt is
-// written.
+// Store the first `cnt` (0..7) elements of a granule the same way; nothing
+// at or past p + cnt is written.
 __device__ __forceinline__ void st_partial(uint16_t* p, u32x4 g, int cnt) {
-  const uint32_t d[4] = {g[0], g[1], g[2], g[3]};
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k < cnt) p[k] = (uint16_t)((k & 1) ? (d[k >> 1] >> 16) : (d[k >> 1] & 0xFFFFu));
+  const int a = cnt & 4, b = cnt & 2;
+  if (a) *reinterpret_cast<u32x2*>(p) = (u32x2){g[0], g[1]};
+  if (b) *reinterpret_cast<uint32_t*>(p + a) = a ? g[2] : g[0];
+  if (cnt & 1) {
+    const int k = (a + b) >> 1;
+    const uint32_t v = k == 0 ? g[0] : k == 1 ? g[1] : k == 2 ? g[2] : g[3];
+    p[a + b] = (uint16_t)(v & 0xFFFFu);
+  }
 }
 
 // ------------------------------------------------------- element formats

@@ -61,7 +61,7 @@ def _ln(rows, n, dt, seed, affine=True, in_place=False):
     return st
 
 
-RAGGED = [1, 3, 7, 13, 100, 513, 1001, 4095, 4099, 8191]
+RAGGED = [1, 3, 7, 10, 13, 14, 100, 513, 1001, 2050, 4095, 4099, 4102, 8191]  # n % 8: every value 1-7
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -84,7 +84,7 @@ def test_ragged_without_weights_and_in_place():
 
 
 # one workgroup of several waves per row (8192 < n <= 65536)
-ROWBLOCK = [8200, 12288, 12289, 16391, 32768, 40000, 65533, 65536]
+ROWBLOCK = [8200, 12288, 12289, 12294, 16386, 16391, 32768, 40000, 65533, 65536]
 # the two-pass kernel (n > 65536, RMSNorm only)
 SPLITK = [65537, 131072, 262147, 1 << 20]
 
