@@ -879,6 +879,36 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <
   }
 }
 
+// One wave per row with Chan statistics (wave_chan, no barrier), for bf16
+// rows of 512 * GPL elements, GPL <= 8, with gamma and beta both given.  Measured on MI355X against the
+// one-wave kernel above, which other rows keep (1 GiB of rotating buffers):
+// 4096 x 4096 bf16 11.5 against 12.2 us, 16384 x 512 1.13x, 8192 x 1024 and
+// 4096 x 2048 1.04x, 4096 x 8192 (16 granules) 0.99x; in f16 the same kernel
+// ran 0.87-1.07x, so f16 rows keep the two-part mean.
+template <typename T, int GPL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_chan1_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
+    uint16_t* y, int64_t rows, int64_t xs, int64_t ys, float n_f, float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const uint16_t* xr = x + row * xs;
+  uint16_t* yr = y + row * ys;
+  u32x4 raw[GPL];
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) raw[g] = ld16_stream(xr + 8 * (g * kWave + lane));
+  float m, q;
+  thread_chan<T, GPL>(raw, m, q);
+  wave_chan(m, q, 8.0f * GPL);
+  const float rstd = 1.0f / sqrtf(q / n_f + eps);
+#pragma unroll
+  for (int g = 0; g < GPL; ++g) {
+    const int gi = g * kWave + lane;
+    st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], ld16(gam + 8 * gi), ld16(bet + 8 * gi), true,
+                                              true, m, 0.0f, rstd));
+  }
+}
+
 // Launch it for rows of n = 16384, 32768 or 65536 elements (W = n / 4096
 // waves; whole_waves gives W, or 0 for any other n); false otherwise.
 template <typename T>
@@ -1119,6 +1149,15 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
     const int gpl = granules_per_lane(ng);
     const bool full = !tail && ng == gpl * kWave;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    if (dtype != 1 && full && gpl <= 8 && gp && bp) {  // bf16 whole affine rows: Chan statistics
+      switch (gpl) {
+        case 1: layernorm_chan1_kernel<BF16, 1><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
+        case 2: layernorm_chan1_kernel<BF16, 2><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
+        case 4: layernorm_chan1_kernel<BF16, 4><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
+        default: layernorm_chan1_kernel<BF16, 8><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
+      }
+      return hipGetLastError();
+    }
     if (dtype == 1)
       QRW_NORM_DISPATCH(layernorm_kernel, F16, gpl, full, tail, grid, stream, xp, gp, bp, yp, rows,
                         nfull, ni, xs, ys, nf, eps);
