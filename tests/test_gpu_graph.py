@@ -178,44 +178,53 @@ import hashlib, sys
 import torch
 sys.path.insert(0, sys.argv[2])
 import quant_row_workgroup_amd as qrw
+op = sys.argv[3]
+rows, n = {"rms_long": (1500, 32768), "ln_long": (1500, 32768), "rms_4096": (4096, 4096)}[op]
 g0 = torch.Generator(device="cuda").manual_seed(5)
-x = (torch.randn(1500, 32768, device="cuda", generator=g0) * 2 + 0.3).to(torch.bfloat16)
-w = (torch.randn(32768, device="cuda", generator=g0) * 0.1 + 1).to(torch.bfloat16)
+x = (torch.randn(rows, n, device="cuda", generator=g0) * 2 + 0.3).to(torch.bfloat16)
+w = (torch.randn(n, device="cuda", generator=g0) * 0.1 + 1).to(torch.bfloat16)
+b = (torch.randn(n, device="cuda", generator=g0) * 0.1).to(torch.bfloat16)
+def run(out):
+    if op == "ln_long":
+        qrw.layernorm_fwd(x, w, b, 1e-5, out=out)
+    else:
+        qrw.rmsnorm_fwd(x, w, 1e-6, out=out)
 y = torch.empty_like(x)
 if sys.argv[1] == "graph":
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(g, stream=side):
-        qrw.rmsnorm_fwd(x, w, 1e-6, out=y)  # this process's first call of the operator
+        run(y)  # this process's first call of the operator
     ref = torch.empty_like(x)
     for rep in range(3):
         y.fill_(0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        qrw.rmsnorm_fwd(x, w, 1e-6, out=ref)
+        run(ref)
         torch.cuda.synchronize()
         assert torch.equal(y, ref), rep
 else:
-    qrw.rmsnorm_fwd(x, w, 1e-6, out=y)
+    run(y)
     torch.cuda.synchronize()
 print(hashlib.sha256(y.view(torch.int16).cpu().numpy().tobytes()).hexdigest())
 """
 
 
-def test_first_call_inside_a_capture():
-    # the pipelined RMSNorm queries the device's occupancy on its first call;
-    # when that call is being captured, the replays must still give the eager
-    # result of a process that never captured, bit for bit (the pipelined and
-    # the row-block kernel sum in different orders, so this also shows that
-    # the captured call took the same kernel)
+@pytest.mark.parametrize("op", ["rms_long", "ln_long", "rms_4096"])
+def test_first_call_inside_a_capture(op):
+    # The first call of an operator on a device may query the device: the
+    # pipelined norms ask for their occupancy (LayerNorm's also raises its
+    # dynamic LDS limit), the one-wave RMSNorm for the CU count.  When that
+    # call is being captured, the replays must still give the eager result of
+    # a process that never captured, bit for bit.
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     out = {}
     for mode in ("graph", "eager"):
-        print(f"[first call] {mode}", flush=True)
-        r = subprocess.run([sys.executable, "-c", _FIRST_CALL, mode, root], capture_output=True,
-                           text=True, timeout=240)
+        print(f"[first call] {op} {mode}", flush=True)
+        r = subprocess.run([sys.executable, "-c", _FIRST_CALL, mode, root, op],
+                           capture_output=True, text=True, timeout=240)
         assert r.returncode == 0, (mode, r.stderr[-2000:])
         out[mode] = r.stdout.strip().splitlines()[-1]
     assert out["graph"] == out["eager"], out
