@@ -119,6 +119,26 @@ def test_layernorm_shapes(dtype, rows, n, affine):
                    term_scale=layernorm_terms(x, g, b, dtype, 1e-5), what=f"layernorm {rows}x{n}")
 
 
+# bf16 rows of 512 * k elements (k = 1, 2, 4, 8) with gamma and beta take the
+# one-wave kernel with Chan statistics; the same rows without them, or in
+# f16, the two-part mean.  Both meet the bar, and a row is the same alone and
+# in a batch.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("rows,n", [(3, 512), (1000, 1024), (37, 2048), (513, 4096)])
+def test_layernorm_whole_rows(dtype, rows, n):
+    x = synth.normal(rows * 3 + n, (rows, n), 0.5, 2.0, dtype)
+    g = synth.normal(n + 1, (n,), 1.0, 0.1, dtype)
+    b = synth.normal(n + 2, (n,), 0.0, 0.1, dtype)
+    xt, gt, bt = dev(x, dtype), dev(g, dtype), dev(b, dtype)
+    got = host(qrw.layernorm_fwd(xt, gt, bt, 1e-5))
+    st = assert_close16(got, oracle.layernorm(x, g, b, dtype, 1e-5), dtype,
+                        term_scale=layernorm_terms(x, g, b, dtype, 1e-5),
+                        what=f"layernorm {rows}x{n} {dtype}")
+    assert st["within_2ulp_of_result"] >= 0.9999
+    for r in (0, rows - 1):
+        assert np.array_equal(host(qrw.layernorm_fwd(xt[r:r + 1], gt, bt, 1e-5))[0], got[r])
+
+
 def test_layernorm_constant_row_gives_beta_and_in_place():
     dt = "bf16"
     n = 4096
