@@ -880,12 +880,19 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <
 }
 
 // One wave per row with Chan statistics (wave_chan, no barrier), for bf16
-// rows of 512 * GPL elements, GPL <= 8, with gamma and beta both given.  Measured on MI355X against the
-// one-wave kernel above, which other rows keep (1 GiB of rotating buffers):
-// 4096 x 4096 bf16 11.5 against 12.2 us, 16384 x 512 1.13x, 8192 x 1024 and
-// 4096 x 2048 1.04x, 4096 x 8192 (16 granules) 0.99x; in f16 the same kernel
-// ran 0.87-1.07x, so f16 rows keep the two-part mean.
-template <typename T, int GPL>
+// rows of 512 * GPL elements, GPL <= 8, with gamma and beta both given.
+// Measured on MI355X against the one-wave kernel above, which other rows keep
+// (1 GiB of rotating buffers): 4096 x 4096 bf16 11.5 against 12.2 us, 16384 x
+// 512 1.13x, 8192 x 1024 and 4096 x 2048 1.04x, 4096 x 8192 (16 granules)
+// 0.99x; in f16 the same kernel ran 0.87-1.07x, so f16 rows keep the
+// two-part mean.
+// EARLY: gamma and beta are requested before the wave's reduction instead of
+// at output time (120 VGPRs instead of 67: 4 waves per SIMD instead of 7).
+// Both forms compute the same bits; EARLY is taken while the launch holds at
+// most 2 workgroups per CU, where a wave's latency is what shows: rows of
+// 4096 took 3.0 against 3.7 us at 1 row, 4.3 against 5.2 at 512, 6.5 against
+// 7.1 at 2048, but 10.6 against 9.1 at 3072 and 14.6 against 11.5 at 4096.
+template <typename T, int GPL, bool EARLY>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_chan1_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
     uint16_t* y, int64_t rows, int64_t xs, int64_t ys, float n_f, float eps) {
@@ -894,18 +901,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   if (row >= rows) return;  // wave-uniform
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
-  u32x4 raw[GPL];
+  u32x4 raw[GPL], gg[GPL], bb[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) raw[g] = ld16_stream(xr + 8 * (g * kWave + lane));
   float m, q;
   thread_chan<T, GPL>(raw, m, q);
+  if (EARLY) {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      gg[g] = ld16(gam + 8 * (g * kWave + lane));
+      bb[g] = ld16(bet + 8 * (g * kWave + lane));
+    }
+  }
   wave_chan(m, q, 8.0f * GPL);
   const float rstd = 1.0f / sqrtf(q / n_f + eps);
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
     const int gi = g * kWave + lane;
-    st16_stream(yr + 8 * gi, layernorm_out<T>(raw[g], ld16(gam + 8 * gi), ld16(bet + 8 * gi), true,
-                                              true, m, 0.0f, rstd));
+    st16_stream(yr + 8 * gi,
+                layernorm_out<T>(raw[g], EARLY ? gg[g] : ld16(gam + 8 * gi),
+                                 EARLY ? bb[g] : ld16(bet + 8 * gi), true, true, m, 0.0f, rstd));
   }
 }
 
@@ -1150,12 +1165,18 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
     const bool full = !tail && ng == gpl * kWave;
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (dtype != 1 && full && gpl <= 8 && gp && bp) {  // bf16 whole affine rows: Chan statistics
+      const int cus = device_cus();
+      const bool early = cus > 0 && (int64_t)grid.x <= 2 * (int64_t)cus;
+#define QRW_LN_CHAN1(GPL)                                                                       \
+  if (early) layernorm_chan1_kernel<BF16, GPL, true><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); \
+  else layernorm_chan1_kernel<BF16, GPL, false><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps);
       switch (gpl) {
-        case 1: layernorm_chan1_kernel<BF16, 1><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
-        case 2: layernorm_chan1_kernel<BF16, 2><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
-        case 4: layernorm_chan1_kernel<BF16, 4><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
-        default: layernorm_chan1_kernel<BF16, 8><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); break;
+        case 1: QRW_LN_CHAN1(1) break;
+        case 2: QRW_LN_CHAN1(2) break;
+        case 4: QRW_LN_CHAN1(4) break;
+        default: QRW_LN_CHAN1(8) break;
       }
+#undef QRW_LN_CHAN1
       return hipGetLastError();
     }
     if (dtype == 1)
