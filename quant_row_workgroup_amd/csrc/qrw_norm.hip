@@ -648,6 +648,31 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4))) v
 // query fails, which is not cached, and the row-block kernel then takes the
 // call.  Raises the kernel's dynamic LDS limit to lds bytes first.
 constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, cached per device; 0 if the query
+// fails (not cached).
+inline int device_cus() {
+  static int cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
+  if (slot) {
+    const int v = __atomic_load_n(slot, __ATOMIC_RELAXED);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();  // leave no error for the caller's launch check
+    return 0;
+  }
+  if (slot) __atomic_store_n(slot, cus, __ATOMIC_RELAXED);
+  return cus;
+}
+
 template <auto K>
 int64_t resident_workgroups(int threads, size_t lds) {
   static int64_t cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
@@ -844,7 +869,7 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(GPL <=
 // from 256 to 1024 rows and 0.98x at 8192.  At 8 and 16 waves, more than 4
 // waves per SIMD made it slower (640 x 32768: 0.89x; 4096 x 32768: 0.92x),
 // 4 gives 1.04x and 0.98x.
-template <typename T, int W, int GPL>
+template <typename T, int W, int GPL, bool EARLY>
 __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <= 4 ? 8 : 4))) void layernorm_rowblock_chan_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
     uint16_t* y, int64_t xs, int64_t ys, float n_f, float eps) {
@@ -853,15 +878,27 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * xs;
   uint16_t* yr = y + row * ys;
-  u32x4 raw[GPL];
+  u32x4 raw[GPL], gg[GPL], bb[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) raw[g] = ld16_stream(xr + 8 * (g * kWave * W + t));
   float m, q, mean, sq;
   thread_chan<T, GPL>(raw, m, q);
+  if (EARLY) {  // gamma and beta both given
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      gg[g] = ld16(gam + 8 * (g * kWave * W + t));
+      bb[g] = ld16(bet + 8 * (g * kWave * W + t));
+    }
+  }
   block_chan<W>(m, q, 8.0f * GPL, slot, mean, sq);
   const float rstd = 1.0f / sqrtf(sq / n_f + eps);
   const u32x4 zero = (u32x4){0u, 0u, 0u, 0u};
-  if (gam && bet) {
+  if (EARLY) {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g)
+      st16_stream(yr + 8 * (g * kWave * W + t),
+                  layernorm_out<T>(raw[g], gg[g], bb[g], true, true, mean, 0.0f, rstd));
+  } else if (gam && bet) {
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       const int gi = g * kWave * W + t;
@@ -888,10 +925,11 @@ __global__ __launch_bounds__(kWave* W) __attribute__((amdgpu_waves_per_eu(4, W <
 // two-part mean.
 // EARLY: gamma and beta are requested before the wave's reduction instead of
 // at output time (120 VGPRs instead of 67: 4 waves per SIMD instead of 7).
-// Both forms compute the same bits; EARLY is taken while the launch holds at
-// most 2 workgroups per CU, where a wave's latency is what shows: rows of
-// 4096 took 3.0 against 3.7 us at 1 row, 4.3 against 5.2 at 512, 6.5 against
-// 7.1 at 2048, but 10.6 against 9.1 at 3072 and 14.6 against 11.5 at 4096.
+// Both forms compute the same bits; EARLY is taken while the launch has at
+// most 8 waves per CU (2 workgroups), where a wave's latency is what shows:
+// rows of 4096 took 3.0 against 3.7 us at 1 row, 4.3 against 5.2 at 512, 6.5
+// against 7.1 at 2048, but 10.6 against 9.1 at 3072 and 14.6 against 11.5 at
+// 4096.
 template <typename T, int GPL, bool EARLY>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void layernorm_chan1_kernel(
     const uint16_t* x, const uint16_t* __restrict__ gam, const uint16_t* __restrict__ bet,
@@ -931,14 +969,22 @@ bool layernorm_rowblock_chan(int W, const uint16_t* x, const uint16_t* g, const 
                              uint16_t* y, int64_t rows, int64_t xs, int64_t ys, float n_f,
                              float eps, hipStream_t st) {
   const dim3 grid((unsigned)rows);
-  if (W == 4)
-    layernorm_rowblock_chan_kernel<T, 4, 8><<<grid, kWave * 4, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
-  else if (W == 8)
-    layernorm_rowblock_chan_kernel<T, 8, 8><<<grid, kWave * 8, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
-  else if (W == 16)
-    layernorm_rowblock_chan_kernel<T, 16, 8><<<grid, kWave * 16, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
-  else
-    return false;
+  const int cus = device_cus();
+  // gamma and beta requested before the reduction while the launch has at most
+  // 8 waves per CU (the one-wave kernel's rule): 16384-wide rows 1.03-1.11x
+  // as fast up to 512 rows, 32768-wide 1.03x up to 256; at 512 x 32768
+  // (16 waves per CU) 0.72x, every workgroup requesting all of gamma and
+  // beta at once
+  const bool early = g && bt && cus > 0 && rows * W <= 8 * (int64_t)cus;
+#define QRW_LN_RB(WV)                                                                            \
+  if (early) layernorm_rowblock_chan_kernel<T, WV, 8, true><<<grid, kWave * WV, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps); \
+  else layernorm_rowblock_chan_kernel<T, WV, 8, false><<<grid, kWave * WV, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
+  if (W == 4) { QRW_LN_RB(4) }
+  else if (W == 8) { QRW_LN_RB(8) }
+  else if (W == 16)  // gamma and beta at output time only: early they spill at 16 waves
+    layernorm_rowblock_chan_kernel<T, 16, 8, false><<<grid, kWave * 16, 0, st>>>(x, g, bt, y, xs, ys, n_f, eps);
+  else return false;
+#undef QRW_LN_RB
   return true;
 }
 
@@ -1010,30 +1056,6 @@ namespace {
 
 int granules_per_lane(int ng) {
   return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16;
-}
-
-// Compute units of the current device, cached per device; 0 if the query
-// fails (not cached).
-int device_cus() {
-  static int cache[kMaxDevices];  // 0 = not known yet; benign race: every writer stores the same value
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  int* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
-  if (slot) {
-    const int v = __atomic_load_n(slot, __ATOMIC_RELAXED);
-    if (v > 0) return v;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1) {
-    (void)hipGetLastError();  // leave no error for the caller's launch check
-    return 0;
-  }
-  if (slot) __atomic_store_n(slot, cus, __ATOMIC_RELAXED);
-  return cus;
 }
 
 }  // namespace
@@ -1166,7 +1188,7 @@ hipError_t launch_layernorm(const void* x, const void* g, const void* b, void* y
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (dtype != 1 && full && gpl <= 8 && gp && bp) {  // bf16 whole affine rows: Chan statistics
       const int cus = device_cus();
-      const bool early = cus > 0 && (int64_t)grid.x <= 2 * (int64_t)cus;
+      const bool early = cus > 0 && (int64_t)grid.x * kRowsPerBlock <= 8 * (int64_t)cus;
 #define QRW_LN_CHAN1(GPL)                                                                       \
   if (early) layernorm_chan1_kernel<BF16, GPL, true><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps); \
   else layernorm_chan1_kernel<BF16, GPL, false><<<grid, kBlock, 0, stream>>>(xp, gp, bp, yp, rows, xs, ys, nf, eps);
