@@ -30,12 +30,14 @@ the same workload on this host: on one thread per core (at most 16) over
 contiguous blocks of rows (`value`, `cores`), and on one thread
 (`single_thread_value`).
 
-`copy_ceiling` (fused workloads with rows of 4096 bf16 channels, on by
-default): the same launches with the operator's arithmetic replaced by byte
-selection -- the same grid, loads and stores on the same buffers
-(qrw_probe_copy_fused_traffic) -- i.e. what a kernel with this access
-structure reaches at this size, its variant without the row dependency, and
-the same grid doing nothing (the fixed cost of a launch).
+`copy_ceiling` (fused workloads with rows of 4096 bf16 channels, and the QK
+workloads of 32 query and 8 key/value heads of 128 channels; on by default):
+the same launches with the operator's arithmetic replaced by byte selection --
+the same grid, loads and stores on the same buffers
+(qrw_probe_copy_fused_traffic, qrw_probe_copy_qk_traffic) -- i.e. what a
+kernel with this access structure reaches at this size, for the fused
+operator also its variant without the row dependency, and the same grid doing
+nothing (the fixed cost of a launch).
 
 Options: --workload runs any of the named workloads instead, --rows runs it at
 another row (token) count, --plain-copy MIB adds `plain_copy`, a bare copy of
@@ -451,11 +453,25 @@ def fused_probe_shape(cfg: dict) -> bool:
             and cfg["cs_dtype"] == "bf16" and cfg["neox"] and not cfg.get("staged"))
 
 
+def qk_probe_shape(cfg: dict) -> bool:
+    """The QK probe reproduces the QK operators' benchmark layout only: 32 query
+    heads and 8 key/value heads of 128 16-bit channels, NeoX over the whole head."""
+    return (cfg["op"] in ("qk_norm_rope", "qk_kv") and cfg["q_heads"] == 32
+            and cfg["kv_heads"] == 8 and cfg["head_dim"] == 128 and cfg["rope_dim"] == 128
+            and cfg["dtype"] in ("bf16", "f16") and cfg["cs_dtype"] in ("bf16", "f16")
+            and cfg["neox"])
+
+
+def probe_shape(cfg: dict) -> bool:
+    return fused_probe_shape(cfg) or qk_probe_shape(cfg)
+
+
 def same_traffic_ceiling(wl, steps: int):
-    """The fused operator's memory traffic and grid with no arithmetic
-    (qrw_probe_copy_fused_traffic, include/qrw_probe.h) on the workload's own
-    buffers, and the same grid doing nothing (qrw_probe_empty): what a kernel
-    with this access structure reaches at this size, and a launch's fixed cost."""
+    """The operator's memory traffic and grid with no arithmetic
+    (qrw_probe_copy_fused_traffic or qrw_probe_copy_qk_traffic,
+    include/qrw_probe.h) on the workload's own buffers, and the same grid doing
+    nothing (qrw_probe_empty): what a kernel with this access structure reaches
+    at this size, and a launch's fixed cost."""
     import torch
 
     import quant_row_workgroup_amd as qrw
@@ -465,6 +481,58 @@ def same_traffic_ceiling(wl, steps: int):
     blocks = (T + 3) // 4
     empty = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda")
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def nothing(i, sp):
+        rc = P.qrw_probe_empty(ptr(empty), blocks, ctypes.c_void_p(sp))
+        if rc != 0:
+            raise RuntimeError(f"qrw_probe_empty: status {rc}")
+
+    def empty_grid():
+        ms = timed_launches(nothing, steps)
+        mode = TIMING["mode"]
+        torch.cuda.synchronize()
+        if not torch.equal(empty.view(-1, 4)[:, 0].cpu(), torch.arange(blocks, dtype=torch.int32)):
+            raise RuntimeError("empty-grid probe wrote the wrong words")
+        return ms, mode
+
+    if wl.cfg["op"] in ("qk_norm_rope", "qk_kv"):
+        kv = wl.cfg["op"] == "qk_kv"
+
+        def qk_copy(i, sp):
+            s = wl.sets[i % len(wl.sets)]
+            if kv:
+                rc = P.qrw_probe_copy_qk_traffic(
+                    ptr(s["x"]), ptr(s["q_weight"]), ptr(s["k_weight"]), ptr(s["cos"]),
+                    ptr(s["sin"]), ptr(s["k_cache"]), ptr(s["v_cache"]), ptr(s["k_scales"]),
+                    ptr(s["v_scales"]), ptr(s["slots"]), wl.cfg["num_slots"], T, 1,
+                    ctypes.c_void_p(sp))
+            else:
+                rc = P.qrw_probe_copy_qk_traffic(
+                    ptr(s["x"]), ptr(s["q_weight"]), ptr(s["k_weight"]), ptr(s["cos"]),
+                    ptr(s["sin"]), None, None, None, None, None, 0, T, 0, ctypes.c_void_p(sp))
+            if rc != 0:
+                raise RuntimeError(f"qrw_probe_copy_qk_traffic: status {rc}")
+
+        ms = timed_launches(qk_copy, steps)
+        timing = TIMING["mode"]
+        gbs = wl.counted / (ms * 1e-3) / 1e9
+        ems, empty_timing = empty_grid()
+        wl.reset()
+        print(f"[bench] same-traffic copy: {ms * 1e3:.3f} us; empty grid of {blocks} workgroups "
+              f"{ems * 1e3:.3f} us", file=sys.stderr, flush=True)
+        what = ("q heads written back in place, k and v heads as 8 bytes per lane to the "
+                "cache rows of their slots, one 4-byte scale per slot and head" if kv else
+                "q and k heads written back in place")
+        return {
+            "kernel": (f"qrw_probe_copy_qk_traffic: the operator's grid (one wave per token), "
+                       f"loads and stores ({what}) with byte selection in place of arithmetic"),
+            "us_per_launch": round(ms * 1e3, 3),
+            "GB/s": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "timing": timing,
+            "empty_grid_us_per_launch": round(ems * 1e3, 3),
+            "empty_grid_timing": empty_timing,
+        }
 
     def copy(dep):
         def go(i, sp):
@@ -476,22 +544,13 @@ def same_traffic_ceiling(wl, steps: int):
                 raise RuntimeError(f"qrw_probe_copy_fused_traffic: status {rc}")
         return go
 
-    def nothing(i, sp):
-        rc = P.qrw_probe_empty(ptr(empty), blocks, ctypes.c_void_p(sp))
-        if rc != 0:
-            raise RuntimeError(f"qrw_probe_empty: status {rc}")
-
     out = {}
     for key, fn in (("row_dependency", copy(1)), ("no_dependency", copy(0))):
         ms = timed_launches(fn, steps)
         gbs = wl.counted / (ms * 1e-3) / 1e9
         out[key] = {"us_per_launch": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "timing": TIMING["mode"]}
-    ms = timed_launches(nothing, steps)
-    empty_timing = TIMING["mode"]
-    torch.cuda.synchronize()
-    if not torch.equal(empty.view(-1, 4)[:, 0].cpu(), torch.arange(blocks, dtype=torch.int32)):
-        raise RuntimeError("empty-grid probe wrote the wrong words")
+    ms, empty_timing = empty_grid()
     wl.reset()
     print(f"[bench] same-traffic copy: {out['row_dependency']['us_per_launch']:.3f} us "
           f"(no row dependency {out['no_dependency']['us_per_launch']:.3f} us); empty grid "
@@ -801,7 +860,7 @@ def main() -> int:
                          "report it as plain_copy (context: what a bare copy of that size reaches)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the same-traffic copy and empty-grid probes (fused 4096-wide "
-                         "workloads run them by default and report copy_ceiling)")
+                         "and QK workloads run them by default and report copy_ceiling)")
     ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
                     help="fused 4096-wide workloads: per-wave timestamps over LAUNCHES "
                          "consecutive launches, reported as timeline")
@@ -850,7 +909,7 @@ def main() -> int:
     print(f"[bench] {ms * 1e3:.3f} us/launch, {gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
     ceiling = None
-    if fused_probe_shape(wl.cfg) and not args.no_ceiling:
+    if probe_shape(wl.cfg) and not args.no_ceiling:
         ceiling = same_traffic_ceiling(wl, args.steps)
         ceiling["kernel_over_ceiling"] = round(ms * 1e3 / ceiling["us_per_launch"], 4)
     tl = timeline(wl, args.timeline) if args.timeline and fused_probe_shape(wl.cfg) else None

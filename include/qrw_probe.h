@@ -44,6 +44,35 @@ int qrw_probe_copy_fused_traffic(const void* x, const void* w, const void* cos,
                                  int64_t n, int wave_dependency, void* stream);
 
 /*
+ * Same-traffic copy of the per-head QK RMSNorm + RoPE operators
+ * ("TileLang tutorial, ch. 13", s2.4: the in-place form, and with kv != 0 the
+ * form with the quantised KV-cache write) at their benchmark layout only: 32
+ * query heads, 8 key and 8 value heads of 128 channels per packed row (row
+ * stride 6144 16-bit channels), NeoX over the whole head.  The operators' grid
+ * (one wave64 per token, four tokens per 256-thread workgroup), loads (the
+ * row's q and k granules, with kv also its v granules, 16 bytes per lane and
+ * instruction; per lane one granule of each weight and of the token's cos and
+ * sin rows) and stores, with byte selection in place of arithmetic:
+ *   every q granule (and without kv every k granule) is written back in place
+ *   as x ^ weight granule ^ cos granule ^ sin granule;
+ *   with kv, for a slot s = slots[t] in [0, num_slots): the k (v) granule's
+ *   high bytes of x ^ weight ^ cos ^ sin (x ^ cos ^ sin) go to
+ *   k_cache (v_cache) [s, 8 * granule .. +7], and each head's scale slot
+ *   [s, head] receives the bits of its first lane's first word, masked with
+ *   0x3FFFFFFF; other slots are skipped as in the operator.
+ * qkv: [tokens, 6144] 16-bit (overwritten); q_weight, k_weight: [128] 16-bit;
+ * cos, sin: [tokens, 64] 16-bit; k_cache, v_cache: [num_slots, 1024] bytes;
+ * k_scales, v_scales: [num_slots, 8] 4-byte words; slots: [tokens].  Without
+ * kv the cache arguments are ignored and may be NULL.  tokens >= 0; qkv,
+ * weights and tables 16-byte aligned, caches 8-byte aligned.
+ */
+int qrw_probe_copy_qk_traffic(void* qkv, const void* q_weight, const void* k_weight,
+                              const void* cos, const void* sin, uint8_t* k_cache,
+                              uint8_t* v_cache, float* k_scales, float* v_scales,
+                              const int64_t* slots, int64_t num_slots, int64_t tokens, int kv,
+                              void* stream);
+
+/*
  * Near-empty control: `blocks` workgroups of 256 threads; lane 0 of each wave
  * writes one 4-byte word, out[4 * block + wave] = block.  out: [4 * blocks].
  * With blocks = tokens / 4 it has the fused operator's grid.

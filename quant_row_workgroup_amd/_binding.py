@@ -77,8 +77,8 @@ def load():
     return L
 
 
-PROBE_EXPORTS = ("qrw_probe_copy_fused_traffic", "qrw_probe_empty", "qrw_probe_fused_timeline",
-                 "qrw_probe_sweep", "qrw_probe_recip_values")
+PROBE_EXPORTS = ("qrw_probe_copy_fused_traffic", "qrw_probe_copy_qk_traffic", "qrw_probe_empty",
+                 "qrw_probe_fused_timeline", "qrw_probe_sweep", "qrw_probe_recip_values")
 
 _probe = None
 
@@ -96,6 +96,7 @@ def load_probe():
     vp, i64, i32, u32, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
                               ctypes.c_float)
     L.qrw_probe_copy_fused_traffic.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]
+    L.qrw_probe_copy_qk_traffic.argtypes = [vp] * 10 + [i64, i64, i32, vp]
     L.qrw_probe_empty.argtypes = [vp, i64, vp]
     L.qrw_probe_fused_timeline.argtypes = [vp, vp, vp, vp, vp, vp, i64, f32, vp, vp]
     L.qrw_probe_sweep.argtypes = [i32, u32, u32, u32, vp, i64, vp]

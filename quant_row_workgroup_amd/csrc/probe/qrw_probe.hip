@@ -4,6 +4,9 @@
 // * copy_fused_traffic_kernel: the fused operator's memory traffic and grid
 //   with byte selection in place of arithmetic -- the bound an operator with
 //   this access structure can reach at this size.
+// * copy_qk_traffic_kernel: the same for the per-head QK RMSNorm + RoPE
+//   operators (in place, and with the FP8 KV-cache write) at their
+//   benchmark layout.
 // * empty_kernel: the same grid doing (almost) nothing -- the fixed cost of a
 //   launch of that grid.
 // * the fused operator's contiguous kernel with per-wave timestamps
@@ -71,6 +74,56 @@ __global__ __launch_bounds__(kProbeBlock) void copy_fused_traffic_kernel(
   const u32x4 mix = DEP ? (cs ^ (u32x4){red, red, red, red}) : cs;
 #pragma unroll
   for (int g = 0; g < G; ++g) st8(qr + 8 * (kWave * g + lane), high_bytes(r[g] ^ wr[g] ^ mix));
+}
+
+// The QK operators' benchmark layout: 32 query heads, 8 key and 8 value heads
+// of 128 channels (16 granules) per packed row of 6144 16-bit channels; one
+// wave per token reads the q and k heads (and, with the KV write, the v heads)
+// as 12 (10) granules per lane.
+constexpr int kQkRowGran = 768;  // granules per packed row
+constexpr int kQkQGran = 512;    // q heads
+constexpr int kQkKGran = 128;    // k heads, and as many v heads
+constexpr int kQkHeadGran = 16;
+
+template <bool KV>
+__global__ __launch_bounds__(kProbeBlock) void copy_qk_traffic_kernel(
+    uint16_t* qkv, const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+    const uint16_t* cosv, const uint16_t* sinv, uint8_t* kc, uint8_t* vc, float* ks, float* vs,
+    const int64_t* slots, int64_t num_slots, int64_t tokens) {
+  constexpr int G = (KV ? kQkQGran + 2 * kQkKGran : kQkQGran + kQkKGran) / kWave;
+  constexpr int GQ = kQkQGran / kWave;     // slots g < GQ hold q granules
+  constexpr int GK = kQkKGran / kWave;     // then GK slots of k, then GK of v
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * kProbeRows + (threadIdx.x >> 6);
+  if (t >= tokens) return;
+  uint16_t* row = qkv + t * (int64_t)(8 * kQkRowGran);
+  u32x4 r[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) r[g] = ld16_stream(row + 8 * (kWave * g + lane));
+  // a lane's place in its head fixes its weight granules and its table
+  // granule (NeoX over the whole head: granule j mod 8 of the 64-entry row)
+  const int j = lane & (kQkHeadGran - 1);
+  const u32x4 cs = ld16(cosv + t * 64 + 8 * (j & 7)) ^ ld16(sinv + t * 64 + 8 * (j & 7));
+  const u32x4 mq = ld16(wq + 8 * j) ^ cs;
+  const u32x4 mk = ld16(wk + 8 * j) ^ cs;
+  int64_t slot = t;
+  if constexpr (KV) slot = slots[t];
+  const bool cached = slot >= 0 && slot < num_slots;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int gi = kWave * g + lane;
+    if (!KV || g < GQ) {
+      st16_stream(row + 8 * gi, r[g] ^ (g < GQ ? mq : mk));
+    } else if (cached) {
+      const bool is_v = g >= GQ + GK;
+      const int hg = gi - (is_v ? kQkQGran + kQkKGran : kQkQGran);  // granule inside the part
+      st8_stream((is_v ? vc : kc) + slot * (8 * kQkKGran) + 8 * hg,
+                 high_bytes(r[g] ^ (is_v ? cs : mk)));
+      if (j == 0)
+        (is_v ? vs : ks)[slot * (kQkKGran / kQkHeadGran) + hg / kQkHeadGran] =
+            __builtin_bit_cast(float, r[g][0] & 0x3FFFFFFFu);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kProbeBlock) void empty_kernel(uint32_t* out) {
@@ -169,6 +222,35 @@ extern "C" int qrw_probe_copy_fused_traffic(const void* x, const void* w, const 
     copy_fused_traffic_kernel<true><<<grid, kProbeBlock, 0, st>>>(xp, wp, cp, sp, q, scales, tokens);
   else
     copy_fused_traffic_kernel<false><<<grid, kProbeBlock, 0, st>>>(xp, wp, cp, sp, q, scales, tokens);
+  return status_of(hipGetLastError());
+}
+
+extern "C" int qrw_probe_copy_qk_traffic(void* qkv, const void* q_weight, const void* k_weight,
+                                         const void* cos, const void* sin, uint8_t* k_cache,
+                                         uint8_t* v_cache, float* k_scales, float* v_scales,
+                                         const int64_t* slots, int64_t num_slots, int64_t tokens,
+                                         int kv, void* stream) {
+  if (tokens < 0 || tokens > (int64_t)0x7FFFFFFF || (kv && num_slots < 0)) return QRW_ERR_SHAPE;
+  if (tokens == 0) return QRW_OK;
+  if (!qkv || !q_weight || !k_weight || !cos || !sin) return QRW_ERR_NULL;
+  if (kv && (!k_cache || !v_cache || !k_scales || !v_scales || !slots)) return QRW_ERR_NULL;
+  if (!al16(qkv) || !al16(q_weight) || !al16(k_weight) || !al16(cos) || !al16(sin))
+    return QRW_ERR_ALIGN;
+  if (kv && ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 7u))
+    return QRW_ERR_ALIGN;
+  const dim3 grid((unsigned)((tokens + kProbeRows - 1) / kProbeRows));
+  auto st = static_cast<hipStream_t>(stream);
+  auto* xp = static_cast<uint16_t*>(qkv);
+  const auto* wqp = static_cast<const uint16_t*>(q_weight);
+  const auto* wkp = static_cast<const uint16_t*>(k_weight);
+  const auto* cp = static_cast<const uint16_t*>(cos);
+  const auto* sp = static_cast<const uint16_t*>(sin);
+  if (kv)
+    copy_qk_traffic_kernel<true><<<grid, kProbeBlock, 0, st>>>(
+        xp, wqp, wkp, cp, sp, k_cache, v_cache, k_scales, v_scales, slots, num_slots, tokens);
+  else
+    copy_qk_traffic_kernel<false><<<grid, kProbeBlock, 0, st>>>(
+        xp, wqp, wkp, cp, sp, nullptr, nullptr, nullptr, nullptr, nullptr, 0, tokens);
   return status_of(hipGetLastError());
 }
 

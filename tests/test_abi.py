@@ -65,6 +65,18 @@ def test_probe_validation():
     assert P.qrw_probe_copy_fused_traffic(None, W, C, S, Q, SC, 4, 4096, 1, None) == NULL
     assert P.qrw_probe_copy_fused_traffic(ctypes.c_void_p((1 << 32) + 8), W, C, S, Q, SC, 4,
                                           4096, 1, None) == ALIGN
+    # QK probe: qkv, q_weight, k_weight, cos, sin, k/v caches, k/v scales, slots
+    qk = (X, W, W, C, S)
+    kvb = (Q, Q, SC, SC, Y)
+    assert P.qrw_probe_copy_qk_traffic(*qk, None, None, None, None, None, 0, -1, 0, None) == SHAPE
+    assert P.qrw_probe_copy_qk_traffic(*qk, *kvb, -1, 4, 1, None) == SHAPE
+    assert P.qrw_probe_copy_qk_traffic(*qk, *kvb, 16, 0, 1, None) == OK
+    assert P.qrw_probe_copy_qk_traffic(None, W, W, C, S, *kvb, 16, 4, 1, None) == NULL
+    assert P.qrw_probe_copy_qk_traffic(*qk, Q, Q, SC, SC, None, 16, 4, 1, None) == NULL
+    assert P.qrw_probe_copy_qk_traffic(ctypes.c_void_p((1 << 32) + 8), W, W, C, S, *kvb, 16, 4,
+                                       1, None) == ALIGN
+    assert P.qrw_probe_copy_qk_traffic(*qk, ctypes.c_void_p(Q_ADDR + 4), Q, SC, SC, Y, 16, 4, 1,
+                                       None) == ALIGN
     assert P.qrw_probe_empty(X, -1, None) == SHAPE
     assert P.qrw_probe_empty(None, 4, None) == NULL
     assert P.qrw_probe_fused_timeline(X, W, C, S, Q, SC, 4, -1.0, Y, None) == VALUE
