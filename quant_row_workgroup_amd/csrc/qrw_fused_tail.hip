@@ -15,7 +15,12 @@
 // is gi ^ XR: lane l ^ XR of the same load instruction, read with a lane
 // exchange; interleaved pairs sit inside a granule.  The table granule of a
 // rotated granule depends on j, hence on the load step; the table is read
-// only in steps where some lane rotates (a wave-uniform test).
+// only in steps where some lane rotates (a wave-uniform test).  A lane's
+// table granule is the same in every step that rotates it: a head of at most
+// 64 granules sits at the same lanes in every step, and a longer head
+// (rope_dim/8 <= 32 granules rotate) rotates in one step of its own, at lanes
+// (s0 mod 64) and up.  So each lane reads its table granule once, with its
+// row, as the all-rotating kernel does.
 //
 // Arithmetic as in the all-rotating kernel: z = RoPE(x * w) * rstd, amax,
 // scale = max(amax, 1e-4) / 448, codes of z * (rstd / scale); with MID the
@@ -26,21 +31,28 @@
 
 namespace qrw {
 
-// Rows (waves) per workgroup: 16, measured faster than 4 or 8 on one 4096-wide
-// head rotating its last 128 channels, 4096 tokens bf16 (11.06 against 11.6
-// us).
-constexpr int kTailRows = 16;
+// Rows (waves) per workgroup: 4.  With the table read once, up front, 4 was
+// measured fastest or within 5% of the fastest of 4, 8 and 16 (MI355X, bf16
+// unless noted, outputs identical): one 4096-wide head rotating its last 128
+// channels at 1024 / 2048 / 4096 / 8192 / 16384 tokens 5.09 / 7.04 / 10.86 /
+// 19.31 / 35.35 us against 7.95 / 8.98 / 11.63 / 21.77 / 39.67 us at 16 rows;
+// 32 heads of 128 rotating 64 at 1024 / 4096 / 16384 tokens 5.72 / 11.93 /
+// 36.87 us against 8.68 / 11.90 / 42.85 us.  (16-row workgroups are ahead only
+// where they fill the GPU in exactly one round, 4096 tokens: by 1-5%.)
+constexpr int kTailRows = 4;
 
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XR, bool MID>
+// PACKED: the codes' row stride is x's (a packed call), one stride for both,
+// as in the all-rotating kernel.
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XR, bool MID, bool PACKED>
 __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, int hg_mask,
-    int s0, float n_f, float eps) {
+    int s0, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kTailRows + (threadIdx.x >> 6);
   if (t >= tokens) return;  // wave-uniform
   const uint16_t* xr = x + t * xs;
-  uint8_t* qr = q + t * qs;
+  uint8_t* qr = q + t * (PACKED ? xs : qs);
 
   u32x4 r[G], wr[G];
 #pragma unroll
@@ -49,8 +61,30 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
 #pragma unroll
     for (int g = 0; g < G; ++g) wr[g] = ld16(w + 8 * (kWave * g + lane));
   }
+  // this lane's position in the rotated span in the steps that rotate it
+  // (< 0: none; its table granule is then a valid, unused one)
+  const int jl = (lane & hg_mask & (kWave - 1)) - (s0 & (kWave - 1));
   const char* crow = table_row<CS>(cosv, t, half);
   const char* srow = table_row<CS>(sinv, t, half);
+  float c[8], sn[8];
+  if (NEOX) {
+    const int tg = jl >= 0 ? (jl & (XR - 1)) : 0;
+    Table8<CS>::load(crow, tg, c);
+    Table8<CS>::load(srow, tg, sn);
+    if (jl < XR) {  // first half of the span: x c - x_partner s
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sn[e] = -sn[e];
+    }
+  } else {
+    float c4[4], s4[4];
+    Table4<CS>::load(crow, jl >= 0 ? jl : 0, c4);
+    Table4<CS>::load(srow, jl >= 0 ? jl : 0, s4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[k] = c4[k];
+      sn[k] = s4[k];
+    }
+  }
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -59,7 +93,8 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
     for (int k = 0; k < 4; ++k) acc[(2 * g + k) & 7] = sumsq2(T{}, r[g][k], acc[(2 * g + k) & 7]);
   }
   const float ss = wave_sum(tree8(acc));
-  const float rstd = 1.0f / sqrtf(ss / n_f + eps);
+  // n = 512 * G is a power of two: the mean is an exact scaling
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / (512 * G)) + eps);
 
   float v[G][8];
   float m[4] = {0.f, 0.f, 0.f, 0.f};
@@ -77,18 +112,11 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
       for (int e = 0; e < 8; ++e) v[g][e] *= rstd;
       round8<T>(v[g]);
     }
-    const int js = ((kWave * g + lane) & hg_mask) - s0;  // position in the rotated span
-    const bool span = js >= 0;
+    // this step rotates the lane when its granule is in the span (then at
+    // position jl)
+    const bool span = ((kWave * g + lane) & hg_mask) >= s0;
     if (__builtin_amdgcn_ballot_w64(span) != 0) {  // wave-uniform: some lane rotates
       if (NEOX) {
-        float c[8], sn[8];
-        const int tg = span ? (js & (XR - 1)) : 0;
-        Table8<CS>::load(crow, tg, c);
-        Table8<CS>::load(srow, tg, sn);
-        if (js < XR) {  // first half of the span: x c - x_partner s
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sn[e] = -sn[e];
-        }
         float rv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) rv[e] = fmaf(v[g][e], c[e], lane_xor<XR>(v[g][e]) * sn[e]);
@@ -97,14 +125,11 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
           for (int e = 0; e < 8; ++e) v[g][e] = rv[e];
         }
       } else if (span) {
-        float c4[4], s4[4];
-        Table4<CS>::load(crow, js, c4);
-        Table4<CS>::load(srow, js, s4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float x0 = v[g][2 * k], x1 = v[g][2 * k + 1];
-          v[g][2 * k] = fmaf(x0, c4[k], -(x1 * s4[k]));
-          v[g][2 * k + 1] = fmaf(x1, c4[k], x0 * s4[k]);
+          v[g][2 * k] = fmaf(x0, c[k], -(x1 * sn[k]));
+          v[g][2 * k + 1] = fmaf(x1, c[k], x0 * sn[k]);
         }
       }
       if (MID) round8<T>(v[g]);  // unrotated values are already T values
@@ -136,18 +161,22 @@ bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 template <typename T, typename CS, bool NEOX, int G, int XR>
 void tail_go(dim3 grid, hipStream_t st, const void* x, const void* w, const void* c,
              const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-             int half, int hg_mask, int s0, float n_f, float eps, bool mid) {
+             int half, int hg_mask, int s0, float eps, bool mid) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
-#define QRW_TAIL_LAUNCH(HW, M)                                                                  \
-  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M><<<grid, kWave * kTailRows, 0, st>>>( \
-      xp, wp, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps)
+#define QRW_TAIL_LAUNCH(HW, M, P)                                                                  \
+  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M, P><<<grid, kWave * kTailRows, 0, st>>>( \
+      xp, wp, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps)
+  // the packed instances are the weighted ones (the usual call)
+  const bool packed = qs == xs;
   if (mid) {
-    if (wp) QRW_TAIL_LAUNCH(true, true);
-    else QRW_TAIL_LAUNCH(false, true);
+    if (wp && packed) QRW_TAIL_LAUNCH(true, true, true);
+    else if (wp) QRW_TAIL_LAUNCH(true, true, false);
+    else QRW_TAIL_LAUNCH(false, true, false);
   } else {
-    if (wp) QRW_TAIL_LAUNCH(true, false);
-    else QRW_TAIL_LAUNCH(false, false);
+    if (wp && packed) QRW_TAIL_LAUNCH(true, false, true);
+    else if (wp) QRW_TAIL_LAUNCH(true, false, false);
+    else QRW_TAIL_LAUNCH(false, false, false);
   }
 #undef QRW_TAIL_LAUNCH
 }
@@ -155,16 +184,16 @@ void tail_go(dim3 grid, hipStream_t st, const void* x, const void* w, const void
 template <typename T, typename CS, bool NEOX, int G>
 void tail_go_xr(int xr, dim3 grid, hipStream_t st, const void* x, const void* w, const void* c,
                 const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
-                int half, int hg_mask, int s0, float n_f, float eps, bool mid) {
+                int half, int hg_mask, int s0, float eps, bool mid) {
   if constexpr (!NEOX) {
-    tail_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid);
+    tail_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid);
   } else {
     switch (xr) {
-      case 1: tail_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-      case 2: tail_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-      case 4: tail_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-      case 8: tail_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-      default: tail_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
+      case 1: tail_go<T, CS, NEOX, G, 1>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      case 2: tail_go<T, CS, NEOX, G, 2>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      case 4: tail_go<T, CS, NEOX, G, 4>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      case 8: tail_go<T, CS, NEOX, G, 8>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      default: tail_go<T, CS, NEOX, G, 16>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
     }
   }
 }
@@ -172,12 +201,12 @@ void tail_go_xr(int xr, dim3 grid, hipStream_t st, const void* x, const void* w,
 template <typename T, typename CS, bool NEOX>
 void tail_go_g(int gg, int xr, dim3 grid, hipStream_t st, const void* x, const void* w,
                const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
-               int64_t qs, int half, int hg_mask, int s0, float n_f, float eps, bool mid) {
+               int64_t qs, int half, int hg_mask, int s0, float eps, bool mid) {
   switch (gg) {
-    case 1: tail_go_xr<T, CS, NEOX, 1>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-    case 2: tail_go_xr<T, CS, NEOX, 2>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-    case 4: tail_go_xr<T, CS, NEOX, 4>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
-    default: tail_go_xr<T, CS, NEOX, 8>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, n_f, eps, mid); break;
+    case 1: tail_go_xr<T, CS, NEOX, 1>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 2: tail_go_xr<T, CS, NEOX, 2>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 4: tail_go_xr<T, CS, NEOX, 4>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    default: tail_go_xr<T, CS, NEOX, 8>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
   }
 }
 
@@ -202,9 +231,8 @@ hipError_t launch_rmsnorm_rope_fp8_tail(const void* x, const void* w, const void
   const int half = (int)(rope_dim / 2);
   const int hg_mask = (int)(head_dim / 8 - 1);
   const int s0 = (int)((head_dim - rope_dim) / 8);
-  const float n_f = (float)(heads * head_dim);
 #define QRW_TAIL_ARGS gg, xr, grid, stream, x, w, cos, sin, q, scales, tokens, xs, qs, half, \
-                      hg_mask, s0, n_f, eps, round_mid
+                      hg_mask, s0, eps, round_mid
   if (dtype == 1) {
     if (cs_dtype == 3) {
       if (neox) tail_go_g<F16, float, true>(QRW_TAIL_ARGS);
