@@ -74,10 +74,11 @@ DEFAULT_WORKLOAD = "rmsnorm_rope_fp8_4096x4096_bf16"
 KERNEL_SOURCES = {
     "rmsnorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
     "layernorm": ("qrw_norm.hip", "qrw_device.h", "qrw_launch.h"),
-    "rope": ("qrw_rope.hip", "qrw_plan.h", "qrw_device.h", "qrw_launch.h"),
+    "rope": ("qrw_rope.hip", "qrw_rope_contig.hip", "qrw_contig.h", "qrw_plan.h", "qrw_device.h",
+             "qrw_launch.h"),
     "fused": ("qrw_rope.hip", "qrw_fused_contig.h", "qrw_fused_contig_bf16.hip",
-              "qrw_fused_contig_f16.hip", "qrw_fused_tail.hip", "qrw_plan.h", "qrw_device.h",
-              "qrw_launch.h"),
+              "qrw_fused_contig_f16.hip", "qrw_fused_tail.hip", "qrw_contig.h", "qrw_plan.h",
+              "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
                      "qrw_qknorm_gc_b.hip", "qrw_qknorm_gc_c.hip", "qrw_device.h", "qrw_launch.h"),
@@ -803,7 +804,7 @@ def cpu_baseline(name: str, seconds: float):
             oracle.layernorm(x, inp["gamma"], inp["beta"], cfg["dtype"], cfg["eps"])
         else:
             oracle.rope(x, cos, sin, cfg["heads"], cfg["head_dim"], cfg["rope_dim"],
-                        cfg["dtype"], cfg["cs_dtype"], True)
+                        cfg["dtype"], cfg["cs_dtype"], cfg.get("neox", True))
 
     def timed(step, budget):
         step()  # warm-up

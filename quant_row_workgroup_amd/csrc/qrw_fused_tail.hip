@@ -26,6 +26,7 @@
 // scale = max(amax, 1e-4) / 448, codes of z * (rstd / scale); with MID the
 // staged form (x*w*rstd and the rotated values rounded to T, correctly
 // rounded quotients of the stored values by the scale).
+#include "qrw_contig.h"
 #include "qrw_device.h"
 #include "qrw_launch.h"
 
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
   }
   // this lane's position in the rotated span in the steps that rotate it
   // (< 0: none; its table granule is then a valid, unused one)
-  const int jl = (lane & hg_mask & (kWave - 1)) - (s0 & (kWave - 1));
+  const int jl = contig_span_pos(lane, hg_mask, s0);
   const char* crow = table_row<CS>(cosv, t, half);
   const char* srow = table_row<CS>(sinv, t, half);
   float c[8], sn[8];
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
     }
     // this step rotates the lane when its granule is in the span (then at
     // position jl)
-    const bool span = ((kWave * g + lane) & hg_mask) >= s0;
+    const bool span = contig_rotates(kWave * g + lane, hg_mask, s0);
     if (__builtin_amdgcn_ballot_w64(span) != 0) {  // wave-uniform: some lane rotates
       if (NEOX) {
         float rv[8];

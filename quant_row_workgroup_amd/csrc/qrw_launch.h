@@ -57,6 +57,14 @@ hipError_t launch_rmsnorm_rope_fp8_contig_bf16(const uint16_t* x, const uint16_t
 // both powers of two, 16 <= rope_dim <= 256, and the row is 1, 2, 4 or 8
 // blocks of 512 channels.
 bool fused_tail_ok(int64_t heads, int64_t head_dim, int64_t rope_dim);
+// RoPE in the contiguous lane mapping (qrw_rope_contig.hip): head_dim and
+// rope_dim powers of two, 16 <= rope_dim <= min(head_dim, 256), and the row
+// is 1, 2, 4, 8 or 16 blocks of 512 channels.
+bool rope_contig_ok(int64_t heads, int64_t head_dim, int64_t rope_dim);
+hipError_t launch_rope_contig(const void* x, const void* cos, const void* sin, void* y,
+                              int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_dim,
+                              int64_t xs, int64_t ys, int dtype, int cs_dtype, bool neox,
+                              hipStream_t stream);
 hipError_t launch_rmsnorm_rope_fp8_tail(const void* x, const void* w, const void* cos,
                                         const void* sin, uint8_t* q, float* scales,
                                         int64_t tokens, int64_t heads, int64_t head_dim,

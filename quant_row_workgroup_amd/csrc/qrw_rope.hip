@@ -7,6 +7,10 @@
 // per-token cast (amax -> scale = max(amax, 1e-4)/fp8_max -> clamp -> cast)
 // in s3.1.5.
 //
+// RoPE shapes with power-of-two heads and rows of 512 * {1, 2, 4, 8, 16}
+// channels take the contiguous kernel (qrw_rope_contig.hip); the item kernel
+// below serves every other shape.
+//
 // Mapping: one wave64 per token, four tokens per workgroup.  The token row is
 // cut into items of two granules (qrw_plan.h) such that both channels of every
 // rotation pair sit in the same lane, so the rotation needs no LDS and no
@@ -526,6 +530,9 @@ int items_per_lane(int n_items, int kmax) {
 hipError_t launch_rope(const void* x, const void* cos, const void* sin, void* y, int64_t tokens,
                        int64_t heads, int64_t head_dim, int64_t rope_dim, int64_t xs,
                        int64_t ys, int dtype, int cs_dtype, bool neox, hipStream_t stream) {
+  if (rope_contig_ok(heads, head_dim, rope_dim))
+    return launch_rope_contig(x, cos, sin, y, tokens, heads, head_dim, rope_dim, xs, ys, dtype,
+                              cs_dtype, neox, stream);
   const RowPlan pl = make_plan(heads, head_dim, rope_dim);
   const int kk = items_per_lane(pl.n_items, 4);
   const dim3 grid((unsigned)((tokens + kRowsPerBlock - 1) / kRowsPerBlock));

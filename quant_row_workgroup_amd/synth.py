@@ -103,6 +103,9 @@ WORKLOADS = {
                                      seed=3),
     "rope_4096x32x128_f16": dict(op="rope", tokens=4096, heads=32, head_dim=128, rope_dim=128,
                                  dtype="f16", cs_dtype="f32", seed=4),
+    "rope_4096x32x128_f16_interleaved": dict(op="rope", tokens=4096, heads=32, head_dim=128,
+                                             rope_dim=128, dtype="f16", cs_dtype="f32",
+                                             neox=False, seed=4),
     "act_quant_4096x4096_bf16_g128": dict(op="act_quant", rows=4096, n=4096, group=128,
                                           dtype="bf16", seed=6),
     "act_quant_4096x4096_bf16_token": dict(op="act_quant", rows=4096, n=4096, group=None,

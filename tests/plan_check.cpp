@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <vector>
 
+#include "qrw_contig.h"
 #include "qrw_plan.h"
 
 using namespace qrw;
@@ -68,6 +69,47 @@ static void check_shape(int heads, int head_dim, int rope_dim, bool neox, int km
           head_dim, rope_dim);
 }
 
+// The contiguous lane mapping (qrw_contig.h) of the RoPE and tail-rotation
+// kernels: lane l owns granules l + 64 g, g < G.  Checks every granule is
+// owned once and in the row; a rotating granule's position in its span is the
+// lane's fixed position (so one table granule per lane is right) and its
+// table entries lie in the table row; the NeoX partner granule is lane
+// l ^ rope_dim/16 of the same step, in the same head's span at the partner
+// position; granules outside every span are never rotated.
+static int contig_checked = 0;
+static void check_contig(int heads, int head_dim, int rope_dim, int g_blocks) {
+  const int n = heads * head_dim;
+  if (g_blocks == 0) return;
+  ++contig_checked;
+  CHECK(n == 512 * g_blocks, "contig row %d is not 512*%d", n, g_blocks);
+  const int hg = head_dim / 8, hg_mask = hg - 1, s0 = (head_dim - rope_dim) / 8;
+  const int span_len = rope_dim / 8, xr = rope_dim / 16, half = rope_dim / 2;
+  std::vector<int> cover(n / 8, 0);
+  for (int lane = 0; lane < 64; ++lane) {
+    const int jl = contig_span_pos(lane, hg_mask, s0);
+    for (int g = 0; g < g_blocks; ++g) {
+      const int gi = 64 * g + lane;
+      CHECK(8 * gi + 8 <= n, "contig granule %d out of row %d", gi, n);
+      if (8 * gi + 8 <= n) cover[gi]++;
+      const int j = gi % hg;  // position inside the head
+      const bool in_span = j >= s0;
+      CHECK(contig_rotates(gi, hg_mask, s0) == in_span, "rotation test wrong at gi=%d", gi);
+      if (!in_span) continue;
+      CHECK(j - s0 == jl, "span position %d != lane's %d (H=%d D=%d R=%d lane=%d g=%d)", j - s0,
+            jl, heads, head_dim, rope_dim, lane, g);
+      CHECK(jl >= 0 && jl < span_len, "span position %d out of [0,%d)", jl, span_len);
+      // NeoX: table granule jl mod xr, 8 entries; interleaved: entries 4 jl .. 4 jl + 3
+      CHECK(8 * (jl % xr) + 8 <= half, "neox table granule out of the row");
+      CHECK(4 * jl + 4 <= half, "interleaved table entries out of the row");
+      const int partner = gi ^ xr;
+      CHECK(partner == 64 * g + (lane ^ xr), "neox partner not lane ^ xr in the same step");
+      CHECK(partner / hg == gi / hg && partner % hg >= s0 && partner % hg - s0 == (jl ^ xr),
+            "neox partner outside the head's span (gi=%d)", gi);
+    }
+  }
+  for (int k = 0; k < n / 8; ++k) CHECK(cover[k] == 1, "contig granule %d owned %d times", k, cover[k]);
+}
+
 int main() {
   // exhaustive: the largest item count over every accepted shape fits one
   // fused launch (64 lanes x 8 items)
@@ -105,6 +147,22 @@ int main() {
     int H = 1 + std::rand() % (Hmax < 40 ? Hmax : 40);
     check_shape(H, D, R, (k & 1) != 0, 8);
   }
+  // the contiguous mapping over every shape it accepts (RoPE) and the tail
+  // kernel's shapes (rope_dim < head_dim, up to 8 blocks), and its refusals
+  for (int D = 16; D <= 8192; D *= 2)
+    for (int R = 16; R <= D && R <= 512; R *= 2)
+      for (int H = 1; H * D <= 16384; ++H) {
+        const int g = rope_contig_blocks(H, D, R);
+        const bool want = R <= 256 && (H * D) % 512 == 0 &&
+                          ((H * D) / 512 == 1 || (H * D) / 512 == 2 || (H * D) / 512 == 4 ||
+                           (H * D) / 512 == 8 || (H * D) / 512 == 16);
+        CHECK((g != 0) == want, "rope_contig_blocks(%d,%d,%d) = %d", H, D, R, g);
+        check_contig(H, D, R, g);
+      }
+  CHECK(rope_contig_blocks(32, 192, 64) == 0 && rope_contig_blocks(4, 128, 24) == 0 &&
+            rope_contig_blocks(40, 128, 128) == 0,
+        "non-power-of-two shapes or rows must take the item kernel");
+  std::printf("contiguous mapping: %d shapes\n", contig_checked);
   if (fails) {
     std::printf("FAILED %d checks\n", fails);
     return 1;
