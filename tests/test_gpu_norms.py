@@ -139,6 +139,48 @@ def test_layernorm_whole_rows(dtype, rows, n):
         assert np.array_equal(host(qrw.layernorm_fwd(xt[r:r + 1], gt, bt, 1e-5))[0], got[r])
 
 
+# Whole rows of 64 * {3, 5, 6, 7, 10, 12, 14} granules (hidden sizes 1536 ...
+# 7168) have one-wave instances of their own; RMSNorm with the weight read at
+# output time (4 or more workgroups per CU) keeps the rounded-up instance, so
+# a row must come out the same alone (exact instance) and in a large batch.
+EXACT_WIDTHS = [1536, 2560, 3072, 3584, 5120, 6144, 7168]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("n", EXACT_WIDTHS)
+def test_norms_exact_width_rows(dtype, n):
+    rows = 37
+    st = _rms_case(rows, n, dtype, seed=n + 7)
+    assert st["within_2ulp_of_result"] >= 0.9999
+    _rms_case(rows, n, dtype, seed=n + 8, with_w=False)
+    x = synth.normal(n + 9, (rows, n), 0.5, 2.0, dtype)
+    g = synth.normal(n + 10, (n,), 1.0, 0.1, dtype)
+    b = synth.normal(n + 11, (n,), 0.0, 0.1, dtype)
+    xt, gt, bt = dev(x, dtype), dev(g, dtype), dev(b, dtype)
+    got = host(qrw.layernorm_fwd(xt, gt, bt, 1e-5))
+    st = assert_close16(got, oracle.layernorm(x, g, b, dtype, 1e-5), dtype,
+                        term_scale=layernorm_terms(x, g, b, dtype, 1e-5),
+                        what=f"layernorm {rows}x{n} {dtype}")
+    assert st["within_2ulp_of_result"] >= 0.9999
+    assert np.array_equal(host(qrw.layernorm_fwd(xt[5:6], gt, bt, 1e-5))[0], got[5])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rmsnorm_exact_width_batch_invariant(dtype):
+    rows, n = 4100, 5120  # over 4 workgroups per CU: the late-weight form
+    x = synth.normal(41, (rows, n), 0.0, 1.0, dtype)
+    w = synth.normal(42, (n,), 1.0, 0.1, dtype)
+    xt, wt = dev(x, dtype), dev(w, dtype)
+    got = host(qrw.rmsnorm_fwd(xt, wt, 1e-6))
+    st = assert_close16(got, oracle.rmsnorm(x, w, dtype, 1e-6), dtype,
+                        what=f"rmsnorm {rows}x{n} {dtype}")
+    assert st["within_2ulp_of_result"] >= 0.9999
+    for r in (0, 2049, rows - 1):
+        assert np.array_equal(host(qrw.rmsnorm_fwd(xt[r:r + 1], wt, 1e-6))[0], got[r])
+    part = host(qrw.rmsnorm_fwd(xt[:300], wt, 1e-6))
+    assert np.array_equal(part, got[:300])
+
+
 def test_layernorm_constant_row_gives_beta_and_in_place():
     dt = "bf16"
     n = 4096
