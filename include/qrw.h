@@ -73,9 +73,9 @@ enum qrw_status {
 /* Largest row length, in elements, of the RoPE, fused and quantisation calls
  * (8192). */
 #define QRW_MAX_ROW 8192
-/* Largest row of rmsnorm_fwd / layernorm_fwd kept in registers (65536); a
- * longer RMSNorm row takes two passes over x (s3.2.4), up to
- * QRW_MAX_ROW_SPLIT. */
+/* Largest row of rmsnorm_fwd / layernorm_fwd kept in registers (65536), and
+ * of act_quant_fp8_fwd; a longer RMSNorm row takes two passes over x
+ * (s3.2.4), up to QRW_MAX_ROW_SPLIT. */
 #define QRW_MAX_ROW_RESIDENT 65536
 #define QRW_MAX_ROW_SPLIT (1 << 26)
 
@@ -183,7 +183,10 @@ int rmsnorm_rope_fp8_rounded_fwd(const void* x, const void* weight, const void* 
  * x: [rows, n] with x_row_stride (elements); q: [rows, n] codes with
  * q_row_stride (bytes, a multiple of 8); scales: [rows, n / group] float,
  * packed, 4-byte aligned.  group is n, or one of 8, 16, 32, 64, 128, 256, 512
- * dividing n.  Requires n <= QRW_MAX_ROW.  Dequantisation is q * scale.
+ * dividing n.  Requires n <= QRW_MAX_ROW_RESIDENT; a row longer than
+ * QRW_MAX_ROW is taken by one workgroup (per token) or by waves on 4096- or
+ * 2048-channel segments (per group), and then rows <= 2^31 / 8.
+ * Dequantisation is q * scale.
  */
 int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, int64_t n,
                       int64_t group, int64_t x_row_stride, int64_t q_row_stride, int dtype,

@@ -246,8 +246,11 @@ int act_quant_fp8_fwd(const void* x, uint8_t* q, float* scales, int64_t rows, in
                       int64_t group, int64_t x_row_stride, int64_t q_row_stride, int dtype,
                       void* stream) {
   if (!is_16bit(dtype)) return QRW_ERR_DTYPE;
-  if (rows < 0 || n < 8 || n % 8 != 0 || n > QRW_MAX_ROW) return QRW_ERR_SHAPE;
+  if (rows < 0 || n < 8 || n % 8 != 0 || n > QRW_MAX_ROW_RESIDENT) return QRW_ERR_SHAPE;
   if (rows > (int64_t)0x7FFFFFFF * 4) return QRW_ERR_SHAPE;
+  // rows longer than QRW_MAX_ROW: one workgroup per row (per token), or up to
+  // 32 waves per row (per group)
+  if (n > QRW_MAX_ROW && rows > (int64_t)0x7FFFFFFF / 8) return QRW_ERR_SHAPE;
   const bool pow2_group = group >= 8 && group <= 512 && (group & (group - 1)) == 0;
   if (group != n && !(pow2_group && n % group == 0)) return QRW_ERR_SHAPE;
   if (x_row_stride < n || x_row_stride % 8 != 0) return QRW_ERR_STRIDE;

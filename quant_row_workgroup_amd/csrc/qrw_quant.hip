@@ -25,20 +25,31 @@
 
 namespace qrw {
 
-template <typename T, int GPL, bool FULL, int L>
+// SEG: rows longer than one wave holds (QRW_MAX_ROW) are cut into segments of
+// GPL * 64 granules (4096 or 2048 channels; with FULL every segment is whole,
+// else the last one is shorter), one wave per (row, segment); groups never
+// straddle a segment.  Otherwise a wave takes a whole row.
+
+template <typename T, int GPL, bool FULL, int L, bool SEG>
 __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t* x, uint8_t* q,
                                                                  float* scales, int64_t rows,
                                                                  int ng, int64_t xs, int64_t qs,
-                                                                 int64_t groups) {
-  // When a whole row has at most 64 groups (GPL <= L), lane j collects the
-  // scale of group j (from any lane of that group, by a lane permute) and the
-  // row's scales leave in one contiguous store instead of one store per group.
+                                                                 int64_t groups, int segs) {
+  // When a whole row (segment) has at most 64 groups (GPL <= L), lane j
+  // collects the scale of group j (from any lane of that group, by a lane
+  // permute) and the scales leave in one contiguous store instead of one
+  // store per group.
   constexpr bool kGather = FULL && GPL <= L;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint16_t* xr = x + row * xs;
-  uint8_t* qr = q + row * qs;
+  const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t row = SEG ? wave / segs : wave;
+  if (row >= rows) return;  // wave-uniform
+  const int seg = SEG ? (int)(wave - row * segs) : 0;
+  const int g0 = seg * GPL * kWave;  // first granule of the segment
+  const uint16_t* xr = x + row * xs + 8 * (int64_t)g0;
+  uint8_t* qr = q + row * qs + 8 * (int64_t)g0;
+  float* sr = scales + row * groups + g0 / L;
+  if (SEG) ng = min(ng - g0, GPL * kWave);  // granules in this segment
   u32x4 raw[GPL];
 #pragma unroll
   for (int g = 0; g < GPL; ++g) {
@@ -71,11 +82,11 @@ __global__ __launch_bounds__(kBlock) void act_quant_group_kernel(const uint16_t*
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
       st8_stream(qr + 8 * gi, fp8x8(v));
-      if (!kGather && (lane & (L - 1)) == 0) scales[row * groups + gi / L] = scale;
+      if (!kGather && (lane & (L - 1)) == 0) sr[gi / L] = scale;
     }
   }
   if constexpr (kGather) {
-    if (lane < GPL * (kWave / L)) scales[row * groups + lane] = mine;
+    if (lane < GPL * (kWave / L)) sr[lane] = mine;
   }
 }
 
@@ -123,22 +134,76 @@ __global__ __launch_bounds__(kBlock) void act_quant_token_kernel(const uint16_t*
   }
 }
 
+// One scale per row for rows longer than one wave holds: one workgroup of
+// kQuantBlockWaves waves per row, thread t owning granules t, t + 1024, ...
+// (GPT of them).  The row's amax is the maximum of the wave maxima, gathered
+// through LDS behind one barrier (a maximum is exact in any order, so the
+// scale is the one the one-wave kernel would form), then the same quotient.
+constexpr int kQuantBlockWaves = 16;
+
+template <typename T, int GPT, bool FULL>
+__global__ __launch_bounds__(kWave * kQuantBlockWaves) void act_quant_token_block_kernel(
+    const uint16_t* x, uint8_t* q, float* scales, int ng, int64_t xs, int64_t qs) {
+  constexpr int HT = kWave * kQuantBlockWaves;
+  __shared__ float slot[kQuantBlockWaves];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * xs;
+  uint8_t* qr = q + row * qs;
+  u32x4 raw[GPT];
+#pragma unroll
+  for (int g = 0; g < GPT; ++g) {
+    const int gi = g * HT + t;
+    raw[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (FULL || gi < ng) raw[g] = ld16_stream(xr + 8 * gi);
+  }
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < GPT; ++g) {
+    float v[8];
+    widen8<T>(raw[g], v);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      m[e >> 1] = fmaxf(m[e >> 1], fmaxf(fabsf(v[e]), fabsf(v[e + 1])));
+  }
+  const float wm = wave_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
+  if ((t & (kWave - 1)) == 0) slot[t >> 6] = wm;
+  __syncthreads();
+  float am = slot[0];
+#pragma unroll
+  for (int i = 1; i < kQuantBlockWaves; ++i) am = fmaxf(am, slot[i]);
+  const float scale = scale_e4m3(fmaxf(am, 1e-4f));
+  const float y = recip_rn(scale);
+  if (t == 0) scales[row] = scale;
+#pragma unroll
+  for (int g = 0; g < GPT; ++g) {
+    const int gi = g * HT + t;
+    if (FULL || gi < ng) {
+      float v[8];
+      widen8<T>(raw[g], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = div_rn(v[e], scale, y);
+      st8_stream(qr + 8 * gi, fp8x8(v));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launch
 namespace {
 
 int quant_gpl(int ng) { return ng <= 64 ? 1 : ng <= 128 ? 2 : ng <= 256 ? 4 : ng <= 512 ? 8 : 16; }
 
-template <typename T, int GPL, bool FULL>
+template <typename T, int GPL, bool FULL, bool SEG = false>
 void group_go(int lanes, dim3 grid, hipStream_t st, const uint16_t* x, uint8_t* q, float* sc,
-              int64_t rows, int ng, int64_t xs, int64_t qs, int64_t groups) {
+              int64_t rows, int ng, int64_t xs, int64_t qs, int64_t groups, int segs = 1) {
   switch (lanes) {
-    case 1: act_quant_group_kernel<T, GPL, FULL, 1><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    case 2: act_quant_group_kernel<T, GPL, FULL, 2><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    case 4: act_quant_group_kernel<T, GPL, FULL, 4><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    case 8: act_quant_group_kernel<T, GPL, FULL, 8><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    case 16: act_quant_group_kernel<T, GPL, FULL, 16><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    case 32: act_quant_group_kernel<T, GPL, FULL, 32><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
-    default: act_quant_group_kernel<T, GPL, FULL, 64><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups); break;
+    case 1: act_quant_group_kernel<T, GPL, FULL, 1, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    case 2: act_quant_group_kernel<T, GPL, FULL, 2, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    case 4: act_quant_group_kernel<T, GPL, FULL, 4, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    case 8: act_quant_group_kernel<T, GPL, FULL, 8, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    case 16: act_quant_group_kernel<T, GPL, FULL, 16, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    case 32: act_quant_group_kernel<T, GPL, FULL, 32, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
+    default: act_quant_group_kernel<T, GPL, FULL, 64, SEG><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs, groups, segs); break;
   }
 }
 
@@ -151,9 +216,50 @@ void quant_go(int64_t group, int64_t n, dim3 grid, hipStream_t st, const uint16_
     group_go<T, GPL, FULL>((int)(group / 8), grid, st, x, q, sc, rows, ng, xs, qs, n / group);
 }
 
+// Rows longer than one wave holds: per group, waves on 4096-channel segments;
+// per token, one workgroup per row.
+template <typename T>
+void quant_long(int64_t group, int64_t n, hipStream_t st, const uint16_t* x, uint8_t* q,
+                float* sc, int64_t rows, int64_t xs, int64_t qs) {
+  const int ng = (int)(n / 8);
+  if (group == n) {
+    const int gpt = (ng + kWave * kQuantBlockWaves - 1) / (kWave * kQuantBlockWaves);
+    const int g = gpt <= 2 ? 2 : gpt <= 4 ? 4 : 8;  // ng <= 8192: at most 8
+    const bool full = ng == g * kWave * kQuantBlockWaves;
+    const dim3 grid((unsigned)rows);
+    const dim3 block(kWave * kQuantBlockWaves);
+#define QRW_AQ_BLOCK(G)                                                                         \
+  if (full) act_quant_token_block_kernel<T, G, true><<<grid, block, 0, st>>>(x, q, sc, ng, xs, qs); \
+  else act_quant_token_block_kernel<T, G, false><<<grid, block, 0, st>>>(x, q, sc, ng, xs, qs);
+    if (g == 2) { QRW_AQ_BLOCK(2) }
+    else if (g == 4) { QRW_AQ_BLOCK(4) }
+    else { QRW_AQ_BLOCK(8) }
+#undef QRW_AQ_BLOCK
+    return;
+  }
+  // whole segments of 512 granules, else of 256 (e.g. rows of 14336 or 18432
+  // channels), else 512 with a shorter last one
+  const int gpl = ng % 512 == 0 ? 8 : ng % 256 == 0 ? 4 : 8;
+  const bool full = ng % (gpl * kWave) == 0;
+  const int segs = (ng + gpl * kWave - 1) / (gpl * kWave);
+  const int64_t waves = rows * segs;
+  const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int lanes = (int)(group / 8);
+  if (gpl == 4)
+    group_go<T, 4, true, true>(lanes, grid, st, x, q, sc, rows, ng, xs, qs, n / group, segs);
+  else if (full)
+    group_go<T, 8, true, true>(lanes, grid, st, x, q, sc, rows, ng, xs, qs, n / group, segs);
+  else
+    group_go<T, 8, false, true>(lanes, grid, st, x, q, sc, rows, ng, xs, qs, n / group, segs);
+}
+
 template <typename T>
 void quant_dispatch(int64_t group, int64_t n, dim3 grid, hipStream_t st, const uint16_t* x,
                     uint8_t* q, float* sc, int64_t rows, int64_t xs, int64_t qs) {
+  if (n > 8 * kOneWaveGranules) {
+    quant_long<T>(group, n, st, x, q, sc, rows, xs, qs);
+    return;
+  }
   const int ng = (int)(n / 8);
   const int gpl = quant_gpl(ng);
   const bool full = ng == gpl * kWave;

@@ -210,6 +210,8 @@ def aq(**kw):
     (dict(dtype=F32), DTYPE),
     (dict(group=96), SHAPE), (dict(group=1024), SHAPE), (dict(group=4), SHAPE),
     (dict(n=1000, xs=1000, qs=1000, group=128), SHAPE), (dict(n=8200), SHAPE),
+    (dict(n=65544, xs=65544, qs=65544, group=8), SHAPE),          # longer than 65536
+    (dict(n=16384, xs=16384, qs=16384, rows=0x7FFFFFFF // 8 + 1), SHAPE),  # long rows: grid
     (dict(xs=4088), STRIDE), (dict(qs=4100), STRIDE),
     (dict(q=ctypes.c_void_p((5 << 32) + 8)), ALIGN), (dict(sc=ctypes.c_void_p((6 << 32) + 2)), ALIGN),
     (dict(sc=ctypes.c_void_p(Q_ADDR + 64)), ALIAS),      # scales inside the codes

@@ -43,6 +43,40 @@ def test_act_quant_shapes(dt, rows, n, group):
     _check(x, dt, group, f"act_quant {rows}x{n}/{group}")
 
 
+# Rows longer than one wave holds (8192 channels, up to 65536): per group,
+# waves on whole 4096- or 2048-channel segments, or 4096-channel segments with
+# a shorter last one; per token, one workgroup of 16 waves per row.
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("rows,n,group", [
+    (3, 8200, None), (3, 8200, 8), (5, 14336, 128), (5, 14336, None), (4, 18432, 128),
+    (4, 18432, None), (3, 16384, 128), (3, 16384, None), (2, 65536, 512), (2, 65536, None),
+    (3, 12296, 8), (7, 20480, 64), (2, 10240, 32),
+])
+def test_act_quant_long_rows(dt, rows, n, group):
+    x = synth.normal(rows * 11 + n + (group or 0), (rows, n), 0.0, 2.0, dt, outlier_frac=0.02,
+                     outlier_mul=20.0)
+    q, sc, _ = _check(x, dt, group, f"act_quant {rows}x{n}/{group}")
+    q1, s1 = qrw.act_quant_fp8_fwd(dev(x[rows - 1:], dt), group)
+    assert np.array_equal(host(q1)[0], q[rows - 1])
+    assert np.array_equal(host(s1)[0], sc[rows - 1])
+
+
+@pytest.mark.parametrize("group", [128, None])
+def test_act_quant_long_rows_strided(group):
+    n, rows = 14336, 6
+    x = synth.normal(77 + (group or 0), (rows, n), 0.0, 3.0, "bf16")
+    x[2, 1024:1152] = 0
+    xw = np.zeros((rows, n + 64), dtype=np.uint16)
+    xw[:, :n] = x
+    qbuf = torch.full((rows, n + 16), 0x5A, dtype=torch.uint8, device="cuda")
+    q, sc = qrw.act_quant_fp8_fwd(dev(xw, "bf16")[:, :n], group, q=qbuf[:, :n])
+    qa = host(qbuf)
+    assert np.all(qa[:, n:] == 0x5A)
+    wq, wsc = oracle.act_quant_fp8(x, "bf16", group)
+    assert_codes(qa[:, :n], wq)
+    assert_scales(host(sc), wsc)
+
+
 def test_act_quant_zero_groups_strides_determinism_batch_invariance():
     n = 4096
     x = synth.normal(40, (64, n), 0.0, 3.0, "bf16")
