@@ -87,8 +87,8 @@ __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* 
   }
   const float ss = wave_sum(tree8(acc));
   if (TL) t1 = realtime();
-  // n = 512 * G is a power of two: the mean is an exact scaling
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / (512 * G)) + eps);
+  // the mean: ss / n, n = 512 * G (for a power of two an exact scaling)
+  const float rstd = 1.0f / sqrtf(ss / (float)(512 * G) + eps);
 
   float v[G][8];
   float m[4] = {0.f, 0.f, 0.f, 0.f};
@@ -221,6 +221,16 @@ hipError_t contig_launch_xd(const uint16_t* x, const uint16_t* w, const void* c,
   }
 }
 
+// Rows of 3, 5, 6 or 7 blocks of 512 channels (e.g. 24 heads of 128): heads of
+// 64 or 128 only (contig_blocks), which keeps the instance count down.
+template <typename T, typename CS, bool NEOX, int G>
+hipError_t contig_launch_xd48(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                              uint8_t* q, float* sc, int64_t tokens, int64_t head_dim, int64_t xs,
+                              int64_t qs, float eps, bool mid, hipStream_t st) {
+  if (head_dim == 64) return contig_launch<T, CS, NEOX, G, 4>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+  return contig_launch<T, CS, NEOX, G, 8>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+}
+
 template <typename T, typename CS, bool NEOX>
 hipError_t contig_launch_g(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
                            uint8_t* q, float* sc, int64_t tokens, int64_t head_dim, int g,
@@ -228,7 +238,11 @@ hipError_t contig_launch_g(const uint16_t* x, const uint16_t* w, const void* c, 
   switch (g) {
     case 1: return contig_launch_xd<T, CS, NEOX, 1>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     case 2: return contig_launch_xd<T, CS, NEOX, 2>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 3: return contig_launch_xd48<T, CS, NEOX, 3>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     case 4: return contig_launch_xd<T, CS, NEOX, 4>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 5: return contig_launch_xd48<T, CS, NEOX, 5>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 6: return contig_launch_xd48<T, CS, NEOX, 6>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 7: return contig_launch_xd48<T, CS, NEOX, 7>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     default: return contig_launch_xd<T, CS, NEOX, 8>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
   }
 }

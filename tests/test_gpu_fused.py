@@ -55,7 +55,10 @@ def test_fused_pages_reading_one_head_tail_rotation():
                                    ("f16", "f16")])
 @pytest.mark.parametrize("T,H,D,R", [(64, 32, 128, 128), (16, 8, 128, 64), (9, 3, 48, 32),
                                      (8, 5, 96, 96), (5, 64, 128, 128), (7, 1, 1000, 16),
-                                     (3, 2, 24, 16), (1, 1, 16, 16), (12, 1, 8192, 512)])
+                                     (3, 2, 24, 16), (1, 1, 16, 16), (12, 1, 8192, 512),
+                                     # 3, 5, 6, 7 blocks of 512 channels, heads of 128 or 64
+                                     (11, 12, 128, 128), (10, 20, 128, 128), (9, 48, 64, 64),
+                                     (13, 28, 128, 128)])
 def test_fused_shapes(neox, dt, cs, T, H, D, R):
     x = synth.normal(T + H + D + R, (T, H * D), 0.0, 3.0, dt, outlier_frac=0.01,
                      outlier_mul=10.0)
