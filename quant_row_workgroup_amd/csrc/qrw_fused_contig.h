@@ -39,28 +39,46 @@ constexpr int kTimelineSlots = 4;
 
 __device__ __forceinline__ uint64_t realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID, bool TL>
+// PAIR: the token's row is 2 * G blocks of 512 channels, and two waves of the
+// workgroup take one half each (half = 0 or 1): they exchange the sum of
+// squares and the amax through pair_slot (4 floats: [half] sums, [2 + half]
+// maxima) behind one workgroup barrier each, so every wave of the workgroup
+// must reach both barriers -- a wave of a token past the end passes live =
+// false and touches no memory.  The sum is slot[0] + slot[1] in that order.
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID, bool TL,
+          bool PAIR = false>
 __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* __restrict__ w,
                                              const void* cosv, const void* sinv, uint8_t* q,
                                              float* scales, int64_t t, int64_t xs, int64_t qs,
-                                             float eps, int lane, uint64_t* stamps) {
+                                             float eps, int lane, uint64_t* stamps,
+                                             int half = 0, bool live = true,
+                                             float* pair_slot = nullptr) {
   uint64_t t0 = 0, t1 = 0, t2 = 0;
   if (TL) t0 = realtime();
-  const uint16_t* xr = x + t * xs;
-  uint8_t* qr = q + t * qs;
+  const int64_t c0 = PAIR ? (int64_t)half * (512 * G) : 0;  // first channel of this wave's part
+  const uint16_t* xr = x + t * xs + c0;
+  uint8_t* qr = q + t * qs + c0;
+  if (PAIR && HAS_W) w += c0;
   const int j = lane & (2 * XD - 1);  // granule index inside the head
 
   u32x4 r[G], wr[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
+  for (int g = 0; g < G; ++g) {
+    r[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (!PAIR || live) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
+  }
   if (HAS_W) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) wr[g] = ld16(w + 8 * (kWave * g + lane));
+    for (int g = 0; g < G; ++g) {
+      wr[g] = (u32x4){0u, 0u, 0u, 0u};
+      if (!PAIR || live) wr[g] = ld16(w + 8 * (kWave * g + lane));
+    }
   }
   float c[8], sn[8];
-  // a table row holds head_dim / 2 = 8 * XD entries
-  const char* crow = table_row<CS>(cosv, t, 8 * XD);
-  const char* srow = table_row<CS>(sinv, t, 8 * XD);
+  // a table row holds head_dim / 2 = 8 * XD entries (a token past the end
+  // reads token 0's row, which exists: tokens >= 1 whenever a kernel runs)
+  const char* crow = table_row<CS>(cosv, PAIR && !live ? 0 : t, 8 * XD);
+  const char* srow = table_row<CS>(sinv, PAIR && !live ? 0 : t, 8 * XD);
   if (NEOX) {
     Table8<CS>::load(crow, j & (XD - 1), c);
     Table8<CS>::load(srow, j & (XD - 1), sn);
@@ -85,10 +103,16 @@ __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* 
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[(2 * g + k) & 7] = sumsq2(T{}, r[g][k], acc[(2 * g + k) & 7]);
   }
-  const float ss = wave_sum(tree8(acc));
+  float ss = wave_sum(tree8(acc));
+  if constexpr (PAIR) {
+    if (lane == 0) pair_slot[half] = ss;
+    __syncthreads();
+    ss = pair_slot[0] + pair_slot[1];
+  }
   if (TL) t1 = realtime();
-  // the mean: ss / n, n = 512 * G (for a power of two an exact scaling)
-  const float rstd = 1.0f / sqrtf(ss / (float)(512 * G) + eps);
+  // the mean: ss / n, n = 512 * G (1024 * G in pairs; for a power of two an
+  // exact scaling)
+  const float rstd = 1.0f / sqrtf(ss / (float)((PAIR ? 1024 : 512) * G) + eps);
 
   float v[G][8];
   float m[4] = {0.f, 0.f, 0.f, 0.f};
@@ -125,11 +149,17 @@ __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* 
       m[(e >> 1) & 3] = fmaxf(fmaxf(m[(e >> 1) & 3], fabsf(v[g][e])), fabsf(v[g][e + 1]));
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-  const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
+  float amax_w = wave_max(amax);
+  if constexpr (PAIR) {
+    if (lane == 0) pair_slot[2 + half] = amax_w;
+    __syncthreads();
+    amax_w = fmaxf(pair_slot[2], pair_slot[3]);
+  }
+  const float amax_z = MID ? amax_w : amax_w * rstd;
   const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float kq = rstd / scale;
   const float inv = recip_rn(scale);
-  if (lane == 0) scales[t] = scale;
+  if (lane == 0 && (!PAIR || (live && half == 0))) scales[t] = scale;
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -139,6 +169,7 @@ __device__ __forceinline__ void contig_token(const uint16_t* x, const uint16_t* 
     // codes: plain stores for the exact form, non-temporal for the staged one
     // (each measured faster on 4096 x 4096 bf16: 10.97 against 11.45 us, and
     // 12.29 against 12.71 us)
+    if (PAIR && !live) continue;
     if (MID)
       st8_stream(qr + 8 * (kWave * g + lane), fp8x8(a));
     else
@@ -174,6 +205,58 @@ __global__ __launch_bounds__(kWave * kContigRows) void rmsnorm_rope_fp8_contig_k
   if (t >= tokens) return;
   contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false>(x, w, cosv, sinv, q, scales, t, xs,
                                                        PACKED ? xs : qs, eps, lane, nullptr);
+}
+
+// Rows of 2 * G blocks (G = 5, 6, 7, 8: 5120 to 8192 channels), heads of 64 or
+// 128: two waves per token, kPairRows tokens per workgroup.  Two tokens (4
+// waves) measured fastest of 1, 2 and 4 (MI355X, 4096 tokens bf16: 48 heads of
+// 128 18.3 against 22.6 us at 4, 64 heads 20.9 against 22.1 us; every barrier
+// waits for all the workgroup's waves), and capping registers at 4 waves per
+// SIMD made the 6-block form spill and run slower.
+constexpr int kPairRows = 2;
+
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XD, bool MID, bool PACKED>
+__global__ __launch_bounds__(2 * kWave * kPairRows) void rmsnorm_rope_fp8_pair_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
+    uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, float eps) {
+  __shared__ float slot[kPairRows][4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int k = wv >> 1;  // token slot in the workgroup
+  const int64_t t = (int64_t)blockIdx.x * kPairRows + k;
+  // no early return: both halves of every slot reach the two barriers
+  contig_token<T, CS, NEOX, G, HAS_W, XD, MID, false, true>(
+      x, w, cosv, sinv, q, scales, t, xs, PACKED ? xs : qs, eps, lane, nullptr, wv & 1,
+      t < tokens, slot[k]);
+}
+
+template <typename T, typename CS, bool NEOX, int G, int XD>
+hipError_t pair_launch(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                       uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs, float eps,
+                       bool mid, hipStream_t st) {
+  const dim3 grid((unsigned)((tokens + kPairRows - 1) / kPairRows));
+  const dim3 block(2 * kWave * kPairRows);
+#define QRW_PAIR(HW, M, P) \
+  rmsnorm_rope_fp8_pair_kernel<T, CS, NEOX, G, HW, XD, M, P><<<grid, block, 0, st>>>(x, w, c, s, q, sc, tokens, xs, qs, eps)
+  if (mid) {
+    if (w && qs == xs) QRW_PAIR(true, true, true);
+    else if (w) QRW_PAIR(true, true, false);
+    else QRW_PAIR(false, true, false);
+  } else {
+    if (w && qs == xs) QRW_PAIR(true, false, true);
+    else if (w) QRW_PAIR(true, false, false);
+    else QRW_PAIR(false, false, false);
+  }
+#undef QRW_PAIR
+  return hipGetLastError();
+}
+
+template <typename T, typename CS, bool NEOX, int G>
+hipError_t pair_launch_xd(const uint16_t* x, const uint16_t* w, const void* c, const void* s,
+                          uint8_t* q, float* sc, int64_t tokens, int64_t head_dim, int64_t xs,
+                          int64_t qs, float eps, bool mid, hipStream_t st) {
+  if (head_dim == 64) return pair_launch<T, CS, NEOX, G, 4>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
+  return pair_launch<T, CS, NEOX, G, 8>(x, w, c, s, q, sc, tokens, xs, qs, eps, mid, st);
 }
 
 template <typename T, typename CS, bool NEOX, int G, int XD>
@@ -243,6 +326,11 @@ hipError_t contig_launch_g(const uint16_t* x, const uint16_t* w, const void* c, 
     case 5: return contig_launch_xd48<T, CS, NEOX, 5>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     case 6: return contig_launch_xd48<T, CS, NEOX, 6>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     case 7: return contig_launch_xd48<T, CS, NEOX, 7>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    // two waves per token (pair_launch: heads of 64 or 128)
+    case 10: return pair_launch_xd<T, CS, NEOX, 5>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 12: return pair_launch_xd<T, CS, NEOX, 6>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 14: return pair_launch_xd<T, CS, NEOX, 7>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
+    case 16: return pair_launch_xd<T, CS, NEOX, 8>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
     default: return contig_launch_xd<T, CS, NEOX, 8>(x, w, c, s, q, sc, tokens, head_dim, xs, qs, eps, mid, st);
   }
 }

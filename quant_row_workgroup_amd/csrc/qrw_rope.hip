@@ -472,7 +472,8 @@ bool dense_ok(const RowPlan& pl, int kk) {
 
 // Granules per lane of the contiguous path, or 0 if it does not apply: whole
 // heads rotate, head_dim / 16 is 1, 2, 4, 8 or 16, and the row is 1, 2, 4 or
-// 8 blocks of 512 channels -- or 3, 5, 6 or 7 blocks of heads of 64 or 128.
+// 8 blocks of 512 channels -- or 3, 5, 6, 7 blocks of heads of 64 or 128, or
+// 10, 12, 14, 16 blocks of them (two waves per token).
 int contig_blocks(const RowPlan& pl) {
   const int xd = pl.head_dim / 16;
   const bool xd_ok = pl.head_dim % 16 == 0 && (xd == 1 || xd == 2 || xd == 4 || xd == 8 || xd == 16);
@@ -480,7 +481,8 @@ int contig_blocks(const RowPlan& pl) {
   const int g = pl.n / 512;
   if (g == 1 || g == 2 || g == 4 || g == 8) return g;
   const bool odd_ok = pl.head_dim == 64 || pl.head_dim == 128;
-  return odd_ok && (g == 3 || g == 5 || g == 6 || g == 7) ? g : 0;
+  return odd_ok && (g == 3 || g == 5 || g == 6 || g == 7 || g == 10 || g == 12 || g == 14 ||
+                    g == 16) ? g : 0;
 }
 
 template <typename T, typename CS, bool NEOX>

@@ -58,7 +58,10 @@ def test_fused_pages_reading_one_head_tail_rotation():
                                      (3, 2, 24, 16), (1, 1, 16, 16), (12, 1, 8192, 512),
                                      # 3, 5, 6, 7 blocks of 512 channels, heads of 128 or 64
                                      (11, 12, 128, 128), (10, 20, 128, 128), (9, 48, 64, 64),
-                                     (13, 28, 128, 128)])
+                                     (13, 28, 128, 128),
+                                     # 10, 12, 14, 16 blocks: two waves per token
+                                     (13, 40, 128, 128), (6, 48, 128, 128), (5, 56, 128, 128),
+                                     (9, 64, 128, 128), (7, 80, 64, 64), (3, 128, 64, 64)])
 def test_fused_shapes(neox, dt, cs, T, H, D, R):
     x = synth.normal(T + H + D + R, (T, H * D), 0.0, 3.0, dt, outlier_frac=0.01,
                      outlier_mul=10.0)
@@ -106,6 +109,31 @@ def test_fused_strided_deterministic_batch_invariant():
         assert np.array_equal(host(qr)[0], q1[r, :n]) and host(sr)[0] == s1[r]
     qe, se = qrw.rmsnorm_rope_fp8_fwd(xt[:0], wt, ct[:0], st[:0], 32, 128)
     assert qe.shape == (0, n) and se.shape == (0,)
+
+
+# rows of 10 to 16 blocks of 512 channels: two waves per token exchanging the
+# row's sum and amax through LDS; a token count that leaves idle waves in the
+# last workgroup, strides, and a token alone against the batch
+@pytest.mark.parametrize("H,D", [(64, 128), (40, 128), (112, 64)])
+def test_fused_pair_rows_strided_batch_invariant(H, D):
+    T, n = 131, H * D
+    x = synth.normal(H + 5, (T, n), 0.0, 3.0, "bf16", outlier_frac=0.01, outlier_mul=10.0)
+    w = synth.normal(H + 6, (n,), 1.0, 0.1, "bf16")
+    c, s = synth.rope_table(T, D, "bf16", base=5.0)
+    xw = np.zeros((T, n + 64), dtype=np.uint16)
+    xw[:, :n] = x
+    xt = dev(xw, "bf16")[:, :n]
+    wt, ct, st = dev(w, "bf16"), dev(c, "bf16"), dev(s, "bf16")
+    qbuf = torch.full((T, n + 32), 0xAB, dtype=torch.uint8, device="cuda")
+    _, s1 = qrw.rmsnorm_rope_fp8_fwd(xt, wt, ct, st, H, D, q=qbuf[:, :n])
+    q1, s1 = host(qbuf), host(s1)
+    assert np.all(q1[:, n:] == 0xAB)
+    wq, wsc = oracle.rmsnorm_rope_fp8(x, w, c, s, H, D, D, "bf16", "bf16", True, 1e-6)
+    assert_codes(q1[:, :n], wq)
+    assert_scales(s1, wsc)
+    for r in (0, 77, T - 1):
+        qr, sr = qrw.rmsnorm_rope_fp8_fwd(xt[r:r + 1], wt, ct[r:r + 1], st[r:r + 1], H, D)
+        assert np.array_equal(host(qr)[0], q1[r, :n]) and host(sr)[0] == s1[r]
 
 
 # heads rotating only their tail span, contiguous layout (rope_dim < head_dim, powers of two)
