@@ -253,6 +253,44 @@ void quant_long(int64_t group, int64_t n, hipStream_t st, const uint16_t* x, uin
     group_go<T, 8, false, true>(lanes, grid, st, x, q, sc, rows, ng, xs, qs, n / group, segs);
 }
 
+// Whole rows of 64 * e granules, e not a power of two (hidden sizes 1536 ...
+// 7168): per token, one-wave instances of their own (e = 3, 5, 6, 7, 10, 12,
+// 14); per group, when the row splits into segments of 128, 256 or 512
+// granules, waves on those segments.  Measured on MI355X (bf16, 1024 and
+// 4096 rows, against the rounded-up one-wave instance; outputs identical):
+// per token 1.01-1.18x; per 128-group 1.02-1.29x at 3072, 5120, 6144 and
+// 7168 channels, but 0.86-1.07x with 64-granule segments (1536, 2560, 3584),
+// which keep the one-wave kernel.  Returns false when neither applies.
+template <typename T>
+bool quant_exact(int64_t group, int ng, dim3 grid, hipStream_t st, const uint16_t* x, uint8_t* q,
+                 float* sc, int64_t rows, int64_t xs, int64_t qs) {
+  if (ng % kWave != 0) return false;
+  const int e = ng / kWave;
+  if ((e & (e - 1)) == 0) return false;  // a power of two: the regular instances
+  if (group == 8 * (int64_t)ng) {
+    switch (e) {
+      case 3: act_quant_token_kernel<T, 3, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 5: act_quant_token_kernel<T, 5, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 6: act_quant_token_kernel<T, 6, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 7: act_quant_token_kernel<T, 7, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 10: act_quant_token_kernel<T, 10, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 12: act_quant_token_kernel<T, 12, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      case 14: act_quant_token_kernel<T, 14, true><<<grid, kBlock, 0, st>>>(x, q, sc, rows, ng, xs, qs); return true;
+      default: return false;
+    }
+  }
+  const int gpl = ng % 512 == 0 ? 8 : ng % 256 == 0 ? 4 : ng % 128 == 0 ? 2 : 0;
+  if (gpl == 0) return false;
+  const int segs = ng / (gpl * kWave);
+  const dim3 g2((unsigned)((rows * segs + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int lanes = (int)(group / 8);
+  const int64_t groups = 8 * (int64_t)ng / group;
+  if (gpl == 8) group_go<T, 8, true, true>(lanes, g2, st, x, q, sc, rows, ng, xs, qs, groups, segs);
+  else if (gpl == 4) group_go<T, 4, true, true>(lanes, g2, st, x, q, sc, rows, ng, xs, qs, groups, segs);
+  else group_go<T, 2, true, true>(lanes, g2, st, x, q, sc, rows, ng, xs, qs, groups, segs);
+  return true;
+}
+
 template <typename T>
 void quant_dispatch(int64_t group, int64_t n, dim3 grid, hipStream_t st, const uint16_t* x,
                     uint8_t* q, float* sc, int64_t rows, int64_t xs, int64_t qs) {
@@ -261,6 +299,7 @@ void quant_dispatch(int64_t group, int64_t n, dim3 grid, hipStream_t st, const u
     return;
   }
   const int ng = (int)(n / 8);
+  if (quant_exact<T>(group, ng, grid, st, x, q, sc, rows, xs, qs)) return;
   const int gpl = quant_gpl(ng);
   const bool full = ng == gpl * kWave;
   switch (gpl) {

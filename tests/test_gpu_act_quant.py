@@ -43,6 +43,21 @@ def test_act_quant_shapes(dt, rows, n, group):
     _check(x, dt, group, f"act_quant {rows}x{n}/{group}")
 
 
+# Whole rows of 64 * e granules, e not a power of two: per token, one-wave
+# instances of their own; per group, waves on 128-, 256- or 512-granule
+# segments when the row splits into them (else the one-wave kernel).
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("n", [1536, 2560, 3072, 3584, 5120, 6144, 7168])
+@pytest.mark.parametrize("group", [None, 128, 32])
+def test_act_quant_exact_widths(dt, n, group):
+    rows = 37
+    x = synth.normal(rows * 13 + n + (group or 0), (rows, n), 0.0, 2.0, dt, outlier_frac=0.02,
+                     outlier_mul=20.0)
+    q, sc, _ = _check(x, dt, group, f"act_quant {rows}x{n}/{group}")
+    q1, s1 = qrw.act_quant_fp8_fwd(dev(x[7:8], dt), group)
+    assert np.array_equal(host(q1)[0], q[7]) and np.array_equal(host(s1)[0], sc[7])
+
+
 # Rows longer than one wave holds (8192 channels, up to 65536): per group,
 # waves on whole 4096- or 2048-channel segments, or 4096-channel segments with
 # a shorter last one; per token, one workgroup of 16 waves per row.
