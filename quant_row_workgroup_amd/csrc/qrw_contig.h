@@ -42,15 +42,20 @@ QRW_CHD bool contig_rotates(int gi, int hg_mask, int s0) { return (gi & hg_mask)
 
 // Granule blocks per lane (G) for the contiguous RoPE path, or 0 when it does
 // not apply: head_dim and rope_dim powers of two with 16 <= rope_dim <=
-// min(head_dim, 256), and a row of 512 * G channels, G in {1, 2, 4, 8, 16}.
-QRW_CHD int rope_contig_blocks(int64_t heads, int64_t head_dim, int64_t rope_dim) {
+// min(head_dim, 256), and a row of 512 * G channels, G in {1, 2, 4, 8, 16};
+// or G in {3, 5, 6, 7, 10, 12, 14} for heads of 64 or 128, interleaved, or
+// NeoX rotating whole heads.
+QRW_CHD int rope_contig_blocks(int64_t heads, int64_t head_dim, int64_t rope_dim, bool neox) {
   const bool p2 = head_dim > 0 && (head_dim & (head_dim - 1)) == 0 && rope_dim > 0 &&
                   (rope_dim & (rope_dim - 1)) == 0;
   if (!p2 || rope_dim < 16 || rope_dim > head_dim || rope_dim > 256 || heads < 1) return 0;
   const int64_t n = heads * head_dim;
   if (n % 512 != 0) return 0;
   const int64_t g = n / 512;
-  return (g == 1 || g == 2 || g == 4 || g == 8 || g == 16) ? (int)g : 0;
+  if (g == 1 || g == 2 || g == 4 || g == 8 || g == 16) return (int)g;
+  const bool odd_ok = (head_dim == 64 || head_dim == 128) && (!neox || rope_dim == head_dim);
+  const bool odd_g = g == 3 || g == 5 || g == 6 || g == 7 || g == 10 || g == 12 || g == 14;
+  return odd_ok && odd_g ? (int)g : 0;
 }
 
 }  // namespace qrw

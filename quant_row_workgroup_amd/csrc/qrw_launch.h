@@ -59,8 +59,9 @@ hipError_t launch_rmsnorm_rope_fp8_contig_bf16(const uint16_t* x, const uint16_t
 bool fused_tail_ok(int64_t heads, int64_t head_dim, int64_t rope_dim);
 // RoPE in the contiguous lane mapping (qrw_rope_contig.hip): head_dim and
 // rope_dim powers of two, 16 <= rope_dim <= min(head_dim, 256), and the row
-// is 1, 2, 4, 8 or 16 blocks of 512 channels.
-bool rope_contig_ok(int64_t heads, int64_t head_dim, int64_t rope_dim);
+// is 1, 2, 4, 8 or 16 blocks of 512 channels (or 3, 5, 6, 7, 10, 12, 14 for
+// heads of 64 or 128; NeoX rotating whole heads).
+bool rope_contig_ok(int64_t heads, int64_t head_dim, int64_t rope_dim, bool neox);
 hipError_t launch_rope_contig(const void* x, const void* cos, const void* sin, void* y,
                               int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_dim,
                               int64_t xs, int64_t ys, int dtype, int cs_dtype, bool neox,

@@ -534,7 +534,7 @@ int items_per_lane(int n_items, int kmax) {
 hipError_t launch_rope(const void* x, const void* cos, const void* sin, void* y, int64_t tokens,
                        int64_t heads, int64_t head_dim, int64_t rope_dim, int64_t xs,
                        int64_t ys, int dtype, int cs_dtype, bool neox, hipStream_t stream) {
-  if (rope_contig_ok(heads, head_dim, rope_dim))
+  if (rope_contig_ok(heads, head_dim, rope_dim, neox))
     return launch_rope_contig(x, cos, sin, y, tokens, heads, head_dim, rope_dim, xs, ys, dtype,
                               cs_dtype, neox, stream);
   const RowPlan pl = make_plan(heads, head_dim, rope_dim);

@@ -128,13 +128,32 @@ void rc_xr(int xr, const RopeArgs& a) {
   }
 }
 
+// The other block counts: heads of 64 or 128 (NeoX: whole heads, rope_dim / 16
+// = 4 or 8), which keeps the instance count down.
+template <typename T, typename CS, bool NEOX, int G>
+void rc_xr48(int xr, const RopeArgs& a) {
+  if constexpr (!NEOX) {
+    rc_launch<T, CS, NEOX, G, 1>(a);
+  } else {
+    if (xr == 4) rc_launch<T, CS, NEOX, G, 4>(a);
+    else rc_launch<T, CS, NEOX, G, 8>(a);
+  }
+}
+
 template <typename T, typename CS, bool NEOX>
 void rc_g(int g, int xr, const RopeArgs& a) {
   switch (g) {
     case 1: rc_xr<T, CS, NEOX, 1>(xr, a); break;
     case 2: rc_xr<T, CS, NEOX, 2>(xr, a); break;
+    case 3: rc_xr48<T, CS, NEOX, 3>(xr, a); break;
     case 4: rc_xr<T, CS, NEOX, 4>(xr, a); break;
+    case 5: rc_xr48<T, CS, NEOX, 5>(xr, a); break;
+    case 6: rc_xr48<T, CS, NEOX, 6>(xr, a); break;
+    case 7: rc_xr48<T, CS, NEOX, 7>(xr, a); break;
     case 8: rc_xr<T, CS, NEOX, 8>(xr, a); break;
+    case 10: rc_xr48<T, CS, NEOX, 10>(xr, a); break;
+    case 12: rc_xr48<T, CS, NEOX, 12>(xr, a); break;
+    case 14: rc_xr48<T, CS, NEOX, 14>(xr, a); break;
     default: rc_xr<T, CS, NEOX, 16>(xr, a); break;
   }
 }
@@ -147,15 +166,15 @@ void rc_neox(bool neox, int g, int xr, const RopeArgs& a) {
 
 }  // namespace
 
-bool rope_contig_ok(int64_t heads, int64_t head_dim, int64_t rope_dim) {
-  return rope_contig_blocks(heads, head_dim, rope_dim) != 0;
+bool rope_contig_ok(int64_t heads, int64_t head_dim, int64_t rope_dim, bool neox) {
+  return rope_contig_blocks(heads, head_dim, rope_dim, neox) != 0;
 }
 
 hipError_t launch_rope_contig(const void* x, const void* cos, const void* sin, void* y,
                               int64_t tokens, int64_t heads, int64_t head_dim, int64_t rope_dim,
                               int64_t xs, int64_t ys, int dtype, int cs_dtype, bool neox,
                               hipStream_t stream) {
-  const int g = rope_contig_blocks(heads, head_dim, rope_dim);
+  const int g = rope_contig_blocks(heads, head_dim, rope_dim, neox);
   if (g == 0) return hipErrorInvalidValue;  // callers check rope_contig_ok first
   RopeArgs a;
   a.grid = dim3((unsigned)((tokens + kRowsPerBlock - 1) / kRowsPerBlock));

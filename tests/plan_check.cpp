@@ -149,19 +149,27 @@ int main() {
   }
   // the contiguous mapping over every shape it accepts (RoPE) and the tail
   // kernel's shapes (rope_dim < head_dim, up to 8 blocks), and its refusals
-  for (int D = 16; D <= 8192; D *= 2)
-    for (int R = 16; R <= D && R <= 512; R *= 2)
-      for (int H = 1; H * D <= 16384; ++H) {
-        const int g = rope_contig_blocks(H, D, R);
-        const bool want = R <= 256 && (H * D) % 512 == 0 &&
-                          ((H * D) / 512 == 1 || (H * D) / 512 == 2 || (H * D) / 512 == 4 ||
-                           (H * D) / 512 == 8 || (H * D) / 512 == 16);
-        CHECK((g != 0) == want, "rope_contig_blocks(%d,%d,%d) = %d", H, D, R, g);
-        check_contig(H, D, R, g);
-      }
-  CHECK(rope_contig_blocks(32, 192, 64) == 0 && rope_contig_blocks(4, 128, 24) == 0 &&
-            rope_contig_blocks(40, 128, 128) == 0,
-        "non-power-of-two shapes or rows must take the item kernel");
+  for (int nx = 0; nx < 2; ++nx)
+    for (int D = 16; D <= 8192; D *= 2)
+      for (int R = 16; R <= D && R <= 512; R *= 2)
+        for (int H = 1; H * D <= 16384; ++H) {
+          const bool neox = nx == 1;
+          const int g = rope_contig_blocks(H, D, R, neox);
+          const int blocks = (H * D) % 512 == 0 ? (H * D) / 512 : 0;
+          const bool p2 = blocks == 1 || blocks == 2 || blocks == 4 || blocks == 8 || blocks == 16;
+          const bool odd = blocks == 3 || blocks == 5 || blocks == 6 || blocks == 7 ||
+                           blocks == 10 || blocks == 12 || blocks == 14;
+          const bool want = R <= 256 && (p2 || (odd && (D == 64 || D == 128) && (!neox || R == D)));
+          CHECK((g != 0) == want, "rope_contig_blocks(%d,%d,%d,%d) = %d", H, D, R, (int)neox, g);
+          CHECK(g == 0 || g == blocks, "rope_contig_blocks(%d,%d,%d) = %d blocks", H, D, R, g);
+          check_contig(H, D, R, g);
+        }
+  CHECK(rope_contig_blocks(32, 192, 64, true) == 0 && rope_contig_blocks(4, 128, 24, false) == 0 &&
+            rope_contig_blocks(40, 128, 64, true) == 0 && rope_contig_blocks(9, 128, 128, true) == 0,
+        "non-power-of-two heads, odd rows rotating part of a NeoX head, rows of 1152 channels "
+        "must take the item kernel");
+  CHECK(rope_contig_blocks(40, 128, 128, true) == 10 && rope_contig_blocks(40, 128, 64, false) == 10,
+        "40 heads of 128 take the contiguous kernel");
   std::printf("contiguous mapping: %d shapes\n", contig_checked);
   if (fails) {
     std::printf("FAILED %d checks\n", fails);

@@ -50,6 +50,10 @@ SHAPES = [
     (4, 64, 32, 32),      # four blocks, head of 4 lanes
     (3, 256, 16, 16),     # eight blocks, head of 2 lanes
     (2, 16, 256, 256),    # eight blocks, head of 32 lanes
+    # 3, 5, 6, 7, 10, 12, 14 blocks: heads of 128 or 64 (NeoX: whole heads)
+    (3, 12, 128, 128), (5, 20, 128, 128), (2, 48, 64, 64), (3, 28, 128, 128),
+    (4, 40, 128, 128), (2, 96, 64, 64), (3, 56, 128, 128),
+    (4, 40, 128, 64),     # partial span: contiguous when interleaved, items for NeoX
 ]
 
 
