@@ -111,6 +111,36 @@ def test_rope_conventions_differ_and_strides_and_in_place():
     assert np.array_equal(gi[:, H * D:], xw[:, H * D:])
 
 
+# the contiguous kernel in place and on strided rows: the rotated span equals
+# the out-of-place result, pass-through channels and the row padding keep
+# their bits (in place the kernel stores only rotated granules)
+@pytest.mark.parametrize("neox,H,D,R", [(True, 8, 128, 64), (False, 40, 128, 64),
+                                        (True, 24, 128, 128), (False, 16, 256, 32)])
+def test_rope_contiguous_in_place_and_strided(neox, H, D, R):
+    import torch
+
+    T, dt, cs = 21, "bf16", "f32"
+    n = H * D
+    xw = synth.normal(H + D + R, (T, n + 24), 0.0, 1.0, dt)
+    c, s = synth.rope_table(T, R, cs)
+    fn = qrw.rope_apply_neox if neox else qrw.rope_apply_interleaved
+    xt = dev(xw, dt)
+    out = torch.full((T, n + 8), 3.0, dtype=torch.bfloat16, device="cuda")
+    fn(xt[:, :n], dev(c, cs), dev(s, cs), H, D, R, out=out[:, :n])
+    got = host(out)
+    want = oracle.rope(np.ascontiguousarray(xw[:, :n]), c, s, H, D, R, dt, cs, neox)
+    assert_close16(got[:, :n], want, dt,
+                   term_scale=rope_terms(np.ascontiguousarray(xw[:, :n]), c, s, H, D, R, dt, cs, neox))
+    assert np.all(got[:, n:] == got[0, n]) and got[0, n] != 0  # padding untouched (3.0)
+    fn(xt[:, :n], dev(c, cs), dev(s, cs), H, D, R, out=xt[:, :n])
+    gi = host(xt)
+    assert np.array_equal(gi[:, :n], got[:, :n])
+    assert np.array_equal(gi[:, n:], xw[:, n:])
+    P = D - R
+    if P:
+        assert np.array_equal(gi[:, :n].reshape(T, H, D)[..., :P], xw[:, :n].reshape(T, H, D)[..., :P])
+
+
 def test_rope_empty_and_deterministic():
     T, H, D = 257, 32, 128
     x = synth.normal(12, (T, H * D), 0.0, 1.0, "f16")
