@@ -77,7 +77,8 @@ KERNEL_SOURCES = {
     "rope": ("qrw_rope.hip", "qrw_rope_contig.hip", "qrw_contig.h", "qrw_plan.h", "qrw_device.h",
              "qrw_launch.h"),
     "fused": ("qrw_rope.hip", "qrw_fused_contig.h", "qrw_fused_contig_bf16.hip",
-              "qrw_fused_contig_f16.hip", "qrw_fused_tail.hip", "qrw_contig.h", "qrw_plan.h",
+              "qrw_fused_contig_f16.hip", "qrw_fused_tail.hip", "qrw_fused_tail.h",
+              "qrw_fused_tail_bf16.hip", "qrw_fused_tail_f16.hip", "qrw_contig.h", "qrw_plan.h",
               "qrw_device.h", "qrw_launch.h"),
     "act_quant": ("qrw_quant.hip", "qrw_device.h", "qrw_launch.h"),
     "qk_norm_rope": ("qrw_qknorm.hip", "qrw_qknorm.h", "qrw_qknorm_gc_a.hip",
