@@ -81,13 +81,22 @@ def assert_close16(got, want, dtype, max_ulp=2, max_abs=1e-2, term_scale=None, w
 
 
 def layernorm_terms(x, gamma, beta, dtype, eps):
-    """|(x - mu) * rstd * gamma| and |beta|, elementwise max (float64)."""
+    """Elementwise max (float64) of |(x - mu) * rstd * gamma|, |beta|, and the
+    scale at which 2 ulp of the 16-bit format cover the binary32 mean's own
+    rounding carried through x - mu: a mean of n values summed in binary32
+    is within (ceil(log2 n) + 2) * 2^-24 * mean|x| of the exact one, and an
+    output whose x - mu cancels below that bound cannot be resolved by any
+    binary32 evaluation (2 * ulp_at(t) >= t * 2^-mbits, so t = e * 2^mbits)."""
     xv = synth.storage_to_f64(x, dtype)
+    n = xv.shape[1]
     mu = xv.mean(axis=1, keepdims=True)
     rstd = 1.0 / np.sqrt(((xv - mu) ** 2).mean(axis=1, keepdims=True) + float(np.float32(eps)))
     g = 1.0 if gamma is None else synth.storage_to_f64(gamma, dtype)[None, :]
     b = 0.0 if beta is None else synth.storage_to_f64(beta, dtype)[None, :]
-    return np.maximum(np.abs((xv - mu) * rstd * g), np.abs(b) + 0 * xv)
+    mbits = 10 if dtype == "f16" else 7
+    e_mu = (np.ceil(np.log2(max(n, 2))) + 2) * 2.0 ** -24 * np.abs(xv).mean(axis=1, keepdims=True)
+    mu_term = e_mu * rstd * np.abs(g) * 2.0 ** mbits
+    return np.maximum(np.maximum(np.abs((xv - mu) * rstd * g), np.abs(b) + 0 * xv), mu_term)
 
 
 def rope_terms(x, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox):

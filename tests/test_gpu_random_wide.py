@@ -17,7 +17,7 @@ from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_term
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 64
 BLOCKS = [3, 5, 6, 7, 10, 12, 14, 16]
 
 
