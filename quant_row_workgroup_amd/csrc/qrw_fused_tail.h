@@ -49,29 +49,50 @@ constexpr int kTailRows = 4;
 
 // PACKED: the codes' row stride is x's (a packed call), one stride for both,
 // as in the all-rotating kernel.
-template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XR, bool MID, bool PACKED>
+// PAIR: the row is 2 * G blocks, and two waves of the workgroup take one half
+// each (kTailRows / 2 tokens per workgroup), exchanging the sum of squares and
+// the amax through LDS behind one workgroup barrier each, as the all-rotating
+// kernel's pair form does; a head of at most 64 granules sits at the same
+// lanes in both halves (G * 64 granules is a multiple of it), so the span test
+// and the table granule are the same.  Every wave reaches both barriers: a
+// token past the end touches no memory.
+template <typename T, typename CS, bool NEOX, int G, bool HAS_W, int XR, bool MID, bool PACKED,
+          bool PAIR = false>
 __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kernel(
     const uint16_t* x, const uint16_t* __restrict__ w, const void* cosv, const void* sinv,
     uint8_t* q, float* scales, int64_t tokens, int64_t xs, int64_t qs, int half, int hg_mask,
     int s0, float eps) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kTailRows + (threadIdx.x >> 6);
-  if (t >= tokens) return;  // wave-uniform
-  const uint16_t* xr = x + t * xs;
-  uint8_t* qr = q + t * (PACKED ? xs : qs);
+  const int wv = threadIdx.x >> 6;
+  const int64_t t = PAIR ? (int64_t)blockIdx.x * (kTailRows / 2) + (wv >> 1)
+                         : (int64_t)blockIdx.x * kTailRows + wv;
+  const int part = PAIR ? (wv & 1) : 0;  // which half of the row (PAIR)
+  const bool live = t < tokens;
+  if (!PAIR && !live) return;  // wave-uniform
+  const int64_t c0 = (int64_t)part * (512 * G);  // first channel of this wave's part
+  const uint16_t* xr = x + t * xs + c0;
+  uint8_t* qr = q + t * (PACKED ? xs : qs) + c0;
+  if (PAIR && HAS_W) w += c0;
 
   u32x4 r[G], wr[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
+  for (int g = 0; g < G; ++g) {
+    r[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (!PAIR || live) r[g] = ld16_stream(xr + 8 * (kWave * g + lane));
+  }
   if (HAS_W) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) wr[g] = ld16(w + 8 * (kWave * g + lane));
+    for (int g = 0; g < G; ++g) {
+      wr[g] = (u32x4){0u, 0u, 0u, 0u};
+      if (!PAIR || live) wr[g] = ld16(w + 8 * (kWave * g + lane));
+    }
   }
   // this lane's position in the rotated span in the steps that rotate it
   // (< 0: none; its table granule is then a valid, unused one)
   const int jl = contig_span_pos(lane, hg_mask, s0);
-  const char* crow = table_row<CS>(cosv, t, half);
-  const char* srow = table_row<CS>(sinv, t, half);
+  // (a token past the end reads token 0's rows, which exist when a kernel runs)
+  const char* crow = table_row<CS>(cosv, live ? t : 0, half);
+  const char* srow = table_row<CS>(sinv, live ? t : 0, half);
   float c[8], sn[8];
   if (NEOX) {
     const int tg = jl >= 0 ? (jl & (XR - 1)) : 0;
@@ -98,9 +119,16 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[(2 * g + k) & 7] = sumsq2(T{}, r[g][k], acc[(2 * g + k) & 7]);
   }
-  const float ss = wave_sum(tree8(acc));
-  // the mean: ss / n, n = 512 * G (for a power of two an exact scaling)
-  const float rstd = 1.0f / sqrtf(ss / (float)(512 * G) + eps);
+  float ss = wave_sum(tree8(acc));
+  __shared__ float pair_slot[kTailRows / 2][4];  // PAIR: [part] sums, [2 + part] maxima
+  if constexpr (PAIR) {
+    if (lane == 0) pair_slot[wv >> 1][part] = ss;
+    __syncthreads();
+    ss = pair_slot[wv >> 1][0] + pair_slot[wv >> 1][1];
+  }
+  // the mean: ss / n, n = 512 * G (1024 * G in pairs; for a power of two an
+  // exact scaling)
+  const float rstd = 1.0f / sqrtf(ss / (float)((PAIR ? 1024 : 512) * G) + eps);
 
   float v[G][8];
   float m[4] = {0.f, 0.f, 0.f, 0.f};
@@ -145,29 +173,37 @@ __global__ __launch_bounds__(kWave * kTailRows) void rmsnorm_rope_fp8_tail_kerne
       m[(e >> 1) & 3] = fmaxf(m[(e >> 1) & 3], fmaxf(fabsf(v[g][e]), fabsf(v[g][e + 1])));
   }
   const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-  const float amax_z = MID ? wave_max(amax) : wave_max(amax) * rstd;
+  float amax_w = wave_max(amax);
+  if constexpr (PAIR) {
+    if (lane == 0) pair_slot[wv >> 1][2 + part] = amax_w;
+    __syncthreads();
+    amax_w = fmaxf(pair_slot[wv >> 1][2], pair_slot[wv >> 1][3]);
+  }
+  const float amax_z = MID ? amax_w : amax_w * rstd;
   const float scale = scale_e4m3(fmaxf(amax_z, 1e-4f));
   const float kq = rstd / scale;
   const float inv = recip_rn(scale);
-  if (lane == 0) scales[t] = scale;
+  if (lane == 0 && (!PAIR || (live && part == 0))) scales[t] = scale;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = MID ? div_rn(v[g][e], scale, inv) : v[g][e] * kq;
+    if (PAIR && !live) continue;
     st8(qr + 8 * (kWave * g + lane), fp8x8(a));
   }
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, typename CS, bool NEOX, int G, int XR>
+template <typename T, typename CS, bool NEOX, int G, int XR, bool PAIR = false>
 void tail_go(dim3 grid, hipStream_t st, const void* x, const void* w, const void* c,
              const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs, int64_t qs,
              int half, int hg_mask, int s0, float eps, bool mid) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
+  if (PAIR) grid = dim3((unsigned)((tokens + kTailRows / 2 - 1) / (kTailRows / 2)));
 #define QRW_TAIL_LAUNCH(HW, M, P)                                                                  \
-  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M, P><<<grid, kWave * kTailRows, 0, st>>>( \
+  rmsnorm_rope_fp8_tail_kernel<T, CS, NEOX, G, HW, XR, M, P, PAIR><<<grid, kWave * kTailRows, 0, st>>>( \
       xp, wp, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps)
   // the packed instances are the weighted ones (the usual call)
   const bool packed = qs == xs;
@@ -218,6 +254,23 @@ void tail_go_xr124(int xr, dim3 grid, hipStream_t st, const void* x, const void*
   }
 }
 
+// Rows of 10, 12, 14 or 16 blocks, heads of 64 or 128: two waves per token,
+// each on G = 5 ... 8 blocks.
+template <typename T, typename CS, bool NEOX, int G>
+void tail_go_pair(int xr, dim3 grid, hipStream_t st, const void* x, const void* w,
+                  const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens,
+                  int64_t xs, int64_t qs, int half, int hg_mask, int s0, float eps, bool mid) {
+  if constexpr (!NEOX) {
+    tail_go<T, CS, NEOX, G, 1, true>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid);
+  } else {
+    switch (xr) {
+      case 1: tail_go<T, CS, NEOX, G, 1, true>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      case 2: tail_go<T, CS, NEOX, G, 2, true>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+      default: tail_go<T, CS, NEOX, G, 4, true>(grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    }
+  }
+}
+
 template <typename T, typename CS, bool NEOX>
 void tail_go_g(int gg, int xr, dim3 grid, hipStream_t st, const void* x, const void* w,
                const void* c, const void* s, uint8_t* q, float* sc, int64_t tokens, int64_t xs,
@@ -230,6 +283,10 @@ void tail_go_g(int gg, int xr, dim3 grid, hipStream_t st, const void* x, const v
     case 5: tail_go_xr124<T, CS, NEOX, 5>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
     case 6: tail_go_xr124<T, CS, NEOX, 6>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
     case 7: tail_go_xr124<T, CS, NEOX, 7>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 10: tail_go_pair<T, CS, NEOX, 5>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 12: tail_go_pair<T, CS, NEOX, 6>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 14: tail_go_pair<T, CS, NEOX, 7>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
+    case 16: tail_go_pair<T, CS, NEOX, 8>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
     default: tail_go_xr<T, CS, NEOX, 8>(xr, grid, st, x, w, c, s, q, sc, tokens, xs, qs, half, hg_mask, s0, eps, mid); break;
   }
 }

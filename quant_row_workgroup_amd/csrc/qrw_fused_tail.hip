@@ -10,8 +10,8 @@ bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 }  // namespace
 
 // Tail rotation (16 <= rope_dim < head_dim, both powers of two, rope_dim <=
-// 256) on rows of 1, 2, 4 or 8 blocks of 512 channels, or of 3, 5, 6 or 7
-// blocks with heads of 64 or 128.
+// 256) on rows of 1, 2, 4 or 8 blocks of 512 channels, or of 3, 5, 6, 7 (one
+// wave per token) or 10, 12, 14, 16 blocks (two) with heads of 64 or 128.
 bool fused_tail_ok(int64_t heads, int64_t head_dim, int64_t rope_dim) {
   const int64_t n = heads * head_dim;
   const int64_t g = n / 512;
@@ -19,7 +19,8 @@ bool fused_tail_ok(int64_t heads, int64_t head_dim, int64_t rope_dim) {
         rope_dim <= 256 && n % 512 == 0))
     return false;
   if (g == 1 || g == 2 || g == 4 || g == 8) return true;
-  return (head_dim == 64 || head_dim == 128) && (g == 3 || g == 5 || g == 6 || g == 7);
+  return (head_dim == 64 || head_dim == 128) &&
+         (g == 3 || g == 5 || g == 6 || g == 7 || g == 10 || g == 12 || g == 14 || g == 16);
 }
 
 hipError_t launch_rmsnorm_rope_fp8_tail(const void* x, const void* w, const void* cos,

@@ -141,7 +141,10 @@ TAIL_SHAPES = [(6, 16, 64, 32), (5, 4, 256, 128), (4, 2, 2048, 64), (3, 1, 512, 
                (9, 8, 128, 16), (2, 1, 4096, 128), (7, 32, 128, 64),
                # 3, 5, 6, 7 blocks of 512 channels, heads of 128 or 64
                (5, 24, 128, 64), (4, 20, 128, 32), (3, 12, 128, 32), (6, 48, 64, 32),
-               (2, 28, 128, 16)]
+               (2, 28, 128, 16),
+               # 10, 12, 14, 16 blocks: two waves per token
+               (5, 40, 128, 64), (3, 48, 128, 32), (7, 56, 128, 16), (4, 64, 128, 64),
+               (9, 128, 64, 32)]
 
 
 def _check_ties(x, w, c, s, H, D, R, dt, cs, neox, what, eps=1e-6):

@@ -43,7 +43,7 @@ def test_rounded_workload_shape():
                                      (7, 1, 1000, 16), (1, 1, 16, 16), (12, 1, 8192, 512),
                                      (8, 1, 4096, 128), (5, 4, 256, 128), (10, 20, 128, 128),
                                      (9, 48, 64, 64), (13, 40, 128, 128), (7, 64, 128, 128),
-                                     (5, 24, 128, 64)])
+                                     (5, 24, 128, 64), (7, 40, 128, 64)])
 def test_rounded_shapes(neox, dt, cs, T, H, D, R):
     x = synth.normal(T + H + D + R, (T, H * D), 0.0, 3.0, dt, outlier_frac=0.01,
                      outlier_mul=10.0)
