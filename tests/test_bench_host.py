@@ -1,6 +1,7 @@
 """Host logic of bench.py on the CPU: the row-count override, the reported
-arithmetic type, the refusal of more than one GPU, the oracle baseline, and
-the summaries of rocprofv3 kernel-trace and counter files."""
+arithmetic type, the layouts the same-traffic probes reproduce, the refusal of
+more than one GPU, the oracle baseline, and the summaries of rocprofv3
+kernel-trace and counter files."""
 import subprocess
 import sys
 
@@ -52,6 +53,21 @@ def test_compute_dtype():
     assert bench.compute_dtype(synth.WORKLOADS["scale_add_1M_f32"]) == "f32"
     assert bench.compute_dtype(dict(op="ew", kind="scale_add", alpha=0.5, dtype="bf16")) == "f64"
     assert bench.compute_dtype(dict(op="ew", kind="scale_add", alpha=1.0, dtype="f16")) == "f32"
+
+
+def test_same_traffic_probes_cover_only_their_own_layouts():
+    covered = {n for n, c in synth.WORKLOADS.items() if bench.probe_shape(c)}
+    assert covered == {"rmsnorm_rope_fp8_4096x4096_bf16", "qk_norm_rope_4096_q32_kv8_d128_bf16",
+                       "qk_norm_rope_fp8_kv_4096_q32_kv8_d128_bf16"}
+    base = dict(synth.WORKLOADS["rmsnorm_rope_fp8_4096x4096_bf16"])
+    for k, v in (("neox", False), ("rope_dim", 64), ("dtype", "f16"), ("cs_dtype", "f32"),
+                 ("staged", True)):
+        assert not bench.probe_shape(dict(base, **{k: v})), k
+    qk = dict(synth.WORKLOADS["qk_norm_rope_4096_q32_kv8_d128_bf16"])
+    for k, v in (("q_heads", 16), ("kv_heads", 4), ("head_dim", 64), ("neox", False),
+                 ("cs_dtype", "f32")):
+        assert not bench.probe_shape(dict(qk, **{k: v})), k
+    assert bench.probe_shape(dict(qk, tokens=17))
 
 
 def test_more_than_one_gpu_is_refused():
