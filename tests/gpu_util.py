@@ -125,6 +125,20 @@ def _pair_terms(xv, cos, sin, rope_dim, cs_dtype, neox):
     return out
 
 
+def rotation_terms(x, w, cos, sin, heads, head_dim, rope_dim, dtype, cs_dtype, neox, eps):
+    """For each channel of the fused operator's output, an upper bound on the
+    sum of the two products its rotation adds, |y_a c| + |y_b s| with
+    y = x * w * rstd over the whole row (float64): twice the larger product.
+    Pass-through channels get 0."""
+    T = x.shape[0]
+    n = heads * head_dim
+    xv = synth.storage_to_f64(x, dtype)[:, :n]
+    rstd = 1.0 / np.sqrt((xv ** 2).mean(axis=1, keepdims=True) + float(np.float32(eps)))
+    wv = np.ones(n) if w is None else synth.storage_to_f64(w, dtype)[:n]
+    y = (xv * wv[None] * rstd).reshape(T, heads, head_dim)
+    return 2.0 * _pair_terms(y, cos, sin, rope_dim, cs_dtype, neox).reshape(T, n)
+
+
 def qk_terms(x, q_weight, k_weight, cos, sin, q_heads, kv_heads, head_dim, rope_dim, dtype,
              cs_dtype, neox, eps):
     """rope_terms of u = x * w for the q/k heads, times each head's rstd (float64);
@@ -170,11 +184,15 @@ def e4m3_boundaries():
     return (v[1:] + v[:-1]) / 2
 
 
-def assert_codes_away_from_ties(got, want, quotient, rel=2.0 ** -20, what=""):
+def assert_codes_away_from_ties(got, want, quotient, rel=2.0 ** -20, what="", magnitude=None):
     """FP8 codes equal wherever the exact quotient z / scale lies farther than
-    ``rel`` (relative) from an E4M3 rounding boundary; within that distance of a
-    boundary either neighbour is a correct rounding at the precision the binary32
-    row statistics resolve.  Never more than one step apart."""
+    ``rel`` times its magnitude from an E4M3 rounding boundary; within that
+    distance of a boundary either neighbour is a correct rounding at the
+    precision the binary32 row statistics resolve.  Never more than one step
+    apart.  The magnitude is |z / scale|, or the larger of it and ``magnitude``
+    where given: a rotated value is a sum of two products, and its binary32
+    error is relative to those products, not to the sum, which cancellation
+    can make far smaller (``rotation_terms``)."""
     got = np.asarray(got)
     want = np.asarray(want)
     d = np.abs(ord8(got) - ord8(want))
@@ -183,7 +201,8 @@ def assert_codes_away_from_ties(got, want, quotient, rel=2.0 ** -20, what=""):
     q = np.abs(np.asarray(quotient, dtype=np.float64))
     i = np.clip(np.searchsorted(b, q), 1, len(b) - 1)
     gap = np.minimum(np.abs(q - b[i - 1]), np.abs(q - b[i]))
-    near = gap <= rel * np.maximum(q, 2.0 ** -9)
+    m = q if magnitude is None else np.maximum(q, np.asarray(magnitude, dtype=np.float64))
+    near = gap <= rel * np.maximum(m, 2.0 ** -9)
     bad = (d != 0) & ~near
     assert not bad.any(), (f"{what}: {int(bad.sum())} codes differ away from a rounding "
                            f"boundary, e.g. at {np.argwhere(bad)[0]}")

@@ -14,7 +14,7 @@ import oracle
 import quant_row_workgroup_amd as qrw
 from quant_row_workgroup_amd import synth
 from tests.gpu_util import (assert_codes, assert_codes_away_from_ties, assert_scales, dev,
-                            host)
+                            host, rotation_terms)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,11 +152,15 @@ def _check_ties(x, w, c, s, H, D, R, dt, cs, neox, what, eps=1e-6):
     channels unrotated and no weight, z / scale is 448 x / x_max up to the
     scale's rounding -- a ratio of 16-bit inputs that often sits exactly on an
     E4M3 midpoint, so the binary32 row statistics cannot resolve it (up to ~3%
-    of the codes); the ordinary 99.9% bar does not apply there."""
+    of the codes); the ordinary 99.9% bar does not apply there.  A rotated
+    channel's distance to a boundary is measured against the products its
+    rotation adds, which can be far larger than the result."""
     q, sc = _run(x, w, c, s, H, D, R, dt, cs, neox, eps)
     wq, wsc, z = oracle.rmsnorm_rope_fp8(x, w, c, s, H, D, R, dt, cs, neox, eps, want_z=True)
     assert_scales(sc, wsc, what=what)
-    return assert_codes_away_from_ties(q, wq, z / wsc.astype(np.float64)[:, None], what=what)
+    sd = wsc.astype(np.float64)[:, None]
+    terms = rotation_terms(x, w, c, s, H, D, R, dt, cs, neox, eps)
+    return assert_codes_away_from_ties(q, wq, z / sd, what=what, magnitude=terms / sd)
 
 
 @pytest.mark.parametrize("neox", [True, False])

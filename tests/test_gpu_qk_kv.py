@@ -15,7 +15,7 @@ import oracle
 import quant_row_workgroup_amd as qrw
 from quant_row_workgroup_amd import synth
 from tests.gpu_util import (assert_close16, assert_codes, assert_codes_away_from_ties,
-                            assert_scales, dev, host, qk_terms)
+                            assert_scales, dev, host, qk_terms, rotation_terms)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,14 +37,17 @@ def _run(x, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, eps, slots, ns, cst):
 
 
 def _k_quotients(x, kw, c, s, Hq, Hk, D, R, dt, cs, neox, eps, k_scales):
-    """z / scale of every k head, [tokens, Hk*D]: a k head is normalised and
-    rotated as one 1-head row of the fused operator, whose oracle returns the
-    unrounded z; the scales are the KV oracle's own."""
+    """z / scale of every k head, [tokens, Hk*D], and the rotation's products
+    on the same scale: a k head is normalised and rotated as one 1-head row of
+    the fused operator, whose oracle returns the unrounded z; the scales are the
+    KV oracle's own."""
     T = x.shape[0]
     kx = np.ascontiguousarray(x[:, Hq * D:(Hq + Hk) * D]).reshape(T * Hk, D)
-    _, _, z = oracle.rmsnorm_rope_fp8(kx, kw, np.repeat(c, Hk, axis=0), np.repeat(s, Hk, axis=0),
-                                      1, D, R, dt, cs, neox, eps, want_z=True)
-    return (z / k_scales.reshape(T * Hk, 1).astype(np.float64)).reshape(T, Hk * D)
+    kc, ks = np.repeat(c, Hk, axis=0), np.repeat(s, Hk, axis=0)
+    _, _, z = oracle.rmsnorm_rope_fp8(kx, kw, kc, ks, 1, D, R, dt, cs, neox, eps, want_z=True)
+    sd = k_scales.reshape(T * Hk, 1).astype(np.float64)
+    terms = rotation_terms(kx, kw, kc, ks, 1, D, R, dt, cs, neox, eps)
+    return (z / sd).reshape(T, Hk * D), (terms / sd).reshape(T, Hk * D)
 
 
 def _check(x, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, eps, slots=None, ns=None, pad=0,
@@ -76,10 +79,11 @@ def _check(x, qw, kw, c, s, Hq, Hk, D, R, dt, cs, neox, eps, slots=None, ns=None
     if rows.any():
         if ties:
             kept = (sl >= 0) & (sl < ns)
-            zq = _k_quotients(x[kept], kw, c[kept], s[kept], Hq, Hk, D, R, dt, cs, neox, eps,
-                              wks[sl[kept]])
+            zq, mag = _k_quotients(x[kept], kw, c[kept], s[kept], Hq, Hk, D, R, dt, cs, neox,
+                                   eps, wks[sl[kept]])
             st["k"] = assert_codes_away_from_ties(gkc[sl[kept], : Hk * D],
-                                                  wkc[sl[kept], : Hk * D], zq, what=what + " k")
+                                                  wkc[sl[kept], : Hk * D], zq, what=what + " k",
+                                                  magnitude=mag)
         else:
             st["k"] = assert_codes(gkc[rows, : Hk * D], wkc[rows, : Hk * D], what=what + " k")
         assert_scales(gks[rows], wks[rows], what=what + " k scales")

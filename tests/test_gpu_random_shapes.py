@@ -22,7 +22,7 @@ from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_term
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 384
 
 
 def _rng(op, i):
@@ -126,11 +126,13 @@ def test_random_fused(i):
     c, s = synth.rope_table(T, R, cs, base=10000.0 if T < 4 else 7.0)
     what = f"fused {T}x{H}x{D}/{R} {dt}/{cs} {'weight' if w is not None else 'no weight'}"
     st = test_gpu_fused._check_ties(x, w, c, s, H, D, R, dt, cs, neox, what=what)
+    # the tie-aware bar decides (scales within 1e-6, never more than one step,
+    # every code exact away from a rounding boundary), not the whole-workload
+    # share of 99.9%: a small case whose first token turns by zero angles, or
+    # whose channels mostly pass through, can hold more than 0.1% of its codes
+    # on exact E4M3 midpoints.  The 99.9% share is asserted on the workloads
+    # and the hand-written shapes (test_gpu_fused).
     print(what, st)
-    if w is not None:
-        # with a weight the stated bar holds as well: >= 99.9% of codes bit-exact
-        # (never more than one step apart and scales within 1e-6: _check_ties)
-        assert st["exact_frac"] >= 0.999, (what, st)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))

